@@ -1,0 +1,232 @@
+"""Benchmark of the MSA fused producer on one MI355X.
+
+Step = one decode step of a 60-layer model at decode batch 64 (64 sequences x 1 new token at
+positions 7000..9199, local heads Q=16 / KV=2 / index-Q=2 / index-K=1, head_dim 128, fp8 e4m3
+HND caches of 10,240 pages per layer): 60 msa_produce launches, each on its own layer's input
+row, norm weights, scales and caches, captured once in a HIP graph and replayed.  Inputs are
+resident in HBM before the timed region.
+
+The JSON line reports:
+  value            algorithmic HBM GB/s of the decode step (bytes the method must move / step time)
+  us_per_layer_call, us_per_step
+  roofline         of the producer kernel at decode batch 64 (HIP-event time over the timed
+                   region / launches, against MI355X's 8 TB/s)
+  prefill          the 65,536-token prefill chunk (8 x 8192 tokens), its own roofline
+  cpu_baseline     the CPU oracle on a bounded sample of the same decode workload
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers 60] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "producer HBM GB/s (% of peak) + µs per layer call at decode batch 64"
+KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_msa_amd", "csrc", "msa_produce.hip")
+COUNTERS = os.path.join(ROOT, "profiles", "produce_kernel_hbm_counters.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_digest() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def counter_traffic(workload_key: str):
+    """Measured HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel
+    calibration) if they were taken on the current kernel source; else None."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_sha256_16") != kernel_digest():
+        return None
+    return c.get("bytes_per_launch", {}).get(workload_key)
+
+
+def call(msa, wl, d, stream=None):
+    msa.msa_produce(d.x, d.positions, d.seq_idx, d.page_table, *d.weights, d.q_out, d.iq_out,
+                    d.caches[0], d.caches[1], d.caches[2], k_scale=d.scales[0], v_scale=d.scales[1],
+                    ik_scale=d.scales[2], num_pages=wl.num_pages, rms_eps=wl.eps, rope_theta=wl.theta,
+                    slots_out=d.slots, stream=stream)
+
+
+def bench_decode(msa, W, torch, layers, steps, warmup):
+    log(f"[bench] staging {layers} decode-64 layers")
+    wls = [W.config1(layer=i) for i in range(layers)]
+    devs = [W.to_device(wl) for wl in wls]
+    # share the metadata buffers across layers (one batch, many layers)
+    for d in devs[1:]:
+        d.positions, d.seq_idx, d.page_table = devs[0].positions, devs[0].seq_idx, devs[0].page_table
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        for wl, d in zip(wls, devs):      # one eager pass before capture
+            call(msa, wl, d)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            for wl, d in zip(wls, devs):
+                call(msa, wl, d)
+    torch.cuda.synchronize()
+    log(f"[bench] decode graph captured ({layers} launches); warmup {warmup}, timing {steps} steps")
+    with torch.cuda.stream(s):
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(steps):
+            g.replay()
+        e1.record(s)
+        torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    bytes_per_call = wls[0].algorithmic_bytes()
+    return dict(ms_total=ms, ms_per_step=ms / steps, bytes_per_call=bytes_per_call,
+                bytes_per_step=bytes_per_call * layers, launches=steps * layers, wls=wls, devs=devs)
+
+
+def bench_prefill(msa, W, torch, iters, warmup):
+    log("[bench] staging the 65,536-token prefill chunk (two input sets)")
+    sets = [W.config3(variant=v) for v in range(2)]
+    devs = [W.to_device(wl) for wl in sets]
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    for i in range(warmup):
+        call(msa, sets[i % 2], devs[i % 2])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for i in range(iters):
+        call(msa, sets[i % 2], devs[i % 2])
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    b = sets[0].algorithmic_bytes()
+    us = ms * 1000 / iters
+    gbs = b / (us * 1e-6) / 1e9
+    traffic = counter_traffic("prefill_65536")
+    out = dict(workload="prefill 8 x 8192 tokens (65,536 rows), heads 16/2/2/1, fp8 e4m3 caches, 12,000-page pool",
+               us_per_call=us, algorithmic_bytes_per_call=b, launches=iters,
+               roofline=dict(bound="hbm", achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=gbs / HBM_PEAK_GBS,
+                             traffic=traffic))
+    del devs
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(W, seconds: float):
+    """The CPU oracle as it stands, on repeated decode-64 layer calls for about `seconds`."""
+    import numpy as np
+    import oracle
+    threads = min(16, os.cpu_count() or 1)
+    wl = W.config1(layer=0)
+    args = (wl.x, wl.x_stride, wl.T, wl.head_dim, wl.hq, wl.hkv, wl.hiq, wl.hik, wl.positions, wl.seq_idx,
+            wl.page_table, wl.max_pages, wl.num_seqs, wl.max_pages, wl.page_size, wl.num_pages, *wl.weights,
+            wl.eps, wl.theta)
+    kw = dict(dtypes=[c.dtype for c in wl.caches], scales=[c.scale for c in wl.caches], num_threads=threads)
+    oracle.produce_rows(*args, **kw)
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.produce_rows(*args, **kw)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    per_call = el / n
+    return dict(value=wl.algorithmic_bytes() / per_call / 1e9, unit="GB/s", cores=threads, kind="oracle",
+                sample=f"{n} decode-64 layer calls (64 tokens, heads 16/2/2/1, fp8) of the CPU oracle "
+                       f"({threads} OpenMP threads, dense per-token output form) in {el:.1f} s; "
+                       f"{per_call * 1e6:.0f} us per layer call")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--layers", type=int, default=60)
+    ap.add_argument("--prefill-iters", type=int, default=50)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the producer runs on one tensor-parallel rank's local heads "
+              f"and never communicates; --gpus {args.gpus} is not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_msa_amd as msa
+    from paged_kv_cache_msa_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    msa.lib()
+    torch.cuda.set_device(0)
+
+    dec = bench_decode(msa, W, torch, args.layers, args.steps, args.warmup)
+    us_step = dec["ms_per_step"] * 1000
+    us_call = us_step / args.layers
+    step_gbs = dec["bytes_per_step"] / (us_step * 1e-6) / 1e9
+    launch_us = dec["ms_total"] * 1000 / dec["launches"]
+    launch_gbs = dec["bytes_per_call"] / (launch_us * 1e-6) / 1e9
+    del dec["devs"]
+    torch.cuda.empty_cache()
+
+    prefill = None if args.no_prefill else bench_prefill(msa, W, torch, args.prefill_iters, 10)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(W, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": step_gbs,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": dec["ms_per_step"],
+        "us_per_step": us_step,
+        "us_per_layer_call": us_call,
+        "pct_of_hbm_peak": 100.0 * step_gbs / HBM_PEAK_GBS,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode batch 64: 64 seqs x 1 token at positions 7000..9199, local heads Q=16 KV=2 "
+                        "index-Q=2 index-K=1, head_dim 128, fp8 e4m3 HND caches [10240, H, 64, 128] per layer; "
+                        f"{args.layers} layer calls per step in one HIP graph",
+            "tokens": 64,
+            "layers": args.layers,
+            "algorithmic_bytes_per_layer_call": dec["bytes_per_call"],
+            "parallelism": "single GPU (one tensor-parallel rank's local heads)",
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": launch_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": launch_gbs / HBM_PEAK_GBS, "traffic": counter_traffic("decode_64"),
+            "kernel": "produce_kernel (decode batch 64)", "avg_launch_us": launch_us,
+        },
+        "prefill": prefill,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,601 @@
+// MiniMax-M3 MSA fused producer for CDNA4 (gfx950): per-head RMSNorm + neox RoPE on the Q, K,
+// index-Q and index-K heads of one packed projection row per token, compact bf16 Q / index-Q,
+// and K / V / index-K scattered into paged HND caches (OCP FP8 E4M3 or bf16), one launch per
+// layer.  Operation: page "Fuse MiniMax-M3 QKV and index projection" (AFTER figure, change
+// list); page/offset computed once per token and the three cache writes fused: page "Fuse
+// MiniMax-M3 MSA per-layer KV-cache writes into one kernel" ("The problem", "The fix", "Nsys
+// trace"); slots derived from the page table: page "Wire in custom decode kernels for
+// MinimaxM3" (conflict-resolution commit notes).  The arithmetic reading is documented in
+// include/msa_produce.h.
+//
+// Work decomposition.  head_dim is 128 = 8 lanes x (8 first-half + 8 second-half elements):
+// lane `sub` of a head holds elements [8 sub, 8 sub + 8) and [64 + 8 sub, 64 + 8 sub + 8), so
+// both members of every rotate-half pair (i, i + 64) sit in the same lane and RoPE needs no
+// cross-lane exchange.  A wavefront (64 lanes) covers 8 heads per pass with two 16-byte loads
+// per lane (1 KiB contiguous per head-row pair); 23 heads take 3 passes.  The per-head sum of
+// squares is reduced over the 8 lanes of a head with three DPP steps in binary64.  Each wave
+// computes its token's 64 RoPE coefficient pairs once (one binary64 sincos per lane) and
+// broadcasts them through LDS.  Token metadata (position, sequence, page-table entry) is
+// wave-uniform and read once per wave; cache offsets are 64-bit.  Large batches run one wave per
+// token (all passes); small batches split a token's passes over several waves to spread the
+// latency.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "msa_produce.h"
+
+namespace {
+
+constexpr int kHeadDim = 128;
+constexpr int kHalf = kHeadDim / 2;
+constexpr int kWave = 64;
+constexpr int kLanesPerHead = 8;
+constexpr int kHeadsPerPass = kWave / kLanesPerHead;
+constexpr int kWavesPerBlock = 4;
+constexpr int kBlock = kWave * kWavesPerBlock;
+constexpr int kMaxPassesPerWave = 4;
+
+enum Stream { kQ = 0, kK = 1, kV = 2, kIQ = 3, kIK = 4 };
+
+struct CacheDev {
+    uint8_t* data;
+    int64_t sp, sh, st;        // element strides (page, head, token)
+    const float* scale;        // fp8 only
+    int32_t heads;
+    int32_t is_bf16;
+};
+
+struct ProduceArgs {
+    const uint16_t* x;
+    int64_t x_stride;
+    const int32_t* pos;
+    const int32_t* seq;
+    const int32_t* pt;
+    int64_t pt_stride;
+    int64_t num_pages;
+    int32_t T, S, max_pages, page_size;
+    int32_t hq, hkv, hiq, hik, heads_total, npass, waves_per_token;
+    float eps;
+    const uint16_t* w[4];      // norm weights of Q, K, index-Q, index-K
+    uint16_t* q_out;
+    uint16_t* iq_out;
+    CacheDev cache[3];         // K, V, index-K
+    int64_t* slots_out;
+    double inv_freq[kHalf];
+};
+
+struct FreqArgs {
+    double inv_freq[kHalf];
+};
+
+// ------------------------------------------------------------------ shared device arithmetic
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ void unpack8(const uint4& v, float* f)
+{
+    f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+    f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+    f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+    f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two binary32 -> bf16 round-to-nearest-even (v_cvt_pk_bf16_f32); NaN -> quiet NaN, sign kept.
+__device__ __forceinline__ uint32_t bf16x2(float a, float b)
+{
+    f32x2_t v = {a, b};
+    bf16x2_t h = __builtin_convertvector(v, bf16x2_t);
+    uint32_t w;
+    __builtin_memcpy(&w, &h, 4);
+    return w;
+}
+
+__device__ __forceinline__ float sat448(float v) { return fabsf(v) > 448.0f ? copysignf(448.0f, v) : v; }
+
+// Four binary32 -> OCP E4M3, round-to-nearest-even, saturating to +-448 (infinities included).
+// v_cvt_pk_fp8_f32 rounds to nearest even but does not saturate and writes 0xff for every NaN;
+// the clamp runs first (a NaN fails the compare and passes through) and positive NaNs get their
+// sign bit cleared afterwards so that a NaN keeps its sign.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d)
+{
+    uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(c), sat448(d), w, true);
+    uint32_t clear = (__float_as_int(a) > 0x7f800000 ? 0x80u : 0u) | (__float_as_int(b) > 0x7f800000 ? 0x8000u : 0u)
+                   | (__float_as_int(c) > 0x7f800000 ? 0x800000u : 0u) | (__float_as_int(d) > 0x7f800000 ? 0x80000000u : 0u);
+    return w & ~clear;
+}
+
+// Dequantisation scale -> quantisation multiplier, binary32 division rounded once.
+__device__ __forceinline__ float inv_scale_of(const float* scale) { return 1.0f / *scale; }
+
+// RMSNorm scale from a binary64 sum of squares: (float)(1 / sqrt(ss / 128 + eps)).
+__device__ __forceinline__ float rms_from_ss(double ss, float eps)
+{
+    return (float)(1.0 / sqrt(ss / (double)kHeadDim + (double)eps));
+}
+
+// RoPE coefficient pair of one (position, frequency).
+__device__ __forceinline__ void rope_coeff(int32_t pos, double inv_freq, float* c, float* s)
+{
+    const double angle = (double)pos * inv_freq;
+    double sn, cs;
+    sincos(angle, &sn, &cs);
+    *c = (float)cs;
+    *s = (float)sn;
+}
+
+template <int Ctrl>
+__device__ __forceinline__ double dpp_f64(double v)
+{
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)u, Ctrl, 0xf, 0xf, false);
+    const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), Ctrl, 0xf, 0xf, false);
+    return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// Sum over the 8 lanes of a head.  Every lane of the group ends with the same value: each step
+// adds a partner's partial, and IEEE addition is commutative.
+__device__ __forceinline__ double head_sum8(double v)
+{
+    v += dpp_f64<0xb1>(v);    // quad_perm [1,0,3,2]: partner lane ^ 1
+    v += dpp_f64<0x4e>(v);    // quad_perm [2,3,0,1]: partner lane ^ 2
+    v += dpp_f64<0x141>(v);   // row_half_mirror: lane i <- 7 - i within each group of 8
+    return v;
+}
+
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ------------------------------------------------------------------ producer kernel
+
+template <int PPW>
+__global__ __launch_bounds__(kBlock) void produce_kernel(const ProduceArgs a)
+{
+    __shared__ __attribute__((aligned(16))) float cs_lds[kWavesPerBlock][2 * kHalf];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t item = blockIdx.x * kWavesPerBlock + wave;
+    if (item >= (uint32_t)a.T * (uint32_t)a.waves_per_token) return;   // wave-uniform; no block barrier follows
+    const uint32_t wpt = a.waves_per_token;
+    const int32_t t = wpt == 1 ? (int32_t)item : (int32_t)(item / wpt);
+    const int32_t chunk = (int32_t)(item - (uint32_t)t * wpt);
+
+    // Token metadata, once per wave.
+    const int32_t pos = a.pos[t];
+    const int32_t sq = a.seq[t];
+    int64_t page = -1;
+    int32_t off = 0;
+    if (sq >= 0 && sq < a.S && pos >= 0) {
+        const int32_t lp = pos / a.page_size;
+        if (lp < a.max_pages) {
+            const int64_t pg = a.pt[(int64_t)sq * a.pt_stride + lp];
+            if (pg >= 0 && pg < a.num_pages) {
+                page = pg;
+                off = pos - lp * a.page_size;
+            }
+        }
+    }
+    const bool valid = page >= 0;
+    if (chunk == 0 && lane == 0 && a.slots_out) a.slots_out[t] = valid ? page * a.page_size + off : -1;
+
+    // Issue the row loads of every pass of this wave before any arithmetic.
+    const int hs = lane / kLanesPerHead;   // head slot within a pass
+    const int sub = lane % kLanesPerHead;  // element group within the head
+    const int pass0 = chunk * PPW;
+    const uint16_t* row = a.x + (int64_t)t * a.x_stride;
+    const int h_k = a.hq, h_v = a.hq + a.hkv, h_iq = a.hq + 2 * a.hkv, h_ik = h_iq + a.hiq;
+
+    uint4 xa[PPW], xb[PPW], wa[PPW], wb[PPW];
+    int hh[PPW];
+#pragma unroll
+    for (int k = 0; k < PPW; ++k) {
+        const int pass = pass0 + k;
+        hh[k] = pass * kHeadsPerPass + hs;
+        xa[k] = xb[k] = wa[k] = wb[k] = make_uint4(0, 0, 0, 0);
+        if (pass < a.npass && hh[k] < a.heads_total) {
+            const uint16_t* hp = row + (int64_t)hh[k] * kHeadDim + sub * 8;
+            xa[k] = *reinterpret_cast<const uint4*>(hp);
+            xb[k] = *reinterpret_cast<const uint4*>(hp + kHalf);
+            const int h = hh[k];
+            const uint16_t* w = h < h_k ? a.w[0] : h < h_v ? a.w[1] : h < h_iq ? nullptr : h < h_ik ? a.w[2] : a.w[3];
+            if (w) {
+                wa[k] = *reinterpret_cast<const uint4*>(w + sub * 8);
+                wb[k] = *reinterpret_cast<const uint4*>(w + kHalf + sub * 8);
+            }
+        }
+    }
+
+    // RoPE coefficients of this token: lane i computes frequency i; lane `sub` then needs
+    // frequencies [8 sub, 8 sub + 8).
+    {
+        float c, s;
+        rope_coeff(pos, a.inv_freq[lane], &c, &s);
+        cs_lds[wave][lane] = c;
+        cs_lds[wave][kHalf + lane] = s;
+    }
+    wave_lds_sync();
+    float cf[8], sf[8];
+    {
+        const float4* cp = reinterpret_cast<const float4*>(&cs_lds[wave][sub * 8]);
+        const float4* sp = reinterpret_cast<const float4*>(&cs_lds[wave][kHalf + sub * 8]);
+        const float4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
+        cf[0] = c0.x; cf[1] = c0.y; cf[2] = c0.z; cf[3] = c0.w; cf[4] = c1.x; cf[5] = c1.y; cf[6] = c1.z; cf[7] = c1.w;
+        sf[0] = s0.x; sf[1] = s0.y; sf[2] = s0.z; sf[3] = s0.w; sf[4] = s1.x; sf[5] = s1.y; sf[6] = s1.z; sf[7] = s1.w;
+    }
+
+    float inv_sc[3];
+#pragma unroll
+    for (int ci = 0; ci < 3; ++ci)
+        inv_sc[ci] = (a.cache[ci].heads > 0 && !a.cache[ci].is_bf16) ? inv_scale_of(a.cache[ci].scale) : 1.0f;
+    int64_t cache_base[3];
+#pragma unroll
+    for (int ci = 0; ci < 3; ++ci) cache_base[ci] = valid ? page * a.cache[ci].sp + (int64_t)off * a.cache[ci].st : 0;
+
+#pragma unroll
+    for (int k = 0; k < PPW; ++k) {
+        const int pass = pass0 + k;
+        if (pass >= a.npass) break;                 // wave-uniform
+        const int h = hh[k];
+        const bool act = h < a.heads_total;
+
+        float v[16], wv[16];
+        unpack8(xa[k], v);
+        unpack8(xb[k], v + 8);
+        unpack8(wa[k], wv);
+        unpack8(wb[k], wv + 8);
+
+        // Per-head sum of squares in binary64 (each square is exact), reduced over 8 lanes.
+        double ss = 0.0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) ss = __builtin_fma((double)v[j], (double)v[j], ss);
+        ss = head_sum8(ss);
+        const float r = rms_from_ss(ss, a.eps);
+
+        const int st = h < h_k ? kQ : h < h_v ? kK : h < h_iq ? kV : h < h_ik ? kIQ : kIK;
+        float o[16];
+        if (st == kV) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) o[j] = v[j];
+        } else {
+            float y[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) y[j] = (v[j] * r) * wv[j];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                o[j] = y[j] * cf[j] - y[j + 8] * sf[j];
+                o[j + 8] = y[j + 8] * cf[j] + y[j] * sf[j];
+            }
+        }
+        if (!act) continue;
+
+        if (st == kQ || st == kIQ) {
+            uint16_t* dst = st == kQ ? a.q_out + ((int64_t)t * a.hq + h) * kHeadDim
+                                     : a.iq_out + ((int64_t)t * a.hiq + (h - h_iq)) * kHeadDim;
+            dst += sub * 8;
+            uint4 lo, hi;
+            lo.x = bf16x2(o[0], o[1]); lo.y = bf16x2(o[2], o[3]); lo.z = bf16x2(o[4], o[5]); lo.w = bf16x2(o[6], o[7]);
+            hi.x = bf16x2(o[8], o[9]); hi.y = bf16x2(o[10], o[11]); hi.z = bf16x2(o[12], o[13]); hi.w = bf16x2(o[14], o[15]);
+            *reinterpret_cast<uint4*>(dst) = lo;
+            *reinterpret_cast<uint4*>(dst + kHalf) = hi;
+        } else if (valid) {
+            const int ci = st == kK ? 0 : st == kV ? 1 : 2;
+            const int hl = st == kK ? h - h_k : st == kV ? h - h_v : h - h_ik;
+            const CacheDev& cd = a.cache[ci];
+            const int64_t e = cache_base[ci] + (int64_t)hl * cd.sh + sub * 8;
+            if (cd.is_bf16) {
+                uint16_t* dst = reinterpret_cast<uint16_t*>(cd.data) + e;
+                uint4 lo, hi;
+                lo.x = bf16x2(o[0], o[1]); lo.y = bf16x2(o[2], o[3]); lo.z = bf16x2(o[4], o[5]); lo.w = bf16x2(o[6], o[7]);
+                hi.x = bf16x2(o[8], o[9]); hi.y = bf16x2(o[10], o[11]); hi.z = bf16x2(o[12], o[13]); hi.w = bf16x2(o[14], o[15]);
+                *reinterpret_cast<uint4*>(dst) = lo;
+                *reinterpret_cast<uint4*>(dst + kHalf) = hi;
+            } else {
+                const float m = inv_sc[ci];
+                uint8_t* dst = cd.data + e;
+                uint2 lo, hi;
+                lo.x = e4m3x4(o[0] * m, o[1] * m, o[2] * m, o[3] * m);
+                lo.y = e4m3x4(o[4] * m, o[5] * m, o[6] * m, o[7] * m);
+                hi.x = e4m3x4(o[8] * m, o[9] * m, o[10] * m, o[11] * m);
+                hi.y = e4m3x4(o[12] * m, o[13] * m, o[14] * m, o[15] * m);
+                *reinterpret_cast<uint2*>(dst) = lo;
+                *reinterpret_cast<uint2*>(dst + kHalf) = hi;
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ step-level kernels
+
+__global__ __launch_bounds__(256) void rope_table_kernel(const int32_t* pos, int64_t n, float* cos_out,
+                                                         float* sin_out, const FreqArgs f)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n * kHalf) return;
+    const int64_t t = i / kHalf;
+    const int k = (int)(i - t * kHalf);
+    float c, s;
+    rope_coeff(pos[t], f.inv_freq[k], &c, &s);
+    cos_out[i] = c;
+    sin_out[i] = s;
+}
+
+__global__ __launch_bounds__(256) void quantize_kernel(const float* v, int64_t n, int32_t is_bf16,
+                                                       const float* scale, void* out)
+{
+    const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    if (i >= n) return;
+    float x[4];
+    for (int j = 0; j < 4; ++j) x[j] = i + j < n ? v[i + j] : 0.0f;
+    if (is_bf16) {
+        const uint32_t w0 = bf16x2(x[0], x[1]), w1 = bf16x2(x[2], x[3]);
+        uint16_t* o = reinterpret_cast<uint16_t*>(out) + i;
+        const uint16_t h[4] = {(uint16_t)w0, (uint16_t)(w0 >> 16), (uint16_t)w1, (uint16_t)(w1 >> 16)};
+        for (int j = 0; j < 4; ++j)
+            if (i + j < n) o[j] = h[j];
+    } else {
+        const float m = inv_scale_of(scale);
+        const uint32_t w = e4m3x4(x[0] * m, x[1] * m, x[2] * m, x[3] * m);
+        uint8_t* o = reinterpret_cast<uint8_t*>(out) + i;
+        for (int j = 0; j < 4; ++j)
+            if (i + j < n) o[j] = (uint8_t)(w >> (8 * j));
+    }
+}
+
+__global__ __launch_bounds__(256) void rms_scale_kernel(const double* ss, int64_t n, float eps, float* r)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) r[i] = rms_from_ss(ss[i], eps);
+}
+
+// ------------------------------------------------------------------ host side
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+// inv_freq_i = 1 / theta^(2i/D) in binary64 (one rounding each for the exponent, pow and the
+// division), memoised per host thread for the last theta.
+void fill_inv_freq(double theta, double* out)
+{
+    thread_local double last_theta = 0.0;
+    thread_local double table[kHalf];
+    if (theta != last_theta) {
+        for (int i = 0; i < kHalf; ++i) table[i] = 1.0 / std::pow(theta, (double)(2 * i) / (double)kHeadDim);
+        last_theta = theta;
+    }
+    std::memcpy(out, table, sizeof(table));
+}
+
+msa_status check_cache(const msa_cache_view* v, int32_t heads, int32_t page_size, int64_t num_pages, CacheDev* out)
+{
+    std::memset(out, 0, sizeof(*out));
+    if (heads == 0) return MSA_OK;
+    if (!v || !v->data) return MSA_ERR_NULL_POINTER;
+    if (v->num_heads != heads) return MSA_ERR_SHAPE;
+    if (v->dtype != MSA_CACHE_FP8_E4M3 && v->dtype != MSA_CACHE_BF16) return MSA_ERR_DTYPE;
+    if (v->dtype == MSA_CACHE_FP8_E4M3 && !v->scale) return MSA_ERR_DTYPE;
+    if (!aligned(v->data, 16)) return MSA_ERR_ALIGNMENT;
+    if (v->dtype == MSA_CACHE_FP8_E4M3 && !aligned(v->scale, 4)) return MSA_ERR_ALIGNMENT;
+    const int64_t s[3] = {v->stride_page, v->stride_head, v->stride_token};
+    for (int i = 0; i < 3; ++i)
+        if (s[i] <= 0 || s[i] % 8) return MSA_ERR_STRIDE;
+    // Non-overlap: with the dims ordered by stride, each stride must exceed the largest offset
+    // the smaller dims can reach.  The walk also yields the largest element offset of the view.
+    int64_t ord_s[4] = {1, s[2], s[1], s[0]};
+    int64_t ord_e[4] = {kHeadDim, page_size, heads, num_pages};
+    for (int i = 1; i < 4; ++i)
+        for (int j = i; j > 0 && ord_s[j] < ord_s[j - 1]; --j) {
+            const int64_t ts = ord_s[j]; ord_s[j] = ord_s[j - 1]; ord_s[j - 1] = ts;
+            const int64_t te = ord_e[j]; ord_e[j] = ord_e[j - 1]; ord_e[j - 1] = te;
+        }
+    int64_t max_off = 0;
+    for (int i = 0; i < 4; ++i) {
+        if (ord_e[i] <= 1) continue;
+        if (ord_s[i] <= max_off) return MSA_ERR_STRIDE;
+        int64_t reach;
+        if (__builtin_mul_overflow(ord_s[i], ord_e[i] - 1, &reach) || __builtin_add_overflow(max_off, reach, &max_off))
+            return MSA_ERR_OVERFLOW;
+    }
+    int64_t bytes;
+    if (__builtin_mul_overflow(max_off + 1, (int64_t)(v->dtype == MSA_CACHE_BF16 ? 2 : 1), &bytes))
+        return MSA_ERR_OVERFLOW;
+    out->data = static_cast<uint8_t*>(v->data);
+    out->sp = s[0];
+    out->sh = s[1];
+    out->st = s[2];
+    out->scale = v->scale;
+    out->heads = heads;
+    out->is_bf16 = v->dtype == MSA_CACHE_BF16;
+    return MSA_OK;
+}
+
+template <int PPW>
+hipError_t launch_produce(const ProduceArgs& a, hipStream_t stream)
+{
+    const int64_t waves = (int64_t)a.T * a.waves_per_token;
+    const dim3 grid((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock));
+    void* args[] = {const_cast<ProduceArgs*>(&a)};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&produce_kernel<PPW>), grid, dim3(kBlock), args, 0, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+msa_status msa_produce(const uint16_t* x, int64_t x_row_stride, int32_t num_tokens, int32_t head_dim,
+                       int32_t num_q_heads, int32_t num_kv_heads, int32_t num_iq_heads, int32_t num_ik_heads,
+                       const int32_t* positions, const int32_t* seq_idx,
+                       const int32_t* page_table, int64_t page_table_stride, int32_t num_seqs,
+                       int32_t max_pages_per_seq, int32_t page_size, int64_t num_pages,
+                       const uint16_t* q_norm_weight, const uint16_t* k_norm_weight,
+                       const uint16_t* iq_norm_weight, const uint16_t* ik_norm_weight,
+                       float rms_eps, double rope_theta,
+                       uint16_t* q_out, uint16_t* iq_out,
+                       const msa_cache_view* k_cache, const msa_cache_view* v_cache,
+                       const msa_cache_view* ik_cache,
+                       int64_t* slots_out, void* stream)
+{
+    if (head_dim != kHeadDim) return MSA_ERR_UNSUPPORTED;
+    if (num_tokens < 0 || num_q_heads < 0 || num_kv_heads < 0 || num_iq_heads < 0 || num_ik_heads < 0)
+        return MSA_ERR_SHAPE;
+    const int64_t heads_total = (int64_t)num_q_heads + 2 * (int64_t)num_kv_heads + num_iq_heads + num_ik_heads;
+    if (heads_total < 1 || heads_total > 4096) return MSA_ERR_SHAPE;
+    if (page_size <= 0 || num_seqs < 0 || max_pages_per_seq < 0 || num_pages < 0) return MSA_ERR_SHAPE;
+    if (!(rms_eps >= 0.0f) || !(rope_theta > 0.0) || !std::isfinite(rope_theta)) return MSA_ERR_SHAPE;
+    if (x_row_stride < heads_total * kHeadDim) return MSA_ERR_STRIDE;
+    if (x_row_stride % 8) return MSA_ERR_STRIDE;
+    if (num_seqs > 0 && page_table_stride < max_pages_per_seq) return MSA_ERR_STRIDE;
+    if (num_tokens > 0) {
+        if (!x || !positions || !seq_idx) return MSA_ERR_NULL_POINTER;
+        if (num_seqs > 0 && max_pages_per_seq > 0 && !page_table) return MSA_ERR_NULL_POINTER;
+        if ((num_q_heads > 0 && !q_out) || (num_iq_heads > 0 && !iq_out)) return MSA_ERR_NULL_POINTER;
+    }
+    if ((num_q_heads > 0 && !q_norm_weight) || (num_kv_heads > 0 && !k_norm_weight) ||
+        (num_iq_heads > 0 && !iq_norm_weight) || (num_ik_heads > 0 && !ik_norm_weight))
+        return MSA_ERR_NULL_POINTER;
+    if (!aligned(x, 16) || !aligned(q_out, 16) || !aligned(iq_out, 16) || !aligned(positions, 4) ||
+        !aligned(seq_idx, 4) || !aligned(page_table, 4) || !aligned(slots_out, 8) ||
+        !aligned(q_norm_weight, 16) || !aligned(k_norm_weight, 16) || !aligned(iq_norm_weight, 16) ||
+        !aligned(ik_norm_weight, 16))
+        return MSA_ERR_ALIGNMENT;
+    // Row offsets of the largest token must fit in int64.
+    int64_t row_end;
+    if (__builtin_mul_overflow((int64_t)num_tokens, x_row_stride, &row_end)) return MSA_ERR_OVERFLOW;
+    if (num_seqs > 0 && __builtin_mul_overflow((int64_t)num_seqs, page_table_stride, &row_end)) return MSA_ERR_OVERFLOW;
+
+    ProduceArgs a;
+    std::memset(&a, 0, sizeof(a));
+    msa_status st;
+    if ((st = check_cache(k_cache, num_kv_heads, page_size, num_pages, &a.cache[0])) != MSA_OK) return st;
+    if ((st = check_cache(v_cache, num_kv_heads, page_size, num_pages, &a.cache[1])) != MSA_OK) return st;
+    if ((st = check_cache(ik_cache, num_ik_heads, page_size, num_pages, &a.cache[2])) != MSA_OK) return st;
+    int64_t slot_max;
+    if (__builtin_mul_overflow(num_pages, (int64_t)page_size, &slot_max)) return MSA_ERR_OVERFLOW;
+    if (num_tokens == 0) return MSA_OK;
+
+    a.x = x;
+    a.x_stride = x_row_stride;
+    a.pos = positions;
+    a.seq = seq_idx;
+    a.pt = page_table;
+    a.pt_stride = page_table_stride;
+    a.num_pages = num_pages;
+    a.T = num_tokens;
+    a.S = num_seqs;
+    a.max_pages = max_pages_per_seq;
+    a.page_size = page_size;
+    a.hq = num_q_heads;
+    a.hkv = num_kv_heads;
+    a.hiq = num_iq_heads;
+    a.hik = num_ik_heads;
+    a.heads_total = (int32_t)heads_total;
+    a.npass = (int32_t)((heads_total + kHeadsPerPass - 1) / kHeadsPerPass);
+    a.eps = rms_eps;
+    a.w[0] = q_norm_weight;
+    a.w[1] = k_norm_weight;
+    a.w[2] = iq_norm_weight;
+    a.w[3] = ik_norm_weight;
+    a.q_out = q_out;
+    a.iq_out = iq_out;
+    a.slots_out = slots_out;
+    fill_inv_freq(rope_theta, a.inv_freq);
+
+    // Small batches: one wave per (token, pass) to spread latency over more waves; large
+    // batches: one wave per token so the token's RoPE coefficients are computed once.
+    int ppw;
+    if ((int64_t)num_tokens * a.npass <= 16384) ppw = 1;
+    else ppw = a.npass < kMaxPassesPerWave ? a.npass : kMaxPassesPerWave;
+    a.waves_per_token = (a.npass + ppw - 1) / ppw;
+    if ((int64_t)num_tokens * a.waves_per_token + kWavesPerBlock > 0x7fffffffLL) return MSA_ERR_SHAPE;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    switch (ppw) {
+        case 1: e = launch_produce<1>(a, s); break;
+        case 2: e = launch_produce<2>(a, s); break;
+        case 3: e = launch_produce<3>(a, s); break;
+        default: e = launch_produce<4>(a, s); break;
+    }
+    return e == hipSuccess ? MSA_OK : MSA_ERR_LAUNCH;
+}
+
+msa_status msa_rope_table(const int32_t* positions, int64_t n, double rope_theta, int32_t head_dim,
+                          float* cos_out, float* sin_out, void* stream)
+{
+    if (head_dim != kHeadDim) return MSA_ERR_UNSUPPORTED;
+    if (n < 0 || !(rope_theta > 0.0) || !std::isfinite(rope_theta) || n > ((int64_t)1 << 40)) return MSA_ERR_SHAPE;
+    if (n == 0) return MSA_OK;
+    if (!positions || !cos_out || !sin_out) return MSA_ERR_NULL_POINTER;
+    if (!aligned(positions, 4) || !aligned(cos_out, 4) || !aligned(sin_out, 4)) return MSA_ERR_ALIGNMENT;
+    FreqArgs f;
+    fill_inv_freq(rope_theta, f.inv_freq);
+    const int64_t total = n * kHalf;
+    const dim3 grid((unsigned)((total + 255) / 256));
+    if ((total + 255) / 256 > 0x7fffffffLL) return MSA_ERR_SHAPE;
+    void* args[] = {const_cast<int32_t**>(&positions), &n, &cos_out, &sin_out, &f};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&rope_table_kernel), grid, dim3(256), args, 0,
+                                         static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MSA_OK : MSA_ERR_LAUNCH;
+}
+
+msa_status msa_quantize(const float* values, int64_t n, int32_t dtype, const float* scale, void* codes_out,
+                        void* stream)
+{
+    if (dtype != MSA_CACHE_FP8_E4M3 && dtype != MSA_CACHE_BF16) return MSA_ERR_DTYPE;
+    if (n < 0 || n > ((int64_t)1 << 40)) return MSA_ERR_SHAPE;
+    if (n == 0) return MSA_OK;
+    if (!values || !codes_out) return MSA_ERR_NULL_POINTER;
+    if (dtype == MSA_CACHE_FP8_E4M3 && !scale) return MSA_ERR_DTYPE;
+    if (!aligned(values, 4) || !aligned(scale, 4) || (dtype == MSA_CACHE_BF16 && !aligned(codes_out, 2)))
+        return MSA_ERR_ALIGNMENT;
+    int32_t is_bf16 = dtype == MSA_CACHE_BF16;
+    const int64_t threads = (n + 3) / 4;
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    void* args[] = {const_cast<float**>(&values), &n, &is_bf16, const_cast<float**>(&scale), &codes_out};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&quantize_kernel), grid, dim3(256), args, 0,
+                                         static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MSA_OK : MSA_ERR_LAUNCH;
+}
+
+msa_status msa_rms_scale(const double* sum_sq, int64_t n, int32_t head_dim, float rms_eps, float* r_out,
+                         void* stream)
+{
+    if (head_dim != kHeadDim) return MSA_ERR_UNSUPPORTED;
+    if (n < 0 || n > ((int64_t)1 << 40) || !(rms_eps >= 0.0f)) return MSA_ERR_SHAPE;
+    if (n == 0) return MSA_OK;
+    if (!sum_sq || !r_out) return MSA_ERR_NULL_POINTER;
+    if (!aligned(sum_sq, 8) || !aligned(r_out, 4)) return MSA_ERR_ALIGNMENT;
+    const dim3 grid((unsigned)((n + 255) / 256));
+    void* args[] = {const_cast<double**>(&sum_sq), &n, &rms_eps, &r_out};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&rms_scale_kernel), grid, dim3(256), args, 0,
+                                         static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MSA_OK : MSA_ERR_LAUNCH;
+}
+
+const char* msa_status_string(msa_status s)
+{
+    switch (s) {
+        case MSA_OK: return "ok";
+        case MSA_ERR_NULL_POINTER: return "a required pointer is NULL";
+        case MSA_ERR_UNSUPPORTED: return "unsupported head_dim (only 128 is built)";
+        case MSA_ERR_SHAPE: return "invalid count or geometry";
+        case MSA_ERR_STRIDE: return "invalid stride (too small, overlapping, or not a multiple of 8 elements)";
+        case MSA_ERR_ALIGNMENT: return "misaligned pointer";
+        case MSA_ERR_DTYPE: return "invalid cache dtype or missing fp8 scale";
+        case MSA_ERR_OVERFLOW: return "element offset overflows int64";
+        case MSA_ERR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

@@ -300,3 +300,49 @@ def ragged(T: int, seed: int = 7, heads=DECODE_HEADS, cache_dtypes=(FP8_E4M3, FP
     caches = [_hnd_cache(num_pages, h, dt, s) for h, dt, s in zip((hkv, hkv, hik), cache_dtypes, scales)]
     return Workload(f"ragged T={T}", hq, hkv, hiq, hik, D, P, num_pages, x, pos, seq, pt, w, caches,
                     n_invalid=int(np.count_nonzero(seq < 0)))
+
+
+@dataclasses.dataclass
+class DeviceWorkload:
+    """A workload staged in device memory: inputs, zero-initialised outputs and sentinel-filled
+    caches.  `storages` are the flat cache allocations; `caches` the 4-D views handed to the
+    producer (over the first num_pages * ... elements of each storage)."""
+    x: torch.Tensor
+    positions: torch.Tensor
+    seq_idx: torch.Tensor
+    page_table: torch.Tensor
+    weights: list
+    q_out: torch.Tensor
+    iq_out: torch.Tensor
+    storages: list
+    caches: list
+    scales: list
+    slots: torch.Tensor
+
+
+def to_device(wl: Workload, device="cuda", sentinel: int = SENTINEL_BYTE) -> DeviceWorkload:
+    T, D = wl.T, wl.head_dim
+    x_full = torch.from_numpy(wl.x.view(np.int16)).to(device)
+    x = x_full[:, : wl.W]
+    pos = torch.from_numpy(wl.positions).to(device)
+    seq = torch.from_numpy(wl.seq_idx).to(device)
+    pt = torch.from_numpy(np.ascontiguousarray(wl.page_table)).to(device)
+    ws = [None if w is None else torch.from_numpy(w.view(np.int16)).to(device) for w in wl.weights]
+    q = torch.zeros((T, wl.hq, D), dtype=torch.int16, device=device)
+    iq = torch.zeros((T, wl.hiq, D), dtype=torch.int16, device=device)
+    storages, views, scales = [], [], []
+    for c in wl.caches:
+        if c.heads == 0:
+            storages.append(None)
+            views.append(None)
+            scales.append(None)
+            continue
+        if c.dtype == FP8_E4M3:
+            s = torch.full((c.storage_elems,), sentinel, dtype=torch.uint8, device=device)
+        else:
+            s = torch.full((c.storage_elems,), sentinel * 0x0101, dtype=torch.int16, device=device)
+        storages.append(s)
+        views.append(s.as_strided((wl.num_pages, c.heads, wl.page_size, D), (*c.strides, 1)))
+        scales.append(torch.tensor([c.scale], dtype=torch.float32, device=device))
+    slots = torch.full((T,), -7, dtype=torch.int64, device=device)
+    return DeviceWorkload(x, pos, seq, pt, ws, q, iq, storages, views, scales, slots)

@@ -1,0 +1,155 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point that
+include/msa_produce.h declares, and rejects invalid arguments on the host before any launch
+(so no call here reaches the device; every pointer below is a never-dereferenced address)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_msa_amd as msa
+from paged_kv_cache_msa_amd import _build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa_produce.h")
+
+OK, NULLP, UNSUP, SHAPE, STRIDE, ALIGN, DTYPE, OVERFLOW = 0, 1, 2, 3, 4, 5, 6, 7
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(msa.LIB_PATH):
+        _build.build()
+    return msa.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(names) >= {"msa_produce", "msa_rope_table", "msa_quantize", "msa_rms_scale", "msa_status_string"}
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code in range(9):
+        assert msa.string(code) and msa.string(code) != "unknown status"
+    assert msa.string(99) == "unknown status"
+
+
+# Fake, aligned device addresses: validation returns before anything could dereference them.
+X, POS, SEQ, PT, W, Q, IQ, SLOTS, DATA, SCALE = (0x10000 * (i + 1) for i in range(10))
+
+
+def view(data=DATA, sp=2 * 64 * 128, sh=64 * 128, st=128, heads=2, dtype=0, scale=SCALE):
+    return msa.MsaCacheView(data, sp, sh, st, heads, dtype, scale)
+
+
+def call(L, **kw):
+    a = dict(x=X, xs=2944, T=64, D=128, hq=16, hkv=2, hiq=2, hik=1, pos=POS, seq=SEQ, pt=PT, pts=160, S=64,
+             maxp=160, P=64, pages=10240, wq=W, wk=W, wiq=W, wik=W, eps=1e-6, theta=1e4, q=Q, iq=IQ,
+             k=view(), v=view(), ik=view(sp=64 * 128, heads=1), slots=SLOTS, stream=None, force_T0=True)
+    a.update(kw)
+    T = 0 if a.pop("force_T0") and kw.get("T") is None else a["T"]
+    ref = lambda v: None if v is None else ctypes.byref(v)
+    return L.msa_produce(a["x"], a["xs"], T, a["D"], a["hq"], a["hkv"], a["hiq"], a["hik"], a["pos"], a["seq"],
+                         a["pt"], a["pts"], a["S"], a["maxp"], a["P"], a["pages"], a["wq"], a["wk"], a["wiq"],
+                         a["wik"], a["eps"], a["theta"], a["q"], a["iq"], ref(a["k"]), ref(a["v"]), ref(a["ik"]),
+                         a["slots"], a["stream"])
+
+
+def test_valid_arguments_with_zero_tokens_enqueue_nothing(L):
+    assert call(L) == OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=64), UNSUP),
+    (dict(T=-1), SHAPE),
+    (dict(hq=-1), SHAPE),
+    (dict(hq=0, hkv=0, hiq=0, hik=0, k=None, v=None, ik=None), SHAPE),
+    (dict(P=0), SHAPE),
+    (dict(pages=-1), SHAPE),
+    (dict(eps=-1.0), SHAPE),
+    (dict(theta=0.0), SHAPE),
+    (dict(xs=2943), STRIDE),
+    (dict(xs=2948), STRIDE),
+    (dict(pts=100), STRIDE),
+    (dict(wq=None), NULLP),
+    (dict(wik=None), NULLP),
+    (dict(k=None), NULLP),
+    (dict(v=view(data=None)), NULLP),
+    (dict(x=X + 8), ALIGN),
+    (dict(q=Q + 2), ALIGN),
+    (dict(slots=SLOTS + 4), ALIGN),
+    (dict(wk=W + 2), ALIGN),
+    (dict(k=view(data=DATA + 8)), ALIGN),
+    (dict(k=view(heads=3)), SHAPE),
+    (dict(ik=view(heads=2)), SHAPE),
+    (dict(k=view(dtype=7)), DTYPE),
+    (dict(k=view(scale=None)), DTYPE),
+    (dict(k=view(st=64)), STRIDE),                       # token rows overlap within a head
+    (dict(k=view(sh=128)), STRIDE),                      # heads overlap tokens
+    (dict(k=view(sp=64 * 128)), STRIDE),                 # pages overlap heads
+    (dict(k=view(st=132)), STRIDE),                      # not a multiple of 8 elements
+    (dict(k=view(sp=-16384)), STRIDE),
+    (dict(pages=1 << 50), OVERFLOW),
+])
+def test_rejects_invalid_arguments(L, kw, status):
+    assert call(L, **kw) == status
+
+
+def test_bf16_cache_needs_no_scale(L):
+    assert call(L, k=view(dtype=1, scale=None), v=view(dtype=1, scale=None)) == OK
+
+
+def test_permuted_nhd_storage_view_is_accepted(L):
+    """An NHD allocation [pages, tokens, heads, D] seen as an HND view is a legal strided layout."""
+    nhd = view(sp=64 * 2 * 128, sh=128, st=2 * 128)
+    assert call(L, k=nhd, v=nhd) == OK
+
+
+def test_padded_head_stride_view_is_accepted(L):
+    padded = view(sp=2 * 65 * 128, sh=65 * 128, st=128)
+    assert call(L, k=padded, v=padded) == OK
+
+
+def test_index_k_optional(L):
+    assert call(L, hik=0, wik=None, ik=None, xs=2816) == OK
+
+
+def test_step_entry_points_validate(L):
+    assert L.msa_rope_table(POS, 10, 1e4, 64, X, Q, None) == UNSUP
+    assert L.msa_rope_table(POS, -1, 1e4, 128, X, Q, None) == SHAPE
+    assert L.msa_rope_table(None, 10, 1e4, 128, X, Q, None) == NULLP
+    assert L.msa_rope_table(POS, 0, 1e4, 128, None, None, None) == OK
+    assert L.msa_quantize(X, 10, 3, SCALE, Q, None) == DTYPE
+    assert L.msa_quantize(X, 10, 0, None, Q, None) == DTYPE
+    assert L.msa_quantize(X + 2, 10, 0, SCALE, Q, None) == ALIGN
+    assert L.msa_quantize(X, 0, 0, SCALE, Q, None) == OK
+    assert L.msa_rms_scale(X, 10, 127, 1e-6, Q, None) == UNSUP
+    assert L.msa_rms_scale(X + 4, 10, 128, 1e-6, Q, None) == ALIGN
+    assert L.msa_rms_scale(X, 10, 128, -1.0, Q, None) == SHAPE
+
+
+def test_python_binding_raises_when_library_missing(monkeypatch, tmp_path):
+    monkeypatch.setattr(msa, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(msa, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        msa.lib()
+
+
+def _has_gpu():
+    import torch
+    return torch.cuda.device_count() > 0
+
+
+@pytest.mark.skipif(_has_gpu(), reason="fake addresses with T > 0 are only exercised where no device exists")
+@pytest.mark.parametrize("kw", [dict(x=None), dict(pos=None), dict(seq=None), dict(q=None), dict(iq=None),
+                                dict(pt=None)])
+def test_rejects_null_inputs_with_tokens(L, kw):
+    assert call(L, T=64, **kw) == NULLP

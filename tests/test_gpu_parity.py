@@ -1,0 +1,327 @@
+"""GPU parity: the HIP producer (through the C ABI) against the CPU oracle, element by element.
+
+Bar (per element): slots and every cache byte bit-exact; Q and index-Q within one bf16 ulp
+(|gpu - oracle| <= 2^-7 |oracle|, NaN where the oracle has NaN); untouched cache bytes keep
+the sentinel.  Workloads: the tiny decode (W = 1024) and its no-index-K variant (W = 896), decode
+batch 64, decode batch 256 with padded / out-of-pool tokens and strided input and cache views,
+the 65,536-token prefill, the mixed batch whose cache offsets exceed 32 bits (bf16 and fp8), and
+ragged token counts that leave partial work-groups and exercise every launch shape.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_msa_amd as msa
+from paged_kv_cache_msa_amd import workloads as W
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+THREADS = min(16, os.cpu_count() or 1)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    msa.lib()
+
+
+def say(*a):
+    print(*a, flush=True, file=sys.stderr)
+
+
+def run(wl):
+    d = W.to_device(wl)
+    say(f"[gpu] msa_produce {wl.name}: T={wl.T} heads={wl.hq}/{wl.hkv}/{wl.hiq}/{wl.hik}")
+    msa.msa_produce(d.x, d.positions, d.seq_idx, d.page_table, *d.weights, d.q_out, d.iq_out,
+                    d.caches[0], d.caches[1], d.caches[2], k_scale=d.scales[0], v_scale=d.scales[1],
+                    ik_scale=d.scales[2], num_pages=wl.num_pages, rms_eps=wl.eps, rope_theta=wl.theta,
+                    slots_out=d.slots)
+    torch.cuda.synchronize()
+    return d
+
+
+def check_q(name, gpu_bits, ref_bits):
+    g = H.bf16_bits_to_f32(gpu_bits).astype(np.float64)
+    r = H.bf16_bits_to_f32(ref_bits).astype(np.float64)
+    nan_g, nan_r = np.isnan(g), np.isnan(r)
+    assert np.array_equal(nan_g, nan_r), f"{name}: NaN positions differ"
+    fin = ~nan_r
+    with np.errstate(invalid="ignore"):
+        ok = (g[fin] == r[fin]) | (np.abs(g[fin] - r[fin]) <= 2.0 ** -7 * np.abs(r[fin]))
+    bad = np.flatnonzero(~ok)
+    assert bad.size == 0, f"{name}: {bad.size} elements beyond 1 bf16 ulp, first {g[fin][bad[:4]]} vs {r[fin][bad[:4]]}"
+    n_inexact = int(np.count_nonzero(gpu_bits != ref_bits))
+    say(f"  {name}: within 1 bf16 ulp; bit-identical elements {gpu_bits.size - n_inexact}/{gpu_bits.size}")
+
+
+def is_nan_code(c, dtype):
+    c = np.asarray(c)
+    if dtype == W.FP8_E4M3:
+        return (c & 0x7F) == 0x7F
+    return (c & 0x7FFF) > 0x7F80
+
+
+def code_diff(gpu, ref, dtype):
+    """Indices where two cache-code arrays disagree.  Codes must be identical except where the
+    oracle's code is a NaN: which NaN (sign, payload) an IEEE-754 operation returns is not fixed
+    by the standard (x86 and the GPU differ), so there the GPU code only has to be a NaN too."""
+    nan_r = is_nan_code(ref, dtype)
+    ok = np.where(nan_r, is_nan_code(gpu, dtype), gpu == ref)
+    return np.flatnonzero(~ok)
+
+
+def check(wl, d, full=None):
+    """Compare a device result with the oracle.  full=True compares whole cache storages against the
+    oracle's cache form; otherwise rows are gathered at the oracle's slots and the untouched count
+    is checked on the device."""
+    if full is None:
+        full = all(c.storage_elems <= (1 << 26) for c in wl.caches)
+    ref = H.oracle_rows(wl, num_threads=THREADS)
+    slots = d.slots.cpu().numpy()
+    np.testing.assert_array_equal(slots, ref["slots"])
+    check_q("q", d.q_out.cpu().numpy().view(np.uint16), ref["q"])
+    check_q("iq", d.iq_out.cpu().numpy().view(np.uint16), ref["iq"])
+    valid = np.flatnonzero(ref["slots"] >= 0)
+    if full:
+        _, st = H.oracle_caches(wl)
+        for name, spec, s_ref, s_gpu in zip(("k", "v", "ik"), wl.caches, st, d.storages):
+            if spec.heads == 0:
+                continue
+            g = s_gpu.cpu().numpy()
+            g = g.view(np.uint8) if spec.dtype == W.FP8_E4M3 else g.view(np.uint16)
+            diff = code_diff(g, s_ref.reshape(-1), spec.dtype)
+            assert diff.size == 0, f"{name} cache: {diff.size} elements differ, first at {diff[:4]}"
+        say(f"  caches: whole storages byte-identical ({len(valid)} tokens written)")
+        return
+    pg = torch.from_numpy(ref["slots"][valid] // wl.page_size).cuda()
+    off = torch.from_numpy(ref["slots"][valid] % wl.page_size).cuda()
+    for name, spec, view, store in zip(("k", "v", "ik"), wl.caches, d.caches, d.storages):
+        if spec.heads == 0:
+            continue
+        rows = view[pg, :, off, :].cpu().numpy()          # [n_valid, H, D]
+        rows = rows.view(np.uint8) if spec.dtype == W.FP8_E4M3 else rows.view(np.uint16)
+        exp = ref[name][valid]
+        diff = code_diff(rows.reshape(-1), exp.reshape(-1), spec.dtype)
+        assert diff.size == 0, f"{name} cache rows: {len(diff)} elements differ, first {diff[:4]}"
+        sent = W.SENTINEL_BYTE if spec.dtype == W.FP8_E4M3 else W.SENTINEL_BYTE * 0x0101
+        changed = int((store != sent).sum().item())
+        assert changed == len(valid) * spec.heads * wl.head_dim, f"{name}: {changed} elements changed"
+    say(f"  caches: gathered rows byte-identical, untouched count exact ({len(valid)} tokens written)")
+
+
+@pytest.mark.parametrize("make", [W.config0, W.config0b], ids=["tiny-w1024", "tiny-w896-no-index-k"])
+def test_tiny_decode(make):
+    wl = make()
+    check(wl, run(wl), full=True)
+
+
+def test_decode_batch_64():
+    wl = W.config1()
+    check(wl, run(wl))
+
+
+def test_decode_batch_256_padded_strided():
+    wl = W.config2()
+    d = run(wl)
+    assert int((d.slots < 0).sum()) == 31
+    check(wl, d)
+
+
+def test_prefill_65536():
+    wl = W.config3()
+    check(wl, run(wl))
+
+
+@pytest.mark.parametrize("dtype", [W.BF16, W.FP8_E4M3], ids=["bf16", "fp8"])
+def test_mixed_64bit_offsets(dtype):
+    wl = W.config4(dtype)
+    assert wl.num_pages * wl.caches[2].strides[0] > 2 ** 31
+    d = run(wl)
+    check(wl, d)
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("T,heads,dtypes,pad", [
+    (1, W.DECODE_HEADS, (0, 0, 0), 0.0),
+    (3, (4, 1, 1, 1), (1, 1, 1), 0.5),
+    (7, (5, 3, 0, 2), (0, 1, 0), 0.2),
+    (63, (16, 2, 2, 0), (0, 0, 0), 0.1),
+    (65, (0, 1, 0, 1), (1, 0, 1), 0.1),
+    (255, (8, 1, 8, 1), (0, 0, 1), 0.0),
+    (1000, W.DECODE_HEADS, (1, 1, 0), 0.1),
+    (2049, (1, 1, 1, 1), (0, 0, 0), 0.05),
+    (5000, (32, 2, 2, 1), (0, 0, 0), 0.1),     # 5 passes: two waves per token
+    (9000, (8, 2, 2, 1), (0, 1, 0), 0.1),      # 2 passes per wave
+    (20001, W.DECODE_HEADS, (0, 0, 0), 0.1),   # 3 passes per wave, ragged last block
+])
+def test_ragged_and_launch_shapes(T, heads, dtypes, pad):
+    wl = W.ragged(T, seed=T, heads=heads, cache_dtypes=dtypes, pad_frac=pad, row_pad=8 * (T % 3))
+    check(wl, run(wl))
+
+
+def test_special_values():
+    """NaN, infinities, huge and tiny values, all-zero heads and saturating scales."""
+    wl = W.ragged(64, seed=77, cache_dtypes=(0, 0, 1), pad_frac=0.0)
+    rng = np.random.default_rng(1)
+    specials = np.array([0x7FC0, 0xFFC0, 0x7F81, 0x7F80, 0xFF80, 0x7F7F, 0xFF7F, 0x0001, 0x8001, 0x0000, 0x8000],
+                        np.uint16)
+    flat = wl.x.reshape(-1)
+    idx = rng.choice(flat.size, 400, replace=False)
+    flat[idx] = rng.choice(specials, idx.size)
+    wl.x[5, :] = 0                                  # every head of token 5 all-zero
+    wl.x[6, : 128 * 20] = 0x4380                    # 256.0: saturates the fp8 cast after scaling
+    wl.caches[0].scale = 0.01
+    wl.caches[1].scale = 1e-3
+    check(wl, run(wl), full=True)
+
+
+# ------------------------------------------------------------------ step-level entry points
+
+def test_rope_table_exhaustive_configs_domain():
+    """Every position in [0, 131072) at theta = 1e4 (all configs' positions) against the oracle,
+    bit for bit."""
+    import oracle
+    pos = np.arange(131072, dtype=np.int32)
+    dp = torch.from_numpy(pos).cuda()
+    c = torch.empty((pos.size, 64), dtype=torch.float32, device="cuda")
+    s = torch.empty_like(c)
+    msa.msa_rope_table(dp, c, s, 1e4)
+    torch.cuda.synchronize()
+    rc, rs = oracle.rope_table(pos, 1e4, 128)
+    assert np.array_equal(c.cpu().numpy().view(np.uint32), rc.view(np.uint32))
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+
+
+def test_rope_table_other_theta_sampled():
+    import oracle
+    rng = np.random.default_rng(3)
+    for theta in (1e6, 5e5, 1e4):
+        pos = np.concatenate([rng.integers(-2 ** 31, 2 ** 31 - 1, 20000), [0, 1, -1, 2 ** 31 - 1, -2 ** 31]]).astype(np.int32)
+        dp = torch.from_numpy(pos).cuda()
+        c = torch.empty((pos.size, 64), dtype=torch.float32, device="cuda")
+        s = torch.empty_like(c)
+        msa.msa_rope_table(dp, c, s, theta)
+        torch.cuda.synchronize()
+        rc, rs = oracle.rope_table(pos, theta, 128)
+        gc, gs = c.cpu().numpy(), s.cpu().numpy()
+        n_diff = int(np.count_nonzero(gc.view(np.uint32) != rc.view(np.uint32)) +
+                     np.count_nonzero(gs.view(np.uint32) != rs.view(np.uint32)))
+        assert np.all(np.abs(gc.astype(np.float64) - rc) <= H.ulp32(rc)), theta
+        assert np.all(np.abs(gs.astype(np.float64) - rs) <= H.ulp32(rs)), theta
+        say(f"  rope theta={theta}: {n_diff} of {2 * gc.size} coefficients differ by one ulp")
+
+
+def _encode_chunks(fn, values, threads=THREADS):
+    from concurrent.futures import ThreadPoolExecutor
+    parts = np.array_split(values, threads)
+    with ThreadPoolExecutor(threads) as ex:
+        return np.concatenate(list(ex.map(fn, parts)))
+
+
+@pytest.mark.timeout(900)
+def test_quantize_exhaustive_fp32():
+    """All 2^32 binary32 inputs through the device casts (scale 1 for fp8) against the oracle."""
+    import oracle
+    one = torch.ones(1, dtype=torch.float32, device="cuda")
+    chunk = 1 << 28
+    for base in range(0, 1 << 32, chunk):
+        u = np.arange(base, base + chunk, dtype=np.uint64).astype(np.uint32)
+        v = u.view(np.float32)
+        dv = torch.from_numpy(v).cuda()
+        out8 = torch.empty(chunk, dtype=torch.uint8, device="cuda")
+        out16 = torch.empty(chunk, dtype=torch.int16, device="cuda")
+        msa.msa_quantize(dv, out8, msa.MSA_CACHE_FP8_E4M3, one)
+        msa.msa_quantize(dv, out16, msa.MSA_CACHE_BF16)
+        torch.cuda.synchronize()
+        g8 = out8.cpu().numpy()
+        g16 = out16.cpu().numpy().view(np.uint16)
+        r8 = _encode_chunks(oracle.encode_e4m3, v)
+        r16 = _encode_chunks(oracle.encode_bf16, v)
+        bad8, bad16 = np.flatnonzero(g8 != r8), np.flatnonzero(g16 != r16)
+        assert bad8.size == 0, f"e4m3: {bad8.size} mismatches from 0x{base:08x}, first input 0x{u[bad8[0]]:08x}"
+        assert bad16.size == 0, f"bf16: {bad16.size} mismatches from 0x{base:08x}, first input 0x{u[bad16[0]]:08x}"
+        del dv, out8, out16
+        say(f"  quantize chunk 0x{base:08x} ok")
+    say("  quantize: all 2^32 inputs identical for e4m3 (scale 1) and bf16")
+
+
+def test_quantize_scales():
+    """e4m3(v * fl32(1/scale)) for many scales: exercises the binary32 reciprocal's rounding."""
+    import oracle
+    rng = np.random.default_rng(4)
+    v = (rng.standard_normal(1 << 20) * 30).astype(np.float32)
+    for sc in np.concatenate([rng.uniform(0.5, 2.0, 24), [3.0, 7.0, 0.1, 1e-3, 448.0, 1e-30, 1e30]]).astype(np.float32):
+        dv = torch.from_numpy(v).cuda()
+        ds = torch.tensor([sc], dtype=torch.float32, device="cuda")
+        out = torch.empty(v.size, dtype=torch.uint8, device="cuda")
+        msa.msa_quantize(dv, out, msa.MSA_CACHE_FP8_E4M3, ds)
+        torch.cuda.synchronize()
+        inv = np.float32(1.0) / sc
+        ref = oracle.encode_e4m3((v * inv).astype(np.float32))
+        assert np.array_equal(out.cpu().numpy(), ref), float(sc)
+
+
+def test_rms_scale_random_and_edges():
+    import oracle
+    rng = np.random.default_rng(5)
+    ss = np.concatenate([rng.uniform(0, 2000, 1 << 20), np.exp2(rng.uniform(-300, 300, 1 << 18)),
+                         [0.0, 1e-300, 128.0, 1e300]]).astype(np.float64)
+    for eps in (1e-6, 0.0, 1e-5, 0.5):
+        d = torch.from_numpy(ss).cuda()
+        r = torch.empty(ss.size, dtype=torch.float32, device="cuda")
+        msa.msa_rms_scale(d, r, eps)
+        torch.cuda.synchronize()
+        ref = oracle.rms_scale(ss, 128, eps)
+        assert np.array_equal(r.cpu().numpy().view(np.uint32), ref.view(np.uint32)), eps
+
+
+# ------------------------------------------------------------------ HIP graph replay
+
+def test_graph_replay_matches_eager():
+    """Three layer calls captured in one HIP graph: every replay (with eager work and
+    synchronisation between replays) writes exactly what the eager calls wrote."""
+    layers = [W.config1(layer=i) for i in range(3)]
+    devs = [W.to_device(wl) for wl in layers]
+
+    def call(wl, d):
+        msa.msa_produce(d.x, d.positions, d.seq_idx, d.page_table, *d.weights, d.q_out, d.iq_out,
+                        d.caches[0], d.caches[1], d.caches[2], k_scale=d.scales[0], v_scale=d.scales[1],
+                        ik_scale=d.scales[2], num_pages=wl.num_pages, slots_out=d.slots)
+
+    for wl, d in zip(layers, devs):
+        call(wl, d)
+    torch.cuda.synchronize()
+    eager = [(d.q_out.clone(), d.iq_out.clone(), [s.clone() for s in d.storages]) for d in devs]
+    for d in devs:
+        d.q_out.zero_()
+        d.iq_out.zero_()
+        for s in d.storages:
+            s.fill_(W.SENTINEL_BYTE if s.dtype == torch.uint8 else W.SENTINEL_BYTE * 0x0101)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for wl, d in zip(layers, devs):
+                call(wl, d)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(4):
+        if rep:
+            # eager work between replays: clobber the outputs the graph rewrites
+            for d in devs:
+                d.q_out.fill_(3)
+                d.iq_out.fill_(3)
+            torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for (q, iq, sts), d in zip(eager, devs):
+            assert torch.equal(q, d.q_out) and torch.equal(iq, d.iq_out), rep
+            for a, b in zip(sts, d.storages):
+                assert torch.equal(a, b), rep
+    check(layers[0], devs[0])
