@@ -56,7 +56,7 @@ struct ProduceArgs {
     const int32_t* pt;
     int64_t pt_stride;
     int64_t num_pages;
-    int32_t T, S, max_pages, page_size;
+    int32_t T, S, max_pages, page_size, page_shift;   // page_shift = log2(page_size), or -1
     int32_t hq, hkv, hiq, hik, heads_total, npass, waves_per_token;
     float eps;
     const uint16_t* w[4];      // norm weights of Q, K, index-Q, index-K
@@ -150,82 +150,136 @@ __device__ __forceinline__ double head_sum8(double v)
     return v;
 }
 
-__device__ __forceinline__ void wave_lds_sync()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // ------------------------------------------------------------------ producer kernel
 
-template <int PPW>
+// Per-lane fp8 cast of 16 values (scaled by m) into two 8-byte halves.  When no value of the lane
+// needs saturation or NaN handling (|v| <= 448), the bare hardware conversion already is the exact
+// saturating RNE cast; otherwise the full cast runs.
+__device__ __forceinline__ void e4m3x16(const float* o, float m, uint2& lo, uint2& hi)
+{
+    float z[16];
+    bool special = false;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        z[j] = o[j] * m;
+        special |= !(fabsf(z[j]) <= 448.0f);
+    }
+    uint32_t w[4];
+    if (!special) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t l = __builtin_amdgcn_cvt_pk_fp8_f32(z[4 * q], z[4 * q + 1], 0, false);
+            w[q] = __builtin_amdgcn_cvt_pk_fp8_f32(z[4 * q + 2], z[4 * q + 3], l, true);
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[q] = e4m3x4(z[4 * q], z[4 * q + 1], z[4 * q + 2], z[4 * q + 3]);
+    }
+    lo = make_uint2(w[0], w[1]);
+    hi = make_uint2(w[2], w[3]);
+}
+
+__device__ __forceinline__ uint4 bf16x8(const float* o)
+{
+    return make_uint4(bf16x2(o[0], o[1]), bf16x2(o[2], o[3]), bf16x2(o[4], o[5]), bf16x2(o[6], o[7]));
+}
+
+// One producer launch.  PPW = passes (groups of 8 heads) per wave.  HQ..HIK fix the head
+// geometry at compile time (the stream of every head slot then folds to constants); all four
+// negative selects the generic build that reads the geometry from the arguments.
+template <int PPW, int HQ, int HKV, int HIQ, int HIK>
 __global__ __launch_bounds__(kBlock) void produce_kernel(const ProduceArgs a)
 {
+    constexpr bool kFixed = HQ >= 0;
+    constexpr int kTotal = HQ + 2 * HKV + HIQ + HIK;
+    constexpr int kNpass = kFixed ? (kTotal + kHeadsPerPass - 1) / kHeadsPerPass : -1;
+    // With a fixed geometry whose passes all fit one wave, every wave starts at pass 0.
+    constexpr bool kWholeToken = kFixed && kNpass <= PPW;
+    // Several passes per wave: stage the norm weights once per block in LDS.
+    constexpr bool kStageW = PPW > 1;
+
+    const int hq = kFixed ? HQ : a.hq;
+    const int hkv = kFixed ? HKV : a.hkv;
+    const int hiq = kFixed ? HIQ : a.hiq;
+    const int heads_total = kFixed ? kTotal : a.heads_total;
+    const int npass = kFixed ? kNpass : a.npass;
+    const int h_k = hq, h_v = hq + hkv, h_iq = hq + 2 * hkv, h_ik = h_iq + hiq;
+
+    __shared__ __attribute__((aligned(16))) float w_lds[kStageW ? 4 : 1][kHeadDim];
     __shared__ __attribute__((aligned(16))) float cs_lds[kWavesPerBlock][2 * kHalf];
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const uint32_t item = blockIdx.x * kWavesPerBlock + wave;
-    if (item >= (uint32_t)a.T * (uint32_t)a.waves_per_token) return;   // wave-uniform; no block barrier follows
-    const uint32_t wpt = a.waves_per_token;
-    const int32_t t = wpt == 1 ? (int32_t)item : (int32_t)(item / wpt);
-    const int32_t chunk = (int32_t)(item - (uint32_t)t * wpt);
-
-    // Token metadata, once per wave.
-    const int32_t pos = a.pos[t];
-    const int32_t sq = a.seq[t];
-    int64_t page = -1;
-    int32_t off = 0;
-    if (sq >= 0 && sq < a.S && pos >= 0) {
-        const int32_t lp = pos / a.page_size;
-        if (lp < a.max_pages) {
-            const int64_t pg = a.pt[(int64_t)sq * a.pt_stride + lp];
-            if (pg >= 0 && pg < a.num_pages) {
-                page = pg;
-                off = pos - lp * a.page_size;
-            }
-        }
+    const bool live = item < (uint32_t)a.T * (uint32_t)a.waves_per_token;   // wave-uniform
+    int32_t t, chunk;
+    if (kWholeToken || a.waves_per_token == 1) {
+        t = (int32_t)item;
+        chunk = 0;
+    } else {
+        t = (int32_t)(item / (uint32_t)a.waves_per_token);
+        chunk = (int32_t)(item - (uint32_t)t * (uint32_t)a.waves_per_token);
     }
-    const bool valid = page >= 0;
-    if (chunk == 0 && lane == 0 && a.slots_out) a.slots_out[t] = valid ? page * a.page_size + off : -1;
+    const int pass0 = kWholeToken ? 0 : chunk * PPW;
 
-    // Issue the row loads of every pass of this wave before any arithmetic.
     const int hs = lane / kLanesPerHead;   // head slot within a pass
     const int sub = lane % kLanesPerHead;  // element group within the head
-    const int pass0 = chunk * PPW;
-    const uint16_t* row = a.x + (int64_t)t * a.x_stride;
-    const int h_k = a.hq, h_v = a.hq + a.hkv, h_iq = a.hq + 2 * a.hkv, h_ik = h_iq + a.hiq;
 
-    uint4 xa[PPW], xb[PPW], wa[PPW], wb[PPW];
-    int hh[PPW];
+    // Row loads of every pass of this wave, issued first.  Slots past the last head (and waves
+    // past the last token) read the token's first head instead, a valid address, and discard it.
+    const int32_t t_ld = live ? t : 0;
+    const uint16_t* row = a.x + (int64_t)t_ld * a.x_stride + sub * 8;
+    uint4 xa[PPW], xb[PPW];
 #pragma unroll
     for (int k = 0; k < PPW; ++k) {
-        const int pass = pass0 + k;
-        hh[k] = pass * kHeadsPerPass + hs;
-        xa[k] = xb[k] = wa[k] = wb[k] = make_uint4(0, 0, 0, 0);
-        if (pass < a.npass && hh[k] < a.heads_total) {
-            const uint16_t* hp = row + (int64_t)hh[k] * kHeadDim + sub * 8;
-            xa[k] = *reinterpret_cast<const uint4*>(hp);
-            xb[k] = *reinterpret_cast<const uint4*>(hp + kHalf);
-            const int h = hh[k];
-            const uint16_t* w = h < h_k ? a.w[0] : h < h_v ? a.w[1] : h < h_iq ? nullptr : h < h_ik ? a.w[2] : a.w[3];
-            if (w) {
-                wa[k] = *reinterpret_cast<const uint4*>(w + sub * 8);
-                wb[k] = *reinterpret_cast<const uint4*>(w + kHalf + sub * 8);
-            }
+        const int h = (pass0 + k) * kHeadsPerPass + hs;
+        const uint16_t* hp = row + (h < heads_total ? h : 0) * kHeadDim;
+        xa[k] = *reinterpret_cast<const uint4*>(hp);
+        xb[k] = *reinterpret_cast<const uint4*>(hp + kHalf);
+    }
+
+    if (kStageW) {
+        for (int i = threadIdx.x; i < 4 * kHeadDim; i += kBlock) {
+            const uint16_t* w = a.w[i / kHeadDim];
+            w_lds[i / kHeadDim][i % kHeadDim] = w ? __uint_as_float((uint32_t)w[i % kHeadDim] << 16) : 0.0f;
         }
     }
 
-    // RoPE coefficients of this token: lane i computes frequency i; lane `sub` then needs
-    // frequencies [8 sub, 8 sub + 8).
-    {
+    // Token metadata, once per wave.
+    int64_t page = -1;
+    int32_t off = 0;
+    if (live) {
+        const int32_t pos = a.pos[t];
+        const int32_t sq = a.seq[t];
+        if (sq >= 0 && sq < a.S && pos >= 0) {
+            const int32_t lp = a.page_shift >= 0 ? pos >> a.page_shift : pos / a.page_size;
+            if (lp < a.max_pages) {
+                const int64_t pg = a.pt[(int64_t)sq * a.pt_stride + lp];
+                if (pg >= 0 && pg < a.num_pages) {
+                    page = pg;
+                    off = pos - lp * a.page_size;
+                }
+            }
+        }
+        // RoPE coefficients of this token: lane i computes frequency i.
         float c, s;
         rope_coeff(pos, a.inv_freq[lane], &c, &s);
         cs_lds[wave][lane] = c;
         cs_lds[wave][kHalf + lane] = s;
     }
-    wave_lds_sync();
+    if (kStageW) {
+        __syncthreads();
+        if (!live) return;   // no block barrier after this point
+    } else {
+        if (!live) return;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+
+    const bool valid = page >= 0;
+    if (chunk == 0 && lane == 0 && a.slots_out) a.slots_out[t] = valid ? page * a.page_size + off : -1;
+
     float cf[8], sf[8];
     {
         const float4* cp = reinterpret_cast<const float4*>(&cs_lds[wave][sub * 8]);
@@ -235,80 +289,92 @@ __global__ __launch_bounds__(kBlock) void produce_kernel(const ProduceArgs a)
         sf[0] = s0.x; sf[1] = s0.y; sf[2] = s0.z; sf[3] = s0.w; sf[4] = s1.x; sf[5] = s1.y; sf[6] = s1.z; sf[7] = s1.w;
     }
 
-    float inv_sc[3];
+    // Unpack every pass once; sums of squares in binary64 (each square exact), reduced over the
+    // 8 lanes of each head.
+    float v[PPW][16];
+    double ss[PPW];
 #pragma unroll
-    for (int ci = 0; ci < 3; ++ci)
-        inv_sc[ci] = (a.cache[ci].heads > 0 && !a.cache[ci].is_bf16) ? inv_scale_of(a.cache[ci].scale) : 1.0f;
-    int64_t cache_base[3];
+    for (int k = 0; k < PPW; ++k) {
+        unpack8(xa[k], v[k]);
+        unpack8(xb[k], v[k] + 8);
+        double acc = 0.0;
 #pragma unroll
-    for (int ci = 0; ci < 3; ++ci) cache_base[ci] = valid ? page * a.cache[ci].sp + (int64_t)off * a.cache[ci].st : 0;
+        for (int j = 0; j < 16; ++j) acc = __builtin_fma((double)v[k][j], (double)v[k][j], acc);
+        ss[k] = head_sum8(acc);
+    }
+    // RMSNorm scales: with several passes, lane `sub` of a head group computes the scale of pass
+    // `sub` once and the group reads it back.
+    float r[PPW];
+    if (PPW == 1) {
+        r[0] = rms_from_ss(ss[0], a.eps);
+    } else {
+        double mine = ss[0];
+#pragma unroll
+        for (int k = 1; k < PPW; ++k)
+            if (sub == k) mine = ss[k];
+        const float rm = rms_from_ss(mine, a.eps);
+#pragma unroll
+        for (int k = 0; k < PPW; ++k) r[k] = __shfl(rm, hs * kLanesPerHead + k);
+    }
 
 #pragma unroll
     for (int k = 0; k < PPW; ++k) {
         const int pass = pass0 + k;
-        if (pass >= a.npass) break;                 // wave-uniform
-        const int h = hh[k];
-        const bool act = h < a.heads_total;
+        if (pass >= npass) break;                   // wave-uniform
+        const int h = pass * kHeadsPerPass + hs;
+        // Slots past the last head compute as the last head (its stream has heads, so its weight
+        // pointer is valid) and store nothing.
+        const int hc = h < heads_total ? h : heads_total - 1;
+        const int st = hc < h_k ? kQ : hc < h_v ? kK : hc < h_iq ? kV : hc < h_ik ? kIQ : kIK;
 
-        float v[16], wv[16];
-        unpack8(xa[k], v);
-        unpack8(xb[k], v + 8);
-        unpack8(wa[k], wv);
-        unpack8(wb[k], wv + 8);
-
-        // Per-head sum of squares in binary64 (each square is exact), reduced over 8 lanes.
-        double ss = 0.0;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) ss = __builtin_fma((double)v[j], (double)v[j], ss);
-        ss = head_sum8(ss);
-        const float r = rms_from_ss(ss, a.eps);
-
-        const int st = h < h_k ? kQ : h < h_v ? kK : h < h_iq ? kV : h < h_ik ? kIQ : kIK;
         float o[16];
         if (st == kV) {
 #pragma unroll
-            for (int j = 0; j < 16; ++j) o[j] = v[j];
+            for (int j = 0; j < 16; ++j) o[j] = v[k][j];
         } else {
+            const int ws = st == kQ ? 0 : st == kK ? 1 : st == kIQ ? 2 : 3;
+            float wv[16];
+            if (kStageW) {
+                const float4* wp = reinterpret_cast<const float4*>(&w_lds[ws][sub * 8]);
+                const float4* wq = reinterpret_cast<const float4*>(&w_lds[ws][kHalf + sub * 8]);
+                const float4 w0 = wp[0], w1 = wp[1], w2 = wq[0], w3 = wq[1];
+                wv[0] = w0.x; wv[1] = w0.y; wv[2] = w0.z; wv[3] = w0.w; wv[4] = w1.x; wv[5] = w1.y; wv[6] = w1.z; wv[7] = w1.w;
+                wv[8] = w2.x; wv[9] = w2.y; wv[10] = w2.z; wv[11] = w2.w; wv[12] = w3.x; wv[13] = w3.y; wv[14] = w3.z; wv[15] = w3.w;
+            } else {
+                const uint16_t* w = a.w[ws] + sub * 8;
+                unpack8(*reinterpret_cast<const uint4*>(w), wv);
+                unpack8(*reinterpret_cast<const uint4*>(w + kHalf), wv + 8);
+            }
             float y[16];
 #pragma unroll
-            for (int j = 0; j < 16; ++j) y[j] = (v[j] * r) * wv[j];
+            for (int j = 0; j < 16; ++j) y[j] = (v[k][j] * r[k]) * wv[j];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 o[j] = y[j] * cf[j] - y[j + 8] * sf[j];
                 o[j + 8] = y[j + 8] * cf[j] + y[j] * sf[j];
             }
         }
-        if (!act) continue;
+        if (h >= heads_total) continue;
 
         if (st == kQ || st == kIQ) {
-            uint16_t* dst = st == kQ ? a.q_out + ((int64_t)t * a.hq + h) * kHeadDim
-                                     : a.iq_out + ((int64_t)t * a.hiq + (h - h_iq)) * kHeadDim;
+            uint16_t* dst = st == kQ ? a.q_out + ((int64_t)t * hq + h) * kHeadDim
+                                     : a.iq_out + ((int64_t)t * hiq + (h - h_iq)) * kHeadDim;
             dst += sub * 8;
-            uint4 lo, hi;
-            lo.x = bf16x2(o[0], o[1]); lo.y = bf16x2(o[2], o[3]); lo.z = bf16x2(o[4], o[5]); lo.w = bf16x2(o[6], o[7]);
-            hi.x = bf16x2(o[8], o[9]); hi.y = bf16x2(o[10], o[11]); hi.z = bf16x2(o[12], o[13]); hi.w = bf16x2(o[14], o[15]);
-            *reinterpret_cast<uint4*>(dst) = lo;
-            *reinterpret_cast<uint4*>(dst + kHalf) = hi;
+            *reinterpret_cast<uint4*>(dst) = bf16x8(o);
+            *reinterpret_cast<uint4*>(dst + kHalf) = bf16x8(o + 8);
         } else if (valid) {
             const int ci = st == kK ? 0 : st == kV ? 1 : 2;
             const int hl = st == kK ? h - h_k : st == kV ? h - h_v : h - h_ik;
             const CacheDev& cd = a.cache[ci];
-            const int64_t e = cache_base[ci] + (int64_t)hl * cd.sh + sub * 8;
+            const int64_t e = page * cd.sp + (int64_t)off * cd.st + (int64_t)hl * cd.sh + sub * 8;
             if (cd.is_bf16) {
                 uint16_t* dst = reinterpret_cast<uint16_t*>(cd.data) + e;
-                uint4 lo, hi;
-                lo.x = bf16x2(o[0], o[1]); lo.y = bf16x2(o[2], o[3]); lo.z = bf16x2(o[4], o[5]); lo.w = bf16x2(o[6], o[7]);
-                hi.x = bf16x2(o[8], o[9]); hi.y = bf16x2(o[10], o[11]); hi.z = bf16x2(o[12], o[13]); hi.w = bf16x2(o[14], o[15]);
-                *reinterpret_cast<uint4*>(dst) = lo;
-                *reinterpret_cast<uint4*>(dst + kHalf) = hi;
+                *reinterpret_cast<uint4*>(dst) = bf16x8(o);
+                *reinterpret_cast<uint4*>(dst + kHalf) = bf16x8(o + 8);
             } else {
-                const float m = inv_sc[ci];
-                uint8_t* dst = cd.data + e;
                 uint2 lo, hi;
-                lo.x = e4m3x4(o[0] * m, o[1] * m, o[2] * m, o[3] * m);
-                lo.y = e4m3x4(o[4] * m, o[5] * m, o[6] * m, o[7] * m);
-                hi.x = e4m3x4(o[8] * m, o[9] * m, o[10] * m, o[11] * m);
-                hi.y = e4m3x4(o[12] * m, o[13] * m, o[14] * m, o[15] * m);
+                e4m3x16(o, inv_scale_of(cd.scale), lo, hi);
+                uint8_t* dst = cd.data + e;
                 *reinterpret_cast<uint2*>(dst) = lo;
                 *reinterpret_cast<uint2*>(dst + kHalf) = hi;
             }
@@ -419,13 +485,14 @@ msa_status check_cache(const msa_cache_view* v, int32_t heads, int32_t page_size
     return MSA_OK;
 }
 
-template <int PPW>
+template <int PPW, int HQ, int HKV, int HIQ, int HIK>
 hipError_t launch_produce(const ProduceArgs& a, hipStream_t stream)
 {
     const int64_t waves = (int64_t)a.T * a.waves_per_token;
     const dim3 grid((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock));
     void* args[] = {const_cast<ProduceArgs*>(&a)};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&produce_kernel<PPW>), grid, dim3(kBlock), args, 0, stream);
+    return hipLaunchKernel(reinterpret_cast<const void*>(&produce_kernel<PPW, HQ, HKV, HIQ, HIK>), grid, dim3(kBlock),
+                           args, 0, stream);
 }
 
 }  // namespace
@@ -494,6 +561,7 @@ msa_status msa_produce(const uint16_t* x, int64_t x_row_stride, int32_t num_toke
     a.S = num_seqs;
     a.max_pages = max_pages_per_seq;
     a.page_size = page_size;
+    a.page_shift = (page_size & (page_size - 1)) == 0 ? __builtin_ctz((unsigned)page_size) : -1;
     a.hq = num_q_heads;
     a.hkv = num_kv_heads;
     a.hiq = num_iq_heads;
@@ -520,11 +588,16 @@ msa_status msa_produce(const uint16_t* x, int64_t x_row_stride, int32_t num_toke
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
-    switch (ppw) {
-        case 1: e = launch_produce<1>(a, s); break;
-        case 2: e = launch_produce<2>(a, s); break;
-        case 3: e = launch_produce<3>(a, s); break;
-        default: e = launch_produce<4>(a, s); break;
+    // Builds specialised for the head geometry of one tensor-parallel rank (16/2/2/1); any other
+    // geometry runs the generic build.
+    const bool rank_geom = num_q_heads == 16 && num_kv_heads == 2 && num_iq_heads == 2 && num_ik_heads == 1;
+    if (rank_geom && ppw == 1) e = launch_produce<1, 16, 2, 2, 1>(a, s);
+    else if (rank_geom && ppw == 3) e = launch_produce<3, 16, 2, 2, 1>(a, s);
+    else switch (ppw) {
+        case 1: e = launch_produce<1, -1, -1, -1, -1>(a, s); break;
+        case 2: e = launch_produce<2, -1, -1, -1, -1>(a, s); break;
+        case 3: e = launch_produce<3, -1, -1, -1, -1>(a, s); break;
+        default: e = launch_produce<4, -1, -1, -1, -1>(a, s); break;
     }
     return e == hipSuccess ? MSA_OK : MSA_ERR_LAUNCH;
 }
