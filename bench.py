@@ -160,7 +160,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--layers", type=int, default=60)
-    ap.add_argument("--prefill-iters", type=int, default=50)
+    ap.add_argument("--prefill-iters", type=int, default=200)
+    ap.add_argument("--prefill-warmup", type=int, default=300,
+                    help="untimed prefill launches first; the engine clock takes tens of ms of load to settle")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
@@ -189,7 +191,7 @@ def main():
     del dec["devs"]
     torch.cuda.empty_cache()
 
-    prefill = None if args.no_prefill else bench_prefill(msa, W, torch, args.prefill_iters, 10)
+    prefill = None if args.no_prefill else bench_prefill(msa, W, torch, args.prefill_iters, args.prefill_warmup)
     cpu = None if args.no_cpu_baseline else cpu_baseline(W, args.cpu_seconds)
 
     line = {

@@ -150,6 +150,35 @@ __device__ __forceinline__ double head_sum8(double v)
     return v;
 }
 
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+// Output stores.  Streaming (nontemporal) stores keep large batches' write-once outputs from
+// displacing cache lines still to be read; small batches use ordinary stores so that their
+// consumer (the next kernel) finds Q and the new cache rows in cache.
+template <bool kStream>
+__device__ __forceinline__ void store16(void* p, uint4 v)
+{
+    if (kStream) {
+        const u32x4_t w = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
+    } else {
+        *reinterpret_cast<uint4*>(p) = v;
+    }
+}
+
+template <bool kStream>
+__device__ __forceinline__ void store8(void* p, uint2 v)
+{
+    if (kStream) {
+        const u32x2_t w = {v.x, v.y};
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x2_t*>(p));
+    } else {
+        *reinterpret_cast<uint2*>(p) = v;
+    }
+}
+
 // ------------------------------------------------------------------ producer kernel
 
 // Per-lane fp8 cast of 16 values (scaled by m) into two 8-byte halves.  When no value of the lane
@@ -195,8 +224,10 @@ __global__ __launch_bounds__(kBlock) void produce_kernel(const ProduceArgs a)
     constexpr int kNpass = kFixed ? (kTotal + kHeadsPerPass - 1) / kHeadsPerPass : -1;
     // With a fixed geometry whose passes all fit one wave, every wave starts at pass 0.
     constexpr bool kWholeToken = kFixed && kNpass <= PPW;
-    // Several passes per wave: stage the norm weights once per block in LDS.
+    // Several passes per wave (large batches): stage the norm weights once per block in LDS and
+    // stream the outputs.
     constexpr bool kStageW = PPW > 1;
+    constexpr bool kStream = PPW > 1;
 
     const int hq = kFixed ? HQ : a.hq;
     const int hkv = kFixed ? HKV : a.hkv;
@@ -289,17 +320,18 @@ __global__ __launch_bounds__(kBlock) void produce_kernel(const ProduceArgs a)
         sf[0] = s0.x; sf[1] = s0.y; sf[2] = s0.z; sf[3] = s0.w; sf[4] = s1.x; sf[5] = s1.y; sf[6] = s1.z; sf[7] = s1.w;
     }
 
-    // Unpack every pass once; sums of squares in binary64 (each square exact), reduced over the
-    // 8 lanes of each head.
-    float v[PPW][16];
+    // Sums of squares of every pass in binary64 (each square exact), reduced over the 8 lanes of
+    // each head.  Rows stay packed between this phase and the per-pass work below, which unpacks
+    // them again: that keeps the register footprint at five waves per SIMD.
     double ss[PPW];
 #pragma unroll
     for (int k = 0; k < PPW; ++k) {
-        unpack8(xa[k], v[k]);
-        unpack8(xb[k], v[k] + 8);
+        float u[16];
+        unpack8(xa[k], u);
+        unpack8(xb[k], u + 8);
         double acc = 0.0;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) acc = __builtin_fma((double)v[k][j], (double)v[k][j], acc);
+        for (int j = 0; j < 16; ++j) acc = __builtin_fma((double)u[j], (double)u[j], acc);
         ss[k] = head_sum8(acc);
     }
     // RMSNorm scales: with several passes, lane `sub` of a head group computes the scale of pass
@@ -327,10 +359,15 @@ __global__ __launch_bounds__(kBlock) void produce_kernel(const ProduceArgs a)
         const int hc = h < heads_total ? h : heads_total - 1;
         const int st = hc < h_k ? kQ : hc < h_v ? kK : hc < h_iq ? kV : hc < h_ik ? kIQ : kIK;
 
+        // Keep each pass's temporaries from being hoisted into the previous pass (register footprint).
+        __builtin_amdgcn_sched_barrier(0);
+        float v[1][16];
+        unpack8(xa[k], v[0]);
+        unpack8(xb[k], v[0] + 8);
         float o[16];
         if (st == kV) {
 #pragma unroll
-            for (int j = 0; j < 16; ++j) o[j] = v[k][j];
+            for (int j = 0; j < 16; ++j) o[j] = v[0][j];
         } else {
             const int ws = st == kQ ? 0 : st == kK ? 1 : st == kIQ ? 2 : 3;
             float wv[16];
@@ -347,7 +384,7 @@ __global__ __launch_bounds__(kBlock) void produce_kernel(const ProduceArgs a)
             }
             float y[16];
 #pragma unroll
-            for (int j = 0; j < 16; ++j) y[j] = (v[k][j] * r[k]) * wv[j];
+            for (int j = 0; j < 16; ++j) y[j] = (v[0][j] * r[k]) * wv[j];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 o[j] = y[j] * cf[j] - y[j + 8] * sf[j];
@@ -360,8 +397,8 @@ __global__ __launch_bounds__(kBlock) void produce_kernel(const ProduceArgs a)
             uint16_t* dst = st == kQ ? a.q_out + ((int64_t)t * hq + h) * kHeadDim
                                      : a.iq_out + ((int64_t)t * hiq + (h - h_iq)) * kHeadDim;
             dst += sub * 8;
-            *reinterpret_cast<uint4*>(dst) = bf16x8(o);
-            *reinterpret_cast<uint4*>(dst + kHalf) = bf16x8(o + 8);
+            store16<kStream>(dst, bf16x8(o));
+            store16<kStream>(dst + kHalf, bf16x8(o + 8));
         } else if (valid) {
             const int ci = st == kK ? 0 : st == kV ? 1 : 2;
             const int hl = st == kK ? h - h_k : st == kV ? h - h_v : h - h_ik;
@@ -369,14 +406,14 @@ __global__ __launch_bounds__(kBlock) void produce_kernel(const ProduceArgs a)
             const int64_t e = page * cd.sp + (int64_t)off * cd.st + (int64_t)hl * cd.sh + sub * 8;
             if (cd.is_bf16) {
                 uint16_t* dst = reinterpret_cast<uint16_t*>(cd.data) + e;
-                *reinterpret_cast<uint4*>(dst) = bf16x8(o);
-                *reinterpret_cast<uint4*>(dst + kHalf) = bf16x8(o + 8);
+                store16<kStream>(dst, bf16x8(o));
+                store16<kStream>(dst + kHalf, bf16x8(o + 8));
             } else {
                 uint2 lo, hi;
                 e4m3x16(o, inv_scale_of(cd.scale), lo, hi);
                 uint8_t* dst = cd.data + e;
-                *reinterpret_cast<uint2*>(dst) = lo;
-                *reinterpret_cast<uint2*>(dst + kHalf) = hi;
+                store8<kStream>(dst, lo);
+                store8<kStream>(dst + kHalf, hi);
             }
         }
     }
