@@ -158,7 +158,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--layers", type=int, default=60)
     ap.add_argument("--prefill-iters", type=int, default=200)
     ap.add_argument("--prefill-warmup", type=int, default=300,
@@ -166,6 +166,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run three plain 1 GiB device-to-device copies (the reference kernel that "
+                         "scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the producer runs on one tensor-parallel rank's local heads "
@@ -181,6 +184,14 @@ def main():
         sys.exit(1)
     msa.lib()
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_each": src.numel() * 4, "copies": 3}), flush=True)
+        return
 
     dec = bench_decode(msa, W, torch, args.layers, args.steps, args.warmup)
     us_step = dec["ms_per_step"] * 1000
