@@ -1,18 +1,18 @@
 """Benchmark of the MSA fused producer on one MI355X.
 
-Step = one decode step of a 60-layer model at decode batch 64 (64 sequences x 1 new token at
-positions 7000..9199, local heads Q=16 / KV=2 / index-Q=2 / index-K=1, head_dim 128, fp8 e4m3
-HND caches of 10,240 pages per layer): 60 msa_produce launches, each on its own layer's input
-row, norm weights, scales and caches, captured once in a HIP graph and replayed.  Inputs are
-resident in HBM before the timed region.
-
-The JSON line reports:
-  value            algorithmic HBM GB/s of the decode step (bytes the method must move / step time)
-  us_per_layer_call, us_per_step
-  roofline         of the producer kernel at decode batch 64 (HIP-event time over the timed
-                   region / launches, against MI355X's 8 TB/s)
-  prefill          the 65,536-token prefill chunk (8 x 8192 tokens), its own roofline
-  cpu_baseline     the CPU oracle on a bounded sample of the same decode workload
+The metric has two parts, measured on two workloads:
+  * producer HBM GB/s (% of peak): the 65,536-token prefill chunk (8 sequences x 8192 tokens, local
+    heads Q=16 / KV=2 / index-Q=2 / index-K=1, head_dim 128, fp8 e4m3 HND caches in a 12,000-page
+    pool).  A step is one msa_produce launch over the whole chunk; `--warmup` untimed steps (the
+    engine clock needs tens of milliseconds of load to settle), then `--steps` timed ones, with
+    HIP events on the launch stream, alternating two input sets.  `value`, `ms_per_step` and
+    `roofline` are this kernel's.
+  * us per layer call at decode batch 64: 64 sequences x 1 token at positions 7000..9199, the same
+    heads, fp8 caches of 10,240 pages per layer; 60 layer calls (each with its own input row, norm
+    weights, scales and caches) captured once in a HIP graph and replayed.  Reported as
+    `us_per_layer_call` and `us_per_decode_step`, with their own roofline under `decode`.
+Inputs are resident in HBM before every timed region.  `cpu_baseline` is the CPU oracle on a
+bounded sample of the prefill workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers 60] [--no-cpu-baseline]
 """
@@ -119,25 +119,21 @@ def bench_prefill(msa, W, torch, iters, warmup):
     b = sets[0].algorithmic_bytes()
     us = ms * 1000 / iters
     gbs = b / (us * 1e-6) / 1e9
-    traffic = counter_traffic("prefill_65536")
-    out = dict(workload="prefill 8 x 8192 tokens (65,536 rows), heads 16/2/2/1, fp8 e4m3 caches, 12,000-page pool",
-               us_per_call=us, algorithmic_bytes_per_call=b, launches=iters,
-               roofline=dict(bound="hbm", achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=gbs / HBM_PEAK_GBS,
-                             traffic=traffic))
+    out = dict(us_per_call=us, bytes=b, gbs=gbs, launches=iters)
     del devs
     torch.cuda.empty_cache()
     return out
 
 
 def cpu_baseline(W, seconds: float):
-    """The CPU oracle as it stands, on repeated decode-64 layer calls for about `seconds`."""
-    import numpy as np
+    """The CPU oracle as it stands, on leading slices of the prefill workload for about `seconds`."""
     import oracle
     threads = min(16, os.cpu_count() or 1)
-    wl = W.config1(layer=0)
-    args = (wl.x, wl.x_stride, wl.T, wl.head_dim, wl.hq, wl.hkv, wl.hiq, wl.hik, wl.positions, wl.seq_idx,
-            wl.page_table, wl.max_pages, wl.num_seqs, wl.max_pages, wl.page_size, wl.num_pages, *wl.weights,
-            wl.eps, wl.theta)
+    wl = W.config3()
+    rows = 4096
+    args = (wl.x, wl.x_stride, rows, wl.head_dim, wl.hq, wl.hkv, wl.hiq, wl.hik, wl.positions[:rows],
+            wl.seq_idx[:rows], wl.page_table, wl.max_pages, wl.num_seqs, wl.max_pages, wl.page_size, wl.num_pages,
+            *wl.weights, wl.eps, wl.theta)
     kw = dict(dtypes=[c.dtype for c in wl.caches], scales=[c.scale for c in wl.caches], num_threads=threads)
     oracle.produce_rows(*args, **kw)
     n, t0 = 0, time.perf_counter()
@@ -148,24 +144,24 @@ def cpu_baseline(W, seconds: float):
         if el >= seconds:
             break
     per_call = el / n
-    return dict(value=wl.algorithmic_bytes() / per_call / 1e9, unit="GB/s", cores=threads, kind="oracle",
-                sample=f"{n} decode-64 layer calls (64 tokens, heads 16/2/2/1, fp8) of the CPU oracle "
-                       f"({threads} OpenMP threads, dense per-token output form) in {el:.1f} s; "
-                       f"{per_call * 1e6:.0f} us per layer call")
+    bytes_per_call = wl.algorithmic_bytes() * rows / wl.T
+    return dict(value=bytes_per_call / per_call / 1e9, unit="GB/s", cores=threads, kind="oracle",
+                sample=f"{n} oracle calls on the first {rows} tokens of the 65,536-token prefill (all heads, fp8 "
+                       f"cache codes in the dense per-token form), {threads} OpenMP threads, {el:.1f} s: "
+                       f"{per_call * 1e3:.1f} ms per {rows} tokens")
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--layers", type=int, default=60)
-    ap.add_argument("--prefill-iters", type=int, default=200)
-    ap.add_argument("--prefill-warmup", type=int, default=300,
+    ap.add_argument("--steps", type=int, default=200, help="timed prefill launches")
+    ap.add_argument("--warmup", type=int, default=300,
                     help="untimed prefill launches first; the engine clock takes tens of ms of load to settle")
+    ap.add_argument("--layers", type=int, default=60)
+    ap.add_argument("--decode-steps", type=int, default=200, help="timed 60-layer decode graph replays")
+    ap.add_argument("--decode-warmup", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run three plain 1 GiB device-to-device copies (the reference kernel that "
                          "scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
@@ -193,49 +189,59 @@ def main():
         print(json.dumps({"copy_calibration_bytes_each": src.numel() * 4, "copies": 3}), flush=True)
         return
 
-    dec = bench_decode(msa, W, torch, args.layers, args.steps, args.warmup)
+    dec = bench_decode(msa, W, torch, args.layers, args.decode_steps, args.decode_warmup)
     us_step = dec["ms_per_step"] * 1000
     us_call = us_step / args.layers
-    step_gbs = dec["bytes_per_step"] / (us_step * 1e-6) / 1e9
     launch_us = dec["ms_total"] * 1000 / dec["launches"]
     launch_gbs = dec["bytes_per_call"] / (launch_us * 1e-6) / 1e9
     del dec["devs"]
     torch.cuda.empty_cache()
 
-    prefill = None if args.no_prefill else bench_prefill(msa, W, torch, args.prefill_iters, args.prefill_warmup)
+    pre = bench_prefill(msa, W, torch, args.steps, args.warmup)
     cpu = None if args.no_cpu_baseline else cpu_baseline(W, args.cpu_seconds)
 
     line = {
         "metric": METRIC,
-        "value": step_gbs,
+        "value": pre["gbs"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": dec["ms_per_step"],
-        "us_per_step": us_step,
+        "ms_per_step": pre["us_per_call"] / 1000,
+        "pct_of_hbm_peak": 100.0 * pre["gbs"] / HBM_PEAK_GBS,
         "us_per_layer_call": us_call,
-        "pct_of_hbm_peak": 100.0 * step_gbs / HBM_PEAK_GBS,
+        "us_per_decode_step": us_step,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": "decode batch 64: 64 seqs x 1 token at positions 7000..9199, local heads Q=16 KV=2 "
-                        "index-Q=2 index-K=1, head_dim 128, fp8 e4m3 HND caches [10240, H, 64, 128] per layer; "
-                        f"{args.layers} layer calls per step in one HIP graph",
-            "tokens": 64,
-            "layers": args.layers,
-            "algorithmic_bytes_per_layer_call": dec["bytes_per_call"],
+            "workload": "prefill chunk: 8 seqs x 8192 tokens (65,536 rows) at positions 0..8191, local heads Q=16 "
+                        "KV=2 index-Q=2 index-K=1, head_dim 128, fp8 e4m3 HND caches, 12,000-page pool; one "
+                        "msa_produce launch per step.  us_per_layer_call: decode batch 64 (64 seqs x 1 token at "
+                        f"positions 7000..9199), {args.layers} layer calls per step in one HIP graph",
+            "tokens": 65536,
+            "algorithmic_bytes_per_step": pre["bytes"],
+            "decode_tokens": 64,
+            "decode_layers": args.layers,
+            "decode_algorithmic_bytes_per_layer_call": dec["bytes_per_call"],
             "parallelism": "single GPU (one tensor-parallel rank's local heads)",
         },
         "roofline": {
-            "bound": "hbm", "achieved": launch_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": launch_gbs / HBM_PEAK_GBS, "traffic": counter_traffic("decode_64"),
-            "kernel": "produce_kernel (decode batch 64)", "avg_launch_us": launch_us,
+            "bound": "hbm", "achieved": pre["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": pre["gbs"] / HBM_PEAK_GBS, "traffic": counter_traffic("prefill_65536"),
+            "kernel": "produce_kernel<3, 16, 2, 2, 1> (prefill)", "avg_launch_us": pre["us_per_call"],
         },
-        "prefill": prefill,
+        "decode": {
+            "steps": args.decode_steps, "warmup": args.decode_warmup, "layers": args.layers,
+            "us_per_layer_call": us_call, "us_per_step": us_step,
+            "roofline": {
+                "bound": "hbm", "achieved": launch_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": launch_gbs / HBM_PEAK_GBS, "traffic": counter_traffic("decode_64"),
+                "kernel": "produce_kernel<1, 16, 2, 2, 1> (decode batch 64)", "avg_launch_us": launch_us,
+            },
+        },
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -224,8 +224,8 @@ __global__ __launch_bounds__(kBlock) void produce_kernel(const ProduceArgs a)
     constexpr int kNpass = kFixed ? (kTotal + kHeadsPerPass - 1) / kHeadsPerPass : -1;
     // With a fixed geometry whose passes all fit one wave, every wave starts at pass 0.
     constexpr bool kWholeToken = kFixed && kNpass <= PPW;
-    // Several passes per wave (large batches): stage the norm weights once per block in LDS and
-    // stream the outputs.
+    // Several passes per wave (large batches): stage the norm weights in LDS (one copy per wave, so
+    // waves never wait on each other) and stream the outputs.
     constexpr bool kStageW = PPW > 1;
     constexpr bool kStream = PPW > 1;
 
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(kBlock) void produce_kernel(const ProduceArgs a)
     const int npass = kFixed ? kNpass : a.npass;
     const int h_k = hq, h_v = hq + hkv, h_iq = hq + 2 * hkv, h_ik = h_iq + hiq;
 
-    __shared__ __attribute__((aligned(16))) float w_lds[kStageW ? 4 : 1][kHeadDim];
+    __shared__ __attribute__((aligned(16))) float w_lds[kStageW ? kWavesPerBlock : 1][kStageW ? 4 : 1][kHeadDim];
     __shared__ __attribute__((aligned(16))) float cs_lds[kWavesPerBlock][2 * kHalf];
 
     const int lane = threadIdx.x & (kWave - 1);
@@ -270,9 +270,18 @@ __global__ __launch_bounds__(kBlock) void produce_kernel(const ProduceArgs a)
     }
 
     if (kStageW) {
-        for (int i = threadIdx.x; i < 4 * kHeadDim; i += kBlock) {
-            const uint16_t* w = a.w[i / kHeadDim];
-            w_lds[i / kHeadDim][i % kHeadDim] = w ? __uint_as_float((uint32_t)w[i % kHeadDim] << 16) : 0.0f;
+        // Each wave stages its own copy (no block barrier): lane L converts weights [8L, 8L + 8) of
+        // the 512 (stream L / 16).
+        const uint16_t* w = a.w[lane / 16];
+        float* dst = &w_lds[wave][lane / 16][(lane % 16) * 8];
+        if (w) {
+            float f[8];
+            unpack8(*reinterpret_cast<const uint4*>(w + (lane % 16) * 8), f);
+            reinterpret_cast<float4*>(dst)[0] = make_float4(f[0], f[1], f[2], f[3]);
+            reinterpret_cast<float4*>(dst)[1] = make_float4(f[4], f[5], f[6], f[7]);
+        } else {
+            reinterpret_cast<float4*>(dst)[0] = make_float4(0.f, 0.f, 0.f, 0.f);
+            reinterpret_cast<float4*>(dst)[1] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
     }
 
@@ -298,15 +307,10 @@ __global__ __launch_bounds__(kBlock) void produce_kernel(const ProduceArgs a)
         cs_lds[wave][lane] = c;
         cs_lds[wave][kHalf + lane] = s;
     }
-    if (kStageW) {
-        __syncthreads();
-        if (!live) return;   // no block barrier after this point
-    } else {
-        if (!live) return;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
+    if (!live) return;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     const bool valid = page >= 0;
     if (chunk == 0 && lane == 0 && a.slots_out) a.slots_out[t] = valid ? page * a.page_size + off : -1;
@@ -372,8 +376,8 @@ __global__ __launch_bounds__(kBlock) void produce_kernel(const ProduceArgs a)
             const int ws = st == kQ ? 0 : st == kK ? 1 : st == kIQ ? 2 : 3;
             float wv[16];
             if (kStageW) {
-                const float4* wp = reinterpret_cast<const float4*>(&w_lds[ws][sub * 8]);
-                const float4* wq = reinterpret_cast<const float4*>(&w_lds[ws][kHalf + sub * 8]);
+                const float4* wp = reinterpret_cast<const float4*>(&w_lds[wave][ws][sub * 8]);
+                const float4* wq = reinterpret_cast<const float4*>(&w_lds[wave][ws][kHalf + sub * 8]);
                 const float4 w0 = wp[0], w1 = wp[1], w2 = wq[0], w3 = wq[1];
                 wv[0] = w0.x; wv[1] = w0.y; wv[2] = w0.z; wv[3] = w0.w; wv[4] = w1.x; wv[5] = w1.y; wv[6] = w1.z; wv[7] = w1.w;
                 wv[8] = w2.x; wv[9] = w2.y; wv[10] = w2.z; wv[11] = w2.w; wv[12] = w3.x; wv[13] = w3.y; wv[14] = w3.z; wv[15] = w3.w;

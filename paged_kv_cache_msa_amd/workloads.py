@@ -346,3 +346,35 @@ def to_device(wl: Workload, device="cuda", sentinel: int = SENTINEL_BYTE) -> Dev
         scales.append(torch.tensor([c.scale], dtype=torch.float32, device=device))
     slots = torch.full((T,), -7, dtype=torch.int64, device=device)
     return DeviceWorkload(x, pos, seq, pt, ws, q, iq, storages, views, scales, slots)
+
+
+def verify_window(draft_len: int = 3, seqs: int = 64, seed: int = 5, cache_dtype: int = FP8_E4M3,
+                  num_pages: int = 10240, max_pages: int = 160, pos_lo: int = 7000, pos_hi: int = 9200,
+                  layer: int = 0) -> Workload:
+    """Speculative-decoding verify rows: every sequence brings 1 + draft_len consecutive tokens (the
+    uniform verify window of one-model Eagle3 decoding in "Wire in custom decode kernels for
+    MinimaxM3", conflict-resolution notes), so windows cross page boundaries.  Each sequence's
+    page table holds distinct pages for every logical page its window touches; `num_pages` and
+    `max_pages` set the pool geometry (a draft model uses its own)."""
+    rng = np.random.Generator(np.random.PCG64([seed, layer]))
+    D, P = HEAD_DIM, PAGE_SIZE
+    hq, hkv, hiq, hik = DECODE_HEADS
+    L = 1 + draft_len
+    base = rng.integers(pos_lo, pos_hi, seqs)
+    # force some windows to straddle a page boundary
+    straddle = rng.random(seqs) < 0.25
+    base = np.where(straddle, (base // P + 1) * P - rng.integers(1, L, seqs), base)
+    pos = (base[:, None] + np.arange(L)[None, :]).reshape(-1).astype(np.int32)
+    seq = np.repeat(np.arange(seqs), L).astype(np.int32)
+    assert int(pos.max()) // P < max_pages
+    pt = rng.integers(0, num_pages, (seqs, max_pages)).astype(np.int32)
+    touched = sorted({(int(s), int(p_) // P) for s, p_ in zip(seq, pos)})
+    for (s, lp), pg in zip(touched, rng.permutation(num_pages)[: len(touched)]):
+        pt[s, lp] = pg
+    W_ = (hq + 2 * hkv + hiq + hik) * D
+    x = _normal_bf16(rng, (seqs * L, W_), 1.0)
+    w = _weights(rng, hq, hkv, hiq, hik, D)
+    scales = rng.uniform(0.5, 2.0, 3)
+    caches = [_hnd_cache(num_pages, h, cache_dtype, s) for h, s in zip((hkv, hkv, hik), scales)]
+    return Workload(f"verify window {seqs} seqs x (1 + {draft_len}) tokens, {num_pages}-page pool", hq, hkv, hiq, hik,
+                    D, P, num_pages, x, pos, seq, pt, w, caches)

@@ -325,3 +325,23 @@ def test_graph_replay_matches_eager():
             for a, b in zip(sts, d.storages):
                 assert torch.equal(a, b), rep
     check(layers[0], devs[0])
+
+
+# ------------------------------------------------------------------ speculative-decoding verify rows
+
+@pytest.mark.parametrize("draft_len,seqs,dtype", [(3, 64, W.FP8_E4M3), (7, 256, W.FP8_E4M3), (1, 64, W.BF16)])
+def test_verify_window_rows(draft_len, seqs, dtype):
+    """1 + draft_len consecutive tokens per sequence (windows straddle page boundaries)."""
+    wl = W.verify_window(draft_len=draft_len, seqs=seqs, cache_dtype=dtype)
+    check(wl, run(wl))
+
+
+def test_target_and_draft_geometries():
+    """A target-model layer and a draft-model layer with its own, smaller page pool and page table
+    (bf16 caches) produced back to back: each matches the oracle and leaves the other's caches
+    untouched (each storage's written-element count is exact)."""
+    target = W.verify_window(draft_len=3, seqs=64, seed=21)
+    draft = W.verify_window(draft_len=3, seqs=64, seed=22, num_pages=3000, max_pages=160, cache_dtype=W.BF16)
+    dt, dd = run(target), run(draft)
+    check(target, dt)
+    check(draft, dd)

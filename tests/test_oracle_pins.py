@@ -371,3 +371,22 @@ def test_threads_do_not_change_results(oracle_lib):
     b = H.oracle_rows(wl, num_threads=4)
     for k in a:
         np.testing.assert_array_equal(a[k], b[k])
+
+
+def test_verify_window_slots_follow_pages(oracle_lib):
+    """Verify rows: consecutive tokens of a sequence take consecutive offsets of one page, and a
+    token at offset 0 starts the page the table lists for its logical page."""
+    wl = W.verify_window(draft_len=3, seqs=64)
+    sl = oracle.slots(wl.positions, wl.seq_idx, wl.page_table, wl.num_seqs, wl.max_pages, wl.page_size,
+                      wl.num_pages)
+    crossings = 0
+    for t in range(1, wl.T):
+        if wl.seq_idx[t] != wl.seq_idx[t - 1]:
+            continue
+        p = int(wl.positions[t])
+        if p % 64 == 0:
+            crossings += 1
+            assert sl[t] == wl.page_table[wl.seq_idx[t], p // 64] * 64
+        else:
+            assert sl[t] == sl[t - 1] + 1
+    assert crossings > 0
