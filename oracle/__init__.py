@@ -72,6 +72,11 @@ def lib() -> ctypes.CDLL:
             [p, i64, i64, i32, i32, i32, i32, i32, p, p, p, i64, i32, i32, i32, i64, p, p, p, p, f32, f64]
             + [p, i64, i64, i64, i32, f32] * 3 + [p, p, p, i32])
         L.msa_oracle_produce.restype = ctypes.c_int
+        L.msa_oracle_index_scores.argtypes = [p, i64, i32, i32, p, p, p, i64, i32, i32, i32, i64, p, i64, i64, i64,
+                                              i32, i32, f32, i32, i32, p]
+        L.msa_oracle_index_scores.restype = ctypes.c_int
+        L.msa_oracle_index_topk.argtypes = [p, i32, i64, i32, i32, p, p]
+        L.msa_oracle_index_topk.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -194,3 +199,37 @@ def produce(x, x_stride, T, head_dim, hq, hkv, hiq, hik, positions, seq_idx, pag
     if rc != 0:
         raise OracleError(f"msa_oracle_produce returned {rc}")
     return dict(q=q, iq=iq, slots=sl)
+
+
+def index_scores(iq, positions, seq_idx, page_table, pt_stride, num_seqs, max_pages, page_size, num_pages,
+                 ik_storage, ik_strides, hik, ik_dtype, ik_scale, block_tokens, max_blocks):
+    """Block scores [hiq, T, max_blocks] (float64) of the indexer reading (see msa_oracle.c).
+    iq: uint16 bf16 bits [T, hiq, D]; ik_storage: the index-K cache storage (uint8 fp8 codes or uint16
+    bf16 bits), element (page, head, token, d) at page*sp + head*sh + token*st + d."""
+    iq = np.ascontiguousarray(iq, dtype=np.uint16)
+    T, hiq, D = iq.shape
+    pos = _c(positions, np.int32)
+    seq = _c(seq_idx, np.int32)
+    pt = _c(page_table, np.int32)
+    st = np.ascontiguousarray(ik_storage)
+    out = np.empty((hiq, T, max_blocks), np.float64)
+    sp, sh, stt = (int(v) for v in ik_strides)
+    rc = lib().msa_oracle_index_scores(_ptr(iq), T, hiq, D, _ptr(pos), _ptr(seq), _ptr(pt), pt_stride, num_seqs,
+                                       max_pages, page_size, num_pages, _ptr(st), sp, sh, stt, hik, int(ik_dtype),
+                                       float(ik_scale), block_tokens, max_blocks, _ptr(out))
+    if rc != 0:
+        raise OracleError(f"msa_oracle_index_scores returned {rc}")
+    return out
+
+
+def index_topk(block_scores, top_k):
+    """ids [hiq, T, top_k] int32 and counts [hiq, T] of the top-k blocks (descending score, ties to the
+    lower block index, -1 padding)."""
+    bs = np.ascontiguousarray(block_scores, dtype=np.float64)
+    hiq, T, nb = bs.shape
+    ids = np.empty((hiq, T, top_k), np.int32)
+    counts = np.empty((hiq, T), np.int32)
+    rc = lib().msa_oracle_index_topk(_ptr(bs), hiq, T, nb, top_k, _ptr(ids), _ptr(counts))
+    if rc != 0:
+        raise OracleError(f"msa_oracle_index_topk returned {rc}")
+    return ids, counts

@@ -369,3 +369,104 @@ int msa_oracle_produce(const uint16_t* x, int64_t x_stride, int64_t T, int32_t h
     for (int ci = 0; ci < 3; ++ci) free(rows[ci]);
     return rc;
 }
+
+/* ------------------------------------------------------------------------------------------------
+ * Indexer (the downstream consumer of the index-K cache): proxy scores of index-Q against the
+ * visible index-K keys, max-pooled over fixed token blocks, then the top-k blocks per query.
+ * Pages: "Fuse MiniMax-M3 MSA per-layer KV-cache writes into one kernel", "Where this PR targets
+ * at", step 4 (proxy-FMHA over index-K, max-reduce, top-16 of 128-token blocks); "Fuse MiniMax-M3
+ * QKV and index projection", BEFORE/AFTER figures (score visible index-K, max-pool by block,
+ * select top-k block IDs).  Reading: the score of key position p for query token t and index-Q
+ * head h is the exact dot product iq[t,h,:] . ik[p,:] (binary64: every product of a bf16 and an
+ * e4m3/bf16 value is exact, and so is the sum for any realistic range), times the index-K
+ * dequantisation scale; visible = same sequence, 0 <= p <= pos_t, with a valid page.  Softmax
+ * and 1/sqrt(D) are monotone per (t, h) and do not change the selection, so they are not applied.
+ * ---------------------------------------------------------------------------------------------- */
+
+/* OCP E4M3 code -> value (NaN for S.1111.111). */
+static double e4m3_value(uint8_t c)
+{
+    int E = (c >> 3) & 15, M = c & 7;
+    double mag;
+    if (E == 15 && M == 7) return NAN;
+    mag = E == 0 ? ldexp((double)M, -9) : ldexp((double)(8 + M), E - 10);
+    return (c & 0x80) ? -mag : mag;
+}
+
+/*
+ * block_scores [hiq, T, max_blocks]: for block b (positions [b*B, (b+1)*B)) the maximum over its
+ * visible keys of the score; -inf when none is visible.  Padded tokens (no valid own slot) get -inf
+ * everywhere.  Index-Q head h reads index-K head h / (hiq / hik).
+ */
+int msa_oracle_index_scores(const uint16_t* iq, int64_t T, int32_t hiq, int32_t head_dim,
+                            const int32_t* positions, const int32_t* seq_idx, const int32_t* page_table,
+                            int64_t pt_stride, int32_t num_seqs, int32_t max_pages, int32_t page_size,
+                            int64_t num_pages, const void* ik_cache, int64_t sp, int64_t sh, int64_t st,
+                            int32_t hik, int32_t ik_dtype, float ik_scale, int32_t block_tokens,
+                            int32_t max_blocks, double* block_scores)
+{
+    if (T < 0 || hiq <= 0 || hik <= 0 || hiq % hik || head_dim <= 0 || page_size <= 0 || block_tokens <= 0 ||
+        max_blocks < 0 || (ik_dtype != ORC_FP8_E4M3 && ik_dtype != ORC_BF16))
+        return ORC_ERR_ARG;
+    const int32_t group = hiq / hik;
+    const double scale = ik_dtype == ORC_FP8_E4M3 ? (double)ik_scale : 1.0;
+    for (int64_t i = 0; i < (int64_t)hiq * T * max_blocks; ++i) block_scores[i] = -INFINITY;
+    for (int64_t t = 0; t < T; ++t) {
+        int64_t pg, off;
+        if (token_slot(positions[t], seq_idx[t], page_table, pt_stride, num_seqs, max_pages, page_size,
+                       num_pages, &pg, &off) < 0)
+            continue;
+        const int32_t s = seq_idx[t];
+        for (int32_t p = 0; p <= positions[t]; ++p) {
+            int64_t kpg, koff;
+            if (token_slot(p, s, page_table, pt_stride, num_seqs, max_pages, page_size, num_pages, &kpg, &koff) < 0)
+                continue;
+            const int32_t b = p / block_tokens;
+            if (b >= max_blocks) continue;
+            for (int32_t h = 0; h < hiq; ++h) {
+                const int64_t base = kpg * sp + (int64_t)(h / group) * sh + koff * st;
+                double dot = 0.0;
+                for (int32_t j = 0; j < head_dim; ++j) {
+                    double k = ik_dtype == ORC_FP8_E4M3 ? e4m3_value(((const uint8_t*)ik_cache)[base + j])
+                                                        : (double)bf16_value(((const uint16_t*)ik_cache)[base + j]);
+                    dot += (double)bf16_value(iq[(t * hiq + h) * head_dim + j]) * k;
+                }
+                const double score = dot * scale;
+                double* dst = &block_scores[((int64_t)h * T + t) * max_blocks + b];
+                if (score > *dst) *dst = score;
+            }
+        }
+    }
+    return ORC_OK;
+}
+
+/*
+ * Top-k blocks of every (head, token) row of block_scores: ids [hiq, T, top_k] in descending score,
+ * equal scores in ascending block index; blocks scored -inf are never selected; unused entries are
+ * -1.  counts [hiq, T] (optional) = number of selected blocks.
+ */
+int msa_oracle_index_topk(const double* block_scores, int32_t hiq, int64_t T, int32_t max_blocks, int32_t top_k,
+                          int32_t* ids, int32_t* counts)
+{
+    if (hiq <= 0 || T < 0 || max_blocks < 0 || top_k <= 0) return ORC_ERR_ARG;
+    for (int64_t r = 0; r < (int64_t)hiq * T; ++r) {
+        const double* row = block_scores + r * max_blocks;
+        int32_t* out = ids + r * top_k;
+        int32_t n = 0;
+        for (int32_t k = 0; k < top_k; ++k) {
+            int32_t best = -1;
+            for (int32_t b = 0; b < max_blocks; ++b) {
+                if (row[b] == -INFINITY || isnan(row[b])) continue;
+                int taken = 0;
+                for (int32_t i = 0; i < n; ++i) taken |= out[i] == b;
+                if (taken) continue;
+                if (best < 0 || row[b] > row[best]) best = b;   /* strict: the lower index wins ties */
+            }
+            if (best < 0) break;
+            out[n++] = best;
+        }
+        for (int32_t k = n; k < top_k; ++k) out[k] = -1;
+        if (counts) counts[r] = n;
+    }
+    return ORC_OK;
+}

@@ -12,6 +12,9 @@ Entry points (same names as the C ABI):
   msa_rope_table(...)   the RoPE coefficients alone.
   msa_quantize(...)     the output casts alone.
   msa_rms_scale(...)    the RMSNorm scale alone.
+  msa_index_scores(...) indexer: block max of the exact dot products of index-Q with the visible keys
+                        of the index-K cache (include/msa_index.h).
+  msa_index_topk(...)   indexer: the top-k blocks of every (index-Q head, token) row.
 """
 from __future__ import annotations
 
@@ -71,6 +74,10 @@ def lib() -> ctypes.CDLL:
         L.msa_quantize.restype = ctypes.c_int
         L.msa_rms_scale.argtypes = [p, i64, i32, f32, p, p]
         L.msa_rms_scale.restype = ctypes.c_int
+        L.msa_index_scores.argtypes = [p, i32, i32, i32, p, p, p, i64, i32, i32, i32, i64, cv, i32, i32, p, p]
+        L.msa_index_scores.restype = ctypes.c_int
+        L.msa_index_topk.argtypes = [p, i32, i32, i32, p, p, p]
+        L.msa_index_topk.restype = ctypes.c_int
         L.msa_status_string.argtypes = [ctypes.c_int]
         L.msa_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -162,3 +169,29 @@ def msa_rms_scale(sum_sq, r_out, rms_eps: float, head_dim: int = 128, stream=Non
     st = lib().msa_rms_scale(_ptr(sum_sq), sum_sq.numel(), head_dim, float(rms_eps), _ptr(r_out), _stream(stream))
     if st != 0:
         raise MsaError(st, "msa_rms_scale")
+
+
+def msa_index_scores(iq, positions, seq_idx, page_table, ik_cache, block_scores, *, ik_scale=None,
+                     num_pages: Optional[int] = None, block_tokens: int = 128, stream=None) -> None:
+    """Indexer block scores.  iq [T, Hiq, 128] bf16; ik_cache a 4-D index-K cache view
+    [num_pages, Hik, page_size, 128] (1-byte fp8 with a float32 [1] scale, or 2-byte bf16);
+    block_scores float64 [Hiq, T, max_blocks]."""
+    T, hiq = iq.shape[0], iq.shape[1]
+    view = cache_view(ik_cache, ik_scale)
+    pages = ik_cache.shape[0] if num_pages is None else num_pages
+    st = lib().msa_index_scores(_ptr(iq), T, 128, hiq, _ptr(positions), _ptr(seq_idx), _ptr(page_table),
+                                page_table.stride(0), page_table.shape[0], page_table.shape[1], ik_cache.shape[2],
+                                pages, ctypes.byref(view), int(block_tokens), block_scores.shape[-1],
+                                _ptr(block_scores), _stream(stream))
+    if st != 0:
+        raise MsaError(st, "msa_index_scores")
+
+
+def msa_index_topk(block_scores, block_ids, counts=None, stream=None) -> None:
+    """Top-k blocks of every row of block_scores [..., max_blocks] into block_ids [..., top_k] (int32)."""
+    nb = block_scores.shape[-1]
+    rows = block_scores.numel() // nb if nb else 0
+    st = lib().msa_index_topk(_ptr(block_scores), rows, nb, block_ids.shape[-1], _ptr(block_ids), _ptr(counts),
+                              _stream(stream))
+    if st != 0:
+        raise MsaError(st, "msa_index_topk")

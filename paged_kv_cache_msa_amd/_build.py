@@ -6,7 +6,7 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "msa_produce.hip")
+SRCS = [os.path.join(PKG, "csrc", n) for n in ("msa_produce.hip", "msa_index.hip")]
 LIB = os.path.join(PKG, "libmsa_produce.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -25,7 +25,7 @@ HIP_FLAGS = [
 def build(verbose: bool = False) -> str:
     inc = os.path.join(ROOT, "include")
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *HIP_FLAGS, "-I", inc, SRC, "-o", tmp]
+    cmd = [HIPCC, *HIP_FLAGS, "-I", inc, *SRCS, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "not a recognized feature for this target"
     err = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)

@@ -1,0 +1,73 @@
+// Host-side pieces shared by the producer and the indexer sources: the device form of a cache view
+// and its validation.  Internal to the library (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "msa_produce.h"
+
+namespace msa_internal {
+
+constexpr int kHeadDim = 128;
+
+// Device form of an msa_cache_view (element strides; the dim stride is 1).
+struct CacheDev {
+    uint8_t* data;
+    int64_t sp, sh, st;        // element strides (page, head, token)
+    const float* scale;        // fp8 only
+    int32_t heads;
+    int32_t is_bf16;
+};
+
+
+inline bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+// Validates a cache view of `heads` heads over `num_pages` pages of `page_size` tokens and fills its
+// device form.  heads == 0: nothing to check, the descriptor may be NULL.
+inline msa_status check_cache(const msa_cache_view* v, int32_t heads, int32_t page_size, int64_t num_pages, CacheDev* out)
+{
+    std::memset(out, 0, sizeof(*out));
+    if (heads == 0) return MSA_OK;
+    if (!v || !v->data) return MSA_ERR_NULL_POINTER;
+    if (v->num_heads != heads) return MSA_ERR_SHAPE;
+    if (v->dtype != MSA_CACHE_FP8_E4M3 && v->dtype != MSA_CACHE_BF16) return MSA_ERR_DTYPE;
+    if (v->dtype == MSA_CACHE_FP8_E4M3 && !v->scale) return MSA_ERR_DTYPE;
+    if (!aligned(v->data, 16)) return MSA_ERR_ALIGNMENT;
+    if (v->dtype == MSA_CACHE_FP8_E4M3 && !aligned(v->scale, 4)) return MSA_ERR_ALIGNMENT;
+    const int64_t s[3] = {v->stride_page, v->stride_head, v->stride_token};
+    for (int i = 0; i < 3; ++i)
+        if (s[i] <= 0 || s[i] % 8) return MSA_ERR_STRIDE;
+    // Non-overlap: with the dims ordered by stride, each stride must exceed the largest offset
+    // the smaller dims can reach.  The walk also yields the largest element offset of the view.
+    int64_t ord_s[4] = {1, s[2], s[1], s[0]};
+    int64_t ord_e[4] = {kHeadDim, page_size, heads, num_pages};
+    for (int i = 1; i < 4; ++i)
+        for (int j = i; j > 0 && ord_s[j] < ord_s[j - 1]; --j) {
+            const int64_t ts = ord_s[j]; ord_s[j] = ord_s[j - 1]; ord_s[j - 1] = ts;
+            const int64_t te = ord_e[j]; ord_e[j] = ord_e[j - 1]; ord_e[j - 1] = te;
+        }
+    int64_t max_off = 0;
+    for (int i = 0; i < 4; ++i) {
+        if (ord_e[i] <= 1) continue;
+        if (ord_s[i] <= max_off) return MSA_ERR_STRIDE;
+        int64_t reach;
+        if (__builtin_mul_overflow(ord_s[i], ord_e[i] - 1, &reach) || __builtin_add_overflow(max_off, reach, &max_off))
+            return MSA_ERR_OVERFLOW;
+    }
+    int64_t bytes;
+    if (__builtin_mul_overflow(max_off + 1, (int64_t)(v->dtype == MSA_CACHE_BF16 ? 2 : 1), &bytes))
+        return MSA_ERR_OVERFLOW;
+    out->data = static_cast<uint8_t*>(v->data);
+    out->sp = s[0];
+    out->sh = s[1];
+    out->st = s[2];
+    out->scale = v->scale;
+    out->heads = heads;
+    out->is_bf16 = v->dtype == MSA_CACHE_BF16;
+    return MSA_OK;
+}
+
+}  // namespace msa_internal

@@ -1,0 +1,328 @@
+// MSA indexer for CDNA4 (gfx950): block scores of index-Q against the paged index-K cache, max-pooled
+// over fixed token blocks, and the top-k blocks per (index-Q head, token).  Operation: page "Fuse
+// MiniMax-M3 MSA per-layer KV-cache writes into one kernel", "Where this PR targets at", step 4;
+// page "Fuse MiniMax-M3 QKV and index projection", BEFORE/AFTER figures (score visible index-K,
+// max-pool by block, select top-k block IDs).  The reading is documented in include/msa_index.h.
+//
+// Scoring is a stream over the visible keys (about 128 B of fp8 per key and 2 multiply-adds per
+// byte per index-Q head): HBM-bound, so it runs on the vector ALUs, not on MFMA.  One wavefront
+// takes one (token, block): 8 lanes per key (16 elements each), 8 keys per step, 16 steps for a
+// 128-token block.  Products of bf16 and e4m3/bf16 values are exact in binary64 and so are their
+// sums, so the block scores do not depend on the summation order.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "msa_common.h"
+#include "msa_index.h"
+
+namespace {
+
+using msa_internal::aligned;
+using msa_internal::CacheDev;
+using msa_internal::check_cache;
+using msa_internal::kHeadDim;
+
+constexpr int kWave = 64;
+constexpr int kWavesPerBlock = 4;
+constexpr int kBlock = kWave * kWavesPerBlock;
+constexpr int kLanesPerKey = 8;
+constexpr int kKeysPerStep = kWave / kLanesPerKey;
+constexpr int kElemsPerLane = kHeadDim / kLanesPerKey;   // 16
+constexpr int kMaxHeadsPerLaunch = 2;
+constexpr int kMaxTopK = 64;
+constexpr int kMaxRowBlocks = 4096;
+
+struct ScoreArgs {
+    const uint16_t* iq;
+    const int32_t* pos;
+    const int32_t* seq;
+    const int32_t* pt;
+    int64_t pt_stride;
+    int64_t num_pages;
+    int32_t T, S, max_pages, page_size, page_shift;
+    int32_t hiq, group, head0, block_tokens, max_blocks;
+    CacheDev ik;
+    double* out;
+};
+
+template <int Ctrl>
+__device__ __forceinline__ double dpp_f64(double v)
+{
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)u, Ctrl, 0xf, 0xf, false);
+    const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), Ctrl, 0xf, 0xf, false);
+    return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// Sum over the 8 lanes of a key group; every lane of the group ends with the same value.
+__device__ __forceinline__ double sum8(double v)
+{
+    v += dpp_f64<0xb1>(v);    // quad_perm [1,0,3,2]
+    v += dpp_f64<0x4e>(v);    // quad_perm [2,3,0,1]
+    v += dpp_f64<0x141>(v);   // row_half_mirror
+    return v;
+}
+
+__device__ __forceinline__ double shfl_xor_f64(double v, int m)
+{
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = __shfl_xor((int)(uint32_t)u, m), hi = __shfl_xor((int)(uint32_t)(u >> 32), m);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// max that never lets a NaN in: a NaN candidate loses against anything.
+__device__ __forceinline__ double max_no_nan(double best, double cand) { return cand > best ? cand : best; }
+
+// Cache slot of a position, or -1 (same rule as the producer's).
+__device__ __forceinline__ int64_t page_of(const ScoreArgs& a, int32_t sq, int32_t p, int32_t* off)
+{
+    if (sq < 0 || sq >= a.S || p < 0) return -1;
+    const int32_t lp = a.page_shift >= 0 ? p >> a.page_shift : p / a.page_size;
+    if (lp >= a.max_pages) return -1;
+    const int64_t pg = a.pt[(int64_t)sq * a.pt_stride + lp];
+    if (pg < 0 || pg >= a.num_pages) return -1;
+    *off = p - lp * a.page_size;
+    return pg;
+}
+
+// Decode 16 cache elements of one key (this lane's share) to binary64.
+__device__ __forceinline__ void load_key(const CacheDev& c, int64_t e, double* k)
+{
+    if (c.is_bf16) {
+        const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(c.data) + e);
+        const uint4 lo = src[0], hi = src[1];
+        const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            k[2 * i] = (double)__uint_as_float(w[i] << 16);
+            k[2 * i + 1] = (double)__uint_as_float(w[i] & 0xffff0000u);
+        }
+    } else {
+        // Two 8-byte loads: cache strides are multiples of 8 elements, so an fp8 row share is
+        // 8-byte aligned but not necessarily 16-byte aligned.
+        const uint2 v0 = reinterpret_cast<const uint2*>(c.data + e)[0];
+        const uint2 v1 = reinterpret_cast<const uint2*>(c.data + e)[1];
+        const uint32_t w[4] = {v0.x, v0.y, v1.x, v1.y};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            // e4m3 -> binary32 is exact (every e4m3 value is a binary32 value)
+            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+            k[4 * i] = (double)lo[0];
+            k[4 * i + 1] = (double)lo[1];
+            k[4 * i + 2] = (double)hi[0];
+            k[4 * i + 3] = (double)hi[1];
+        }
+    }
+}
+
+// One wavefront per (token, block); heads [head0, head0 + NH).
+template <int NH>
+__global__ __launch_bounds__(kBlock) void index_scores_kernel(const ScoreArgs a)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t item = blockIdx.x * kWavesPerBlock + wave;
+    if (item >= (uint32_t)a.T * (uint32_t)a.max_blocks) return;   // wave-uniform
+    const int32_t t = (int32_t)(item / (uint32_t)a.max_blocks);
+    const int32_t b = (int32_t)(item - (uint32_t)t * (uint32_t)a.max_blocks);
+    const int ks = lane / kLanesPerKey;    // key slot of this step
+    const int sub = lane % kLanesPerKey;   // element group within the key
+
+    const int32_t pos = a.pos[t];
+    const int32_t sq = a.seq[t];
+    int32_t own_off;
+    const bool token_ok = page_of(a, sq, pos, &own_off) >= 0;
+    const int32_t p0 = b * a.block_tokens;
+    double best[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) best[h] = -INFINITY;
+
+    if (token_ok && p0 <= pos) {
+        // This lane's 16 elements of every head's query, as binary64.
+        double q[NH][kElemsPerLane];
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            const uint16_t* qp = a.iq + ((int64_t)t * a.hiq + a.head0 + h) * kHeadDim + sub * kElemsPerLane;
+            const uint4 lo = reinterpret_cast<const uint4*>(qp)[0], hi = reinterpret_cast<const uint4*>(qp)[1];
+            const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                q[h][2 * i] = (double)__uint_as_float(w[i] << 16);
+                q[h][2 * i + 1] = (double)__uint_as_float(w[i] & 0xffff0000u);
+            }
+        }
+        const double scale = a.ik.is_bf16 ? 1.0 : (double)*a.ik.scale;
+        const int32_t p_end = (int32_t)min((int64_t)p0 + a.block_tokens, (int64_t)pos + 1);
+        const int64_t head_off = (int64_t)(a.head0 / a.group) * a.ik.sh;   // NH heads share one index-K head
+        for (int32_t pb = p0; pb < p_end; pb += kKeysPerStep) {
+            const int32_t p = pb + ks;
+            int32_t off = 0;
+            const int64_t pg = p < p_end ? page_of(a, sq, p, &off) : -1;
+            double k[kElemsPerLane];
+            if (pg >= 0) {
+                load_key(a.ik, pg * a.ik.sp + head_off + (int64_t)off * a.ik.st + sub * kElemsPerLane, k);
+            } else {
+#pragma unroll
+                for (int j = 0; j < kElemsPerLane; ++j) k[j] = 0.0;
+            }
+#pragma unroll
+            for (int h = 0; h < NH; ++h) {
+                double acc = 0.0;
+#pragma unroll
+                for (int j = 0; j < kElemsPerLane; ++j) acc = __builtin_fma(q[h][j], k[j], acc);
+                const double dot = sum8(acc);
+                if (pg >= 0) best[h] = max_no_nan(best[h], dot * scale);
+            }
+        }
+    }
+    // Max over the 8 key slots (lanes sub, sub + 8, ..., sub + 56).
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        best[h] = max_no_nan(best[h], shfl_xor_f64(best[h], 8));
+        best[h] = max_no_nan(best[h], shfl_xor_f64(best[h], 16));
+        best[h] = max_no_nan(best[h], shfl_xor_f64(best[h], 32));
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < NH; ++h) a.out[((int64_t)(a.head0 + h) * a.T + t) * a.max_blocks + b] = best[h];
+    }
+}
+
+// (score, index) order of the selection: higher score first, then lower index.
+__device__ __forceinline__ bool before(double s1, int32_t i1, double s2, int32_t i2)
+{
+    return s1 > s2 || (s1 == s2 && i1 < i2);
+}
+
+// One wavefront per row: top_k rounds of a wave-wide arg-max over the candidates ranked after the
+// previous pick (so no pick repeats and no membership list is needed).
+__global__ __launch_bounds__(kBlock) void index_topk_kernel(const double* scores, int32_t rows, int32_t nb,
+                                                            int32_t top_k, int32_t* ids, int32_t* counts)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int32_t r = (int32_t)(blockIdx.x * kWavesPerBlock + wave);
+    if (r >= rows) return;   // wave-uniform
+    const double* row = scores + (int64_t)r * nb;
+    double last_s = INFINITY;
+    int32_t last_i = -1;
+    int32_t my_id = -1;   // lane k keeps the k-th pick
+    int32_t n = 0;
+    for (int32_t k = 0; k < top_k; ++k) {
+        double bs = -INFINITY;
+        int32_t bi = -1;
+        for (int32_t i = lane; i < nb; i += kWave) {
+            const double s = row[i];
+            if (!(s > -INFINITY)) continue;                       // -inf and NaN are never picked
+            if (!before(last_s, last_i, s, i)) continue;          // already picked (ranked before the last)
+            if (bi < 0 || before(s, i, bs, bi)) { bs = s; bi = i; }
+        }
+#pragma unroll
+        for (int m = 1; m < kWave; m <<= 1) {
+            const double os = shfl_xor_f64(bs, m);
+            const int32_t oi = __shfl_xor(bi, m);
+            if (oi >= 0 && (bi < 0 || before(os, oi, bs, bi))) { bs = os; bi = oi; }
+        }
+        if (bi < 0) break;                                        // wave-uniform after the reduction
+        if (lane == k) my_id = bi;
+        last_s = bs;
+        last_i = bi;
+        ++n;
+    }
+    if (lane < top_k) ids[(int64_t)r * top_k + lane] = my_id;
+    if (counts && lane == 0) counts[r] = n;
+}
+
+}  // namespace
+
+extern "C" {
+
+msa_status msa_index_scores(const uint16_t* iq, int32_t num_tokens, int32_t head_dim, int32_t num_iq_heads,
+                            const int32_t* positions, const int32_t* seq_idx,
+                            const int32_t* page_table, int64_t page_table_stride, int32_t num_seqs,
+                            int32_t max_pages_per_seq, int32_t page_size, int64_t num_pages,
+                            const msa_cache_view* ik_cache, int32_t block_tokens, int32_t max_blocks,
+                            double* block_scores, void* stream)
+{
+    if (head_dim != kHeadDim) return MSA_ERR_UNSUPPORTED;
+    if (num_tokens < 0 || num_iq_heads < 1 || num_iq_heads > 4096 || block_tokens <= 0 || max_blocks < 0)
+        return MSA_ERR_SHAPE;
+    if (page_size <= 0 || num_seqs < 0 || max_pages_per_seq < 0 || num_pages < 0) return MSA_ERR_SHAPE;
+    if (num_seqs > 0 && page_table_stride < max_pages_per_seq) return MSA_ERR_STRIDE;
+    if (!ik_cache) return MSA_ERR_NULL_POINTER;
+    const int32_t hik = ik_cache->num_heads;
+    if (hik < 1 || num_iq_heads % hik) return MSA_ERR_SHAPE;
+    CacheDev ik;
+    const msa_status st = check_cache(ik_cache, hik, page_size, num_pages, &ik);
+    if (st != MSA_OK) return st;
+    if (num_tokens > 0 && max_blocks > 0) {
+        if (!iq || !positions || !seq_idx || !block_scores) return MSA_ERR_NULL_POINTER;
+        if (num_seqs > 0 && max_pages_per_seq > 0 && !page_table) return MSA_ERR_NULL_POINTER;
+    }
+    if (!aligned(iq, 16) || !aligned(positions, 4) || !aligned(seq_idx, 4) || !aligned(page_table, 4) ||
+        !aligned(block_scores, 8))
+        return MSA_ERR_ALIGNMENT;
+    if ((int64_t)max_blocks * block_tokens > 0x80000000LL) return MSA_ERR_SHAPE;   // block starts fit in int32
+    int64_t items, tmp;
+    if (__builtin_mul_overflow((int64_t)num_tokens, (int64_t)max_blocks, &items) || items + kWavesPerBlock > 0x7fffffffLL)
+        return MSA_ERR_SHAPE;
+    if (num_seqs > 0 && __builtin_mul_overflow((int64_t)num_seqs, page_table_stride, &tmp)) return MSA_ERR_OVERFLOW;
+    if (items == 0) return MSA_OK;
+
+    ScoreArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.iq = iq;
+    a.pos = positions;
+    a.seq = seq_idx;
+    a.pt = page_table;
+    a.pt_stride = page_table_stride;
+    a.num_pages = num_pages;
+    a.T = num_tokens;
+    a.S = num_seqs;
+    a.max_pages = max_pages_per_seq;
+    a.page_size = page_size;
+    a.page_shift = (page_size & (page_size - 1)) == 0 ? __builtin_ctz((unsigned)page_size) : -1;
+    a.hiq = num_iq_heads;
+    a.group = num_iq_heads / hik;
+    a.block_tokens = block_tokens;
+    a.max_blocks = max_blocks;
+    a.ik = ik;
+    a.out = block_scores;
+    const dim3 grid((unsigned)((items + kWavesPerBlock - 1) / kWavesPerBlock));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // Launches over pairs of index-Q heads that read the same index-K head (two heads' queries fit
+    // the registers at once).
+    for (int32_t h0 = 0; h0 < num_iq_heads;) {
+        const int32_t group_end = (h0 / a.group + 1) * a.group;
+        const int nh = (group_end - h0 >= kMaxHeadsPerLaunch) ? kMaxHeadsPerLaunch : 1;
+        a.head0 = h0;
+        void* args[] = {&a};
+        const hipError_t e = nh == 2
+            ? hipLaunchKernel(reinterpret_cast<const void*>(&index_scores_kernel<2>), grid, dim3(kBlock), args, 0, s)
+            : hipLaunchKernel(reinterpret_cast<const void*>(&index_scores_kernel<1>), grid, dim3(kBlock), args, 0, s);
+        if (e != hipSuccess) return MSA_ERR_LAUNCH;
+        h0 += nh;
+    }
+    return MSA_OK;
+}
+
+msa_status msa_index_topk(const double* block_scores, int32_t rows, int32_t max_blocks, int32_t top_k,
+                          int32_t* block_ids, int32_t* counts, void* stream)
+{
+    if (rows < 0 || max_blocks < 0 || max_blocks > kMaxRowBlocks || top_k < 1 || top_k > kMaxTopK)
+        return MSA_ERR_SHAPE;
+    if (rows == 0) return MSA_OK;
+    if (!block_ids || (max_blocks > 0 && !block_scores)) return MSA_ERR_NULL_POINTER;
+    if (!aligned(block_scores, 8) || !aligned(block_ids, 4) || !aligned(counts, 4)) return MSA_ERR_ALIGNMENT;
+    const dim3 grid((unsigned)(((int64_t)rows + kWavesPerBlock - 1) / kWavesPerBlock));
+    void* args[] = {const_cast<double**>(&block_scores), &rows, &max_blocks, &top_k, &block_ids, &counts};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&index_topk_kernel), grid, dim3(kBlock), args, 0,
+                                         static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MSA_OK : MSA_ERR_LAUNCH;
+}
+
+}  // extern "C"

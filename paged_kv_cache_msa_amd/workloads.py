@@ -378,3 +378,26 @@ def verify_window(draft_len: int = 3, seqs: int = 64, seed: int = 5, cache_dtype
     caches = [_hnd_cache(num_pages, h, cache_dtype, s) for h, s in zip((hkv, hkv, hik), scales)]
     return Workload(f"verify window {seqs} seqs x (1 + {draft_len}) tokens, {num_pages}-page pool", hq, hkv, hiq, hik,
                     D, P, num_pages, x, pos, seq, pt, w, caches)
+
+
+def index_cache_fill(wl: Workload, seed: int = 99) -> np.ndarray:
+    """Pre-populated index-K cache storage (the keys of earlier tokens): random finite codes over the
+    whole storage (fp8: every byte except the NaN codes 0x7F / 0xFF; bf16: N(0, 1) values)."""
+    c = wl.caches[2]
+    rng = np.random.Generator(np.random.PCG64([seed, 7]))
+    if c.dtype == FP8_E4M3:
+        codes = rng.integers(0, 254, c.storage_elems, dtype=np.uint16).astype(np.uint8)
+        codes[codes >= 0x7F] += 1            # 0..253 -> every code but 0x7F and 0xFF
+        return codes
+    return to_bf16_bits(rng.standard_normal(c.storage_elems, dtype=np.float32))
+
+
+def index_queries(T: int, hiq: int, seed: int = 98) -> np.ndarray:
+    """Index-Q rows [T, hiq, 128] as bf16 bits, N(0, 1)."""
+    rng = np.random.Generator(np.random.PCG64([seed, 8]))
+    return to_bf16_bits(rng.standard_normal((T, hiq, HEAD_DIM), dtype=np.float32))
+
+
+def index_blocks(wl: Workload, block_tokens: int = 128) -> int:
+    """Row length of the block-score table: enough blocks for the largest position."""
+    return int(wl.positions.max()) // block_tokens + 1 if wl.T else 0

@@ -11,7 +11,8 @@ import paged_kv_cache_msa_amd as msa
 from paged_kv_cache_msa_amd import _build
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "msa_produce.h")
+HEADERS = [os.path.join(ROOT, "include", n) for n in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if n.endswith(".h")]
 
 OK, NULLP, UNSUP, SHAPE, STRIDE, ALIGN, DTYPE, OVERFLOW = 0, 1, 2, 3, 4, 5, 6, 7
 
@@ -24,14 +25,17 @@ def L():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(msa_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(msa_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert set(names) >= {"msa_produce", "msa_rope_table", "msa_quantize", "msa_rms_scale", "msa_status_string"}
+    assert set(names) >= {"msa_produce", "msa_rope_table", "msa_quantize", "msa_rms_scale", "msa_status_string",
+                          "msa_index_scores", "msa_index_topk"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -153,3 +157,24 @@ def _has_gpu():
                                 dict(pt=None)])
 def test_rejects_null_inputs_with_tokens(L, kw):
     assert call(L, T=64, **kw) == NULLP
+
+
+def test_index_entry_points_validate(L):
+    ik = view(sp=64 * 128, heads=1)
+    ref = ctypes.byref
+    # head_dim, negative counts, group mismatch, block size, null cache, overflow of block starts
+    assert L.msa_index_scores(Q, 64, 64, 2, POS, SEQ, PT, 160, 64, 160, 64, 10240, ref(ik), 128, 72, SLOTS, None) == UNSUP
+    assert L.msa_index_scores(Q, -1, 128, 2, POS, SEQ, PT, 160, 64, 160, 64, 10240, ref(ik), 128, 72, SLOTS, None) == SHAPE
+    assert L.msa_index_scores(Q, 0, 128, 3, POS, SEQ, PT, 160, 64, 160, 64, 10240, ref(view(sp=2 * 64 * 128)), 128, 72,
+                              SLOTS, None) == SHAPE
+    assert L.msa_index_scores(Q, 0, 128, 2, POS, SEQ, PT, 160, 64, 160, 64, 10240, ref(ik), 0, 72, SLOTS, None) == SHAPE
+    assert L.msa_index_scores(Q, 0, 128, 2, POS, SEQ, PT, 160, 64, 160, 64, 10240, None, 128, 72, SLOTS, None) == NULLP
+    assert L.msa_index_scores(Q, 0, 128, 2, POS, SEQ, PT, 160, 64, 160, 64, 10240, ref(ik), 1 << 20, 1 << 12, SLOTS,
+                              None) == SHAPE
+    assert L.msa_index_scores(Q + 8, 0, 128, 2, POS, SEQ, PT, 160, 64, 160, 64, 10240, ref(ik), 128, 72, SLOTS, None) == ALIGN
+    assert L.msa_index_scores(Q, 0, 128, 2, POS, SEQ, PT, 160, 64, 160, 64, 10240, ref(ik), 128, 72, SLOTS, None) == OK
+    assert L.msa_index_topk(SLOTS, 10, 72, 0, Q, None, None) == SHAPE
+    assert L.msa_index_topk(SLOTS, 10, 72, 65, Q, None, None) == SHAPE
+    assert L.msa_index_topk(SLOTS, 10, 5000, 16, Q, None, None) == SHAPE
+    assert L.msa_index_topk(SLOTS + 4, 10, 72, 16, Q, None, None) == ALIGN
+    assert L.msa_index_topk(SLOTS, 0, 72, 16, Q, None, None) == OK

@@ -1,0 +1,154 @@
+"""GPU parity of the indexer (msa_index_scores + msa_index_topk, through the C ABI) against the CPU
+oracle.  Block scores are exact binary64 sums on both sides, so they are compared bit for bit, and so
+are the selected block ids and the per-row counts.
+
+Inputs never come from the HIP path: the standalone cases draw index-Q and a pre-populated index-K
+cache from the seeded generator; the chained cases run the GPU producer then the GPU indexer, and
+the oracle producer then the oracle indexer, from the same generated inputs."""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_msa_amd as msa
+from paged_kv_cache_msa_amd import workloads as W
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+THREADS = min(16, os.cpu_count() or 1)
+TOPK = 16
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    msa.lib()
+
+
+def say(*a):
+    print(*a, flush=True, file=sys.stderr)
+
+
+def ik_device(wl, fill):
+    c = wl.caches[2]
+    if c.dtype == W.FP8_E4M3:
+        st = torch.from_numpy(fill).cuda()
+    else:
+        st = torch.from_numpy(fill.view(np.int16)).cuda()
+    view = st.as_strided((wl.num_pages, c.heads, wl.page_size, 128), (*c.strides, 1))
+    scale = torch.tensor([c.scale], dtype=torch.float32, device="cuda")
+    return st, view, scale
+
+
+def gpu_index(wl, iq_dev, pos, seq, pt, ik_view, ik_scale, nb):
+    bs = torch.full((iq_dev.shape[1], wl.T, nb), 7.0, dtype=torch.float64, device="cuda")
+    ids = torch.full((iq_dev.shape[1], wl.T, TOPK), -9, dtype=torch.int32, device="cuda")
+    counts = torch.full((iq_dev.shape[1], wl.T), -9, dtype=torch.int32, device="cuda")
+    msa.msa_index_scores(iq_dev, pos, seq, pt, ik_view, bs, ik_scale=ik_scale, num_pages=wl.num_pages)
+    msa.msa_index_topk(bs, ids, counts)
+    torch.cuda.synchronize()
+    return bs.cpu().numpy(), ids.cpu().numpy(), counts.cpu().numpy()
+
+
+def oracle_index(wl, iq_bits, ik_storage, nb):
+    c = wl.caches[2]
+    bs = oracle.index_scores(iq_bits, wl.positions, wl.seq_idx, wl.page_table, wl.max_pages, wl.num_seqs,
+                             wl.max_pages, wl.page_size, wl.num_pages, ik_storage, c.strides, c.heads, c.dtype,
+                             c.scale, 128, nb)
+    ids, counts = oracle.index_topk(bs, TOPK)
+    return bs, ids, counts
+
+
+def compare(name, got, ref):
+    gbs, gids, gc = got
+    rbs, rids, rc = ref
+    diff = np.argwhere(~((gbs == rbs) | (np.isneginf(gbs) & np.isneginf(rbs))))
+    assert diff.size == 0, f"{name}: {len(diff)} block scores differ, first {diff[:3]}"
+    np.testing.assert_array_equal(gids, rids)
+    np.testing.assert_array_equal(gc, rc)
+    say(f"  {name}: block scores, ids and counts identical ({rbs.shape[1]} tokens x {rbs.shape[0]} heads, "
+        f"{int(np.isfinite(rbs).sum())} scored blocks)")
+
+
+@pytest.mark.parametrize("dtype", [W.FP8_E4M3, W.BF16], ids=["fp8", "bf16"])
+def test_index_standalone_decode64(dtype):
+    wl = W.config1()
+    if dtype == W.BF16:
+        wl.caches[2].dtype = W.BF16
+    fill = W.index_cache_fill(wl)
+    iq = W.index_queries(wl.T, wl.hiq)
+    nb = W.index_blocks(wl)
+    st, view, scale = ik_device(wl, fill)
+    dev = W.to_device(wl)
+    say(f"[gpu] msa_index_scores/topk standalone decode-64, {nb} blocks, {'fp8' if dtype == 0 else 'bf16'}")
+    got = gpu_index(wl, torch.from_numpy(iq.view(np.int16)).cuda(), dev.positions, dev.seq_idx, dev.page_table,
+                    view, scale, nb)
+    compare("standalone", got, oracle_index(wl, iq, fill, nb))
+
+
+@pytest.mark.parametrize("make", [lambda: W.config1(), lambda: W.config2(), lambda: W.verify_window(draft_len=3)],
+                         ids=["decode64", "decode256-padded", "verify-window"])
+def test_producer_then_indexer(make):
+    """The chain of one sparse layer's front half: produce (writes this step's index-K), then score and
+    select with this step's index-Q."""
+    wl = make()
+    fill = W.index_cache_fill(wl)
+    nb = W.index_blocks(wl)
+    d = W.to_device(wl)
+    c = wl.caches[2]
+    ik_store = torch.from_numpy(fill).cuda() if c.dtype == W.FP8_E4M3 else torch.from_numpy(fill.view(np.int16)).cuda()
+    d.storages[2] = ik_store
+    d.caches[2] = ik_store.as_strided((wl.num_pages, c.heads, wl.page_size, 128), (*c.strides, 1))
+    say(f"[gpu] produce then index: {wl.name}, {nb} blocks")
+    msa.msa_produce(d.x, d.positions, d.seq_idx, d.page_table, *d.weights, d.q_out, d.iq_out,
+                    d.caches[0], d.caches[1], d.caches[2], k_scale=d.scales[0], v_scale=d.scales[1],
+                    ik_scale=d.scales[2], num_pages=wl.num_pages, rms_eps=wl.eps, rope_theta=wl.theta,
+                    slots_out=d.slots)
+    got = gpu_index(wl, d.iq_out.view(torch.int16), d.positions, d.seq_idx, d.page_table, d.caches[2],
+                    d.scales[2], nb)
+    # oracle chain on host copies of the same generated inputs
+    host = [H.cache_fill(wl.caches[0]), H.cache_fill(wl.caches[1]), fill.copy()]
+    caches = [dict(storage=s, strides=cs.strides, dtype=cs.dtype, scale=cs.scale) for s, cs in zip(host, wl.caches)]
+    r = oracle.produce(wl.x, wl.x_stride, wl.T, wl.head_dim, wl.hq, wl.hkv, wl.hiq, wl.hik, wl.positions,
+                       wl.seq_idx, wl.page_table, wl.max_pages, wl.num_seqs, wl.max_pages, wl.page_size,
+                       wl.num_pages, *wl.weights, wl.eps, wl.theta, caches, num_threads=THREADS)
+    compare("chain", got, oracle_index(wl, r["iq"], host[2], nb))
+
+
+@pytest.mark.parametrize("hiq,hik", [(4, 1), (4, 2), (1, 1), (3, 1)])
+def test_index_head_groups(hiq, hik):
+    """Several index-Q heads per index-K head and several index-K heads (head h reads h // (hiq/hik))."""
+    wl = W.ragged(40, seed=hiq * 10 + hik, heads=(2, 1, hiq, hik), pad_frac=0.1)
+    fill = W.index_cache_fill(wl, seed=hiq)
+    iq = W.index_queries(wl.T, hiq, seed=hik)
+    nb = W.index_blocks(wl) + 3          # extra, never-visible blocks stay -inf
+    st, view, scale = ik_device(wl, fill)
+    dev = W.to_device(wl)
+    got = gpu_index(wl, torch.from_numpy(iq.view(np.int16)).cuda(), dev.positions, dev.seq_idx, dev.page_table,
+                    view, scale, nb)
+    compare(f"groups {hiq}/{hik}", got, oracle_index(wl, iq, fill, nb))
+
+
+def test_topk_rows_with_ties_and_gaps():
+    """Rows of up to 4096 blocks with repeated scores, -inf gaps and NaN entries."""
+    rng = np.random.default_rng(8)
+    rows, nb = 64, 4096
+    bs = rng.integers(-20, 20, (rows, nb)).astype(np.float64)      # many exact ties
+    bs[rng.random((rows, nb)) < 0.3] = -np.inf
+    bs[rng.random((rows, nb)) < 0.01] = np.nan
+    bs[5, :] = -np.inf                                              # nothing selectable
+    bs[6, :10] = 1.0                                                # fewer than k candidates
+    bs[6, 10:] = -np.inf
+    for k in (1, 16, 64):
+        d = torch.from_numpy(bs).cuda()
+        ids = torch.full((rows, k), -9, dtype=torch.int32, device="cuda")
+        cnt = torch.full((rows,), -9, dtype=torch.int32, device="cuda")
+        msa.msa_index_topk(d, ids, cnt)
+        torch.cuda.synchronize()
+        rids, rc = oracle.index_topk(bs[None], k)
+        np.testing.assert_array_equal(ids.cpu().numpy(), rids[0])
+        np.testing.assert_array_equal(cnt.cpu().numpy(), rc[0])
