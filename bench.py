@@ -125,6 +125,59 @@ def bench_prefill(msa, W, torch, iters, warmup):
     return out
 
 
+def bench_indexer(msa, W, torch, np, reps):
+    """Indexer at decode batch 64 (positions 7000..9199, about 8k keys per sequence in a pre-populated
+    fp8 index-K cache): msa_index_scores + msa_index_topk (top 16 of 128-token blocks), 20 calls per
+    captured graph, `reps` graph replays timed after 5 warm ones."""
+    wl = W.config1()
+    fill = W.index_cache_fill(wl)
+    iq = torch.from_numpy(W.index_queries(wl.T, wl.hiq).view(np.int16)).cuda()
+    nb = W.index_blocks(wl)
+    c = wl.caches[2]
+    store = torch.from_numpy(fill).cuda()
+    view = store.as_strided((wl.num_pages, c.heads, wl.page_size, 128), (*c.strides, 1))
+    scale = torch.tensor([c.scale], dtype=torch.float32, device="cuda")
+    pos = torch.from_numpy(wl.positions).cuda()
+    seq = torch.from_numpy(wl.seq_idx).cuda()
+    pt = torch.from_numpy(np.ascontiguousarray(wl.page_table)).cuda()
+    bs = torch.empty((wl.hiq, wl.T, nb), dtype=torch.float64, device="cuda")
+    ids = torch.empty((wl.hiq, wl.T, 16), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((wl.hiq, wl.T), dtype=torch.int32, device="cuda")
+    per_graph = 20
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        msa.msa_index_scores(iq, pos, seq, pt, view, bs, ik_scale=scale, num_pages=wl.num_pages)
+        msa.msa_index_topk(bs, ids, cnt)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(per_graph):
+                msa.msa_index_scores(iq, pos, seq, pt, view, bs, ik_scale=scale, num_pages=wl.num_pages)
+                msa.msa_index_topk(bs, ids, cnt)
+        for _ in range(5):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(reps):
+            g.replay()
+        e1.record(s)
+        torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000 / (reps * per_graph)
+    keys = int((wl.positions.astype(np.int64) + 1).sum())
+    # keys (128 B each, shared by both index-Q heads) + index-Q rows + token metadata + one page-table
+    # entry per 64 keys + the block-score table written and read back + the selected ids
+    b = (keys * 128 + wl.T * wl.hiq * 256 + wl.T * 8 + keys // 64 * 4 + 2 * wl.hiq * wl.T * nb * 8
+         + wl.hiq * wl.T * (16 * 4 + 4))
+    gbs = b / (us * 1e-6) / 1e9
+    return dict(workload=f"decode batch 64 indexer: {keys} visible fp8 index-K keys, 2 index-Q heads, "
+                         f"{nb} blocks of 128 tokens, top 16",
+                us_per_call=us, algorithmic_bytes_per_call=b,
+                roofline=dict(bound="hbm", achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=gbs / HBM_PEAK_GBS,
+                              traffic=None, kernel="index_scores_kernel<2> + index_topk_kernel"))
+
+
 def cpu_baseline(W, seconds: float):
     """The CPU oracle as it stands, on leading slices of the prefill workload for about `seconds`."""
     import oracle
@@ -162,6 +215,7 @@ def main():
     ap.add_argument("--decode-warmup", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-indexer", action="store_true", help="skip the indexer measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run three plain 1 GiB device-to-device copies (the reference kernel that "
                          "scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
@@ -197,6 +251,9 @@ def main():
     del dec["devs"]
     torch.cuda.empty_cache()
 
+    import numpy as np
+    idx = None if args.no_indexer else bench_indexer(msa, W, torch, np, 50)
+    torch.cuda.empty_cache()
     pre = bench_prefill(msa, W, torch, args.steps, args.warmup)
     cpu = None if args.no_cpu_baseline else cpu_baseline(W, args.cpu_seconds)
 
@@ -242,6 +299,7 @@ def main():
                 "kernel": "produce_kernel<1, 16, 2, 2, 1> (decode batch 64)", "avg_launch_us": launch_us,
             },
         },
+        "indexer": idx,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

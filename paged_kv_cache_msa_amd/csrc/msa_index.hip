@@ -88,29 +88,46 @@ __device__ __forceinline__ int64_t page_of(const ScoreArgs& a, int32_t sq, int32
     return pg;
 }
 
-// Decode 16 cache elements of one key (this lane's share) to binary64.
-__device__ __forceinline__ void load_key(const CacheDev& c, int64_t e, double* k)
+// This lane's 16 elements of one key, raw: fp8 keys take 16 bytes (two 8-byte loads; cache strides
+// are multiples of 8 elements, so an fp8 row share is 8-byte but not always 16-byte aligned), bf16
+// keys 32 bytes.
+template <bool kBf16>
+struct KeyRaw {
+    uint32_t w[kBf16 ? 8 : 4];
+};
+
+template <bool kBf16>
+__device__ __forceinline__ KeyRaw<kBf16> load_key(const CacheDev& c, int64_t e)
 {
-    if (c.is_bf16) {
+    KeyRaw<kBf16> r;
+    if (kBf16) {
         const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(c.data) + e);
         const uint4 lo = src[0], hi = src[1];
-        const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            k[2 * i] = (double)__uint_as_float(w[i] << 16);
-            k[2 * i + 1] = (double)__uint_as_float(w[i] & 0xffff0000u);
-        }
+        r.w[0] = lo.x; r.w[1] = lo.y; r.w[2] = lo.z; r.w[3] = lo.w;
+        r.w[kBf16 ? 4 : 0] = hi.x; r.w[kBf16 ? 5 : 1] = hi.y; r.w[kBf16 ? 6 : 2] = hi.z; r.w[kBf16 ? 7 : 3] = hi.w;
     } else {
-        // Two 8-byte loads: cache strides are multiples of 8 elements, so an fp8 row share is
-        // 8-byte aligned but not necessarily 16-byte aligned.
         const uint2 v0 = reinterpret_cast<const uint2*>(c.data + e)[0];
         const uint2 v1 = reinterpret_cast<const uint2*>(c.data + e)[1];
-        const uint32_t w[4] = {v0.x, v0.y, v1.x, v1.y};
+        r.w[0] = v0.x; r.w[1] = v0.y; r.w[2] = v1.x; r.w[3] = v1.y;
+    }
+    return r;
+}
+
+// Decode to binary64 (e4m3 and bf16 values are exact in binary32, hence in binary64).
+template <bool kBf16>
+__device__ __forceinline__ void decode_key(const KeyRaw<kBf16>& r, double* k)
+{
+    if (kBf16) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            k[2 * i] = (double)__uint_as_float(r.w[i] << 16);
+            k[2 * i + 1] = (double)__uint_as_float(r.w[i] & 0xffff0000u);
+        }
+    } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            // e4m3 -> binary32 is exact (every e4m3 value is a binary32 value)
-            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
-            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)r.w[i], false);
+            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)r.w[i], true);
             k[4 * i] = (double)lo[0];
             k[4 * i + 1] = (double)lo[1];
             k[4 * i + 2] = (double)hi[0];
@@ -119,17 +136,20 @@ __device__ __forceinline__ void load_key(const CacheDev& c, int64_t e, double* k
     }
 }
 
-// One wavefront per (token, block); heads [head0, head0 + NH).
-template <int NH>
+// One wavefront per (token, block); heads [head0, head0 + NH).  The keys of a block are fetched in
+// batches of BATCH steps (8 keys per step): every page-table entry of a batch first, then every
+// key, then the arithmetic, so a wave waits on two memory round trips per batch, not two per step.
+template <int NH, bool kBf16>
 __global__ __launch_bounds__(kBlock) void index_scores_kernel(const ScoreArgs a)
 {
+    constexpr int BATCH = kBf16 ? 8 : 16;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const uint32_t item = blockIdx.x * kWavesPerBlock + wave;
     if (item >= (uint32_t)a.T * (uint32_t)a.max_blocks) return;   // wave-uniform
     const int32_t t = (int32_t)(item / (uint32_t)a.max_blocks);
     const int32_t b = (int32_t)(item - (uint32_t)t * (uint32_t)a.max_blocks);
-    const int ks = lane / kLanesPerKey;    // key slot of this step
+    const int ks = lane / kLanesPerKey;    // key slot of a step
     const int sub = lane % kLanesPerKey;   // element group within the key
 
     const int32_t pos = a.pos[t];
@@ -155,27 +175,37 @@ __global__ __launch_bounds__(kBlock) void index_scores_kernel(const ScoreArgs a)
                 q[h][2 * i + 1] = (double)__uint_as_float(w[i] & 0xffff0000u);
             }
         }
-        const double scale = a.ik.is_bf16 ? 1.0 : (double)*a.ik.scale;
+        const double scale = kBf16 ? 1.0 : (double)*a.ik.scale;
         const int32_t p_end = (int32_t)min((int64_t)p0 + a.block_tokens, (int64_t)pos + 1);
         const int64_t head_off = (int64_t)(a.head0 / a.group) * a.ik.sh;   // NH heads share one index-K head
-        for (int32_t pb = p0; pb < p_end; pb += kKeysPerStep) {
-            const int32_t p = pb + ks;
-            int32_t off = 0;
-            const int64_t pg = p < p_end ? page_of(a, sq, p, &off) : -1;
-            double k[kElemsPerLane];
-            if (pg >= 0) {
-                load_key(a.ik, pg * a.ik.sp + head_off + (int64_t)off * a.ik.st + sub * kElemsPerLane, k);
-            } else {
+        for (int32_t pb = p0; pb < p_end; pb += BATCH * kKeysPerStep) {
+            int64_t e[BATCH];
+            uint32_t live = 0;                     // bit i: key of step i exists and has a page
 #pragma unroll
-                for (int j = 0; j < kElemsPerLane; ++j) k[j] = 0.0;
+            for (int i = 0; i < BATCH; ++i) {
+                const int32_t p = pb + i * kKeysPerStep + ks;
+                int32_t off = 0;
+                const int64_t pg = p < p_end ? page_of(a, sq, p, &off) : -1;
+                // A key outside the block or without a valid page reads the pool's first row (a
+                // valid address) and is discarded.
+                e[i] = pg >= 0 ? pg * a.ik.sp + head_off + (int64_t)off * a.ik.st : 0;
+                live |= (pg >= 0 ? 1u : 0u) << i;
             }
+            KeyRaw<kBf16> raw[BATCH];
 #pragma unroll
-            for (int h = 0; h < NH; ++h) {
-                double acc = 0.0;
+            for (int i = 0; i < BATCH; ++i) raw[i] = load_key<kBf16>(a.ik, e[i] + sub * kElemsPerLane);
 #pragma unroll
-                for (int j = 0; j < kElemsPerLane; ++j) acc = __builtin_fma(q[h][j], k[j], acc);
-                const double dot = sum8(acc);
-                if (pg >= 0) best[h] = max_no_nan(best[h], dot * scale);
+            for (int i = 0; i < BATCH; ++i) {
+                double k[kElemsPerLane];
+                decode_key<kBf16>(raw[i], k);
+#pragma unroll
+                for (int h = 0; h < NH; ++h) {
+                    double acc = 0.0;
+#pragma unroll
+                    for (int j = 0; j < kElemsPerLane; ++j) acc = __builtin_fma(q[h][j], k[j], acc);
+                    const double dot = sum8(acc);
+                    if (live >> i & 1u) best[h] = max_no_nan(best[h], dot * scale);
+                }
             }
         }
     }
@@ -198,8 +228,52 @@ __device__ __forceinline__ bool before(double s1, int32_t i1, double s2, int32_t
     return s1 > s2 || (s1 == s2 && i1 < i2);
 }
 
-// One wavefront per row: top_k rounds of a wave-wide arg-max over the candidates ranked after the
-// previous pick (so no pick repeats and no membership list is needed).
+// Rows of up to kRankRowBlocks blocks: one wavefront per row stages the row in LDS, and every lane
+// computes the rank of each of its candidates (how many candidates are ordered before it); a
+// candidate of rank r < top_k is the r-th pick.  No serial rounds.
+constexpr int kRankRowBlocks = 512;
+
+__global__ __launch_bounds__(kBlock) void index_topk_rank_kernel(const double* scores, int32_t rows, int32_t nb,
+                                                                 int32_t top_k, int32_t* ids, int32_t* counts)
+{
+    __shared__ double row_lds[kWavesPerBlock][kRankRowBlocks];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int32_t r = (int32_t)(blockIdx.x * kWavesPerBlock + wave);
+    if (r >= rows) return;   // wave-uniform; only wave-level synchronisation below
+    const double* row = scores + (int64_t)r * nb;
+    double* sh = row_lds[wave];
+    int n_local = 0;
+    for (int32_t i = lane; i < nb; i += kWave) {
+        const double v = row[i];
+        const bool cand = v > -INFINITY;              // -inf and NaN are never picked
+        sh[i] = cand ? v : -INFINITY;
+        n_local += cand;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    int32_t n = n_local;
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) n += __shfl_xor(n, m);
+    const int32_t picked = n < top_k ? n : top_k;
+    int32_t* out = ids + (int64_t)r * top_k;
+    for (int32_t k = picked + lane; k < top_k; k += kWave) out[k] = -1;
+    for (int32_t i = lane; i < nb; i += kWave) {
+        const double si = sh[i];
+        if (!(si > -INFINITY)) continue;
+        int32_t rank = 0;
+        for (int32_t j = 0; j < nb; ++j) {
+            const double sj = sh[j];
+            rank += (sj > si || (sj == si && j < i)) ? 1 : 0;   // -inf entries never count
+        }
+        if (rank < top_k) out[rank] = i;
+    }
+    if (counts && lane == 0) counts[r] = picked;
+}
+
+// Longer rows: one wavefront per row, top_k rounds of a wave-wide arg-max over the candidates ranked
+// after the previous pick (so no pick repeats and no membership list is needed).
 __global__ __launch_bounds__(kBlock) void index_topk_kernel(const double* scores, int32_t rows, int32_t nb,
                                                             int32_t top_k, int32_t* ids, int32_t* counts)
 {
@@ -301,9 +375,11 @@ msa_status msa_index_scores(const uint16_t* iq, int32_t num_tokens, int32_t head
         const int nh = (group_end - h0 >= kMaxHeadsPerLaunch) ? kMaxHeadsPerLaunch : 1;
         a.head0 = h0;
         void* args[] = {&a};
-        const hipError_t e = nh == 2
-            ? hipLaunchKernel(reinterpret_cast<const void*>(&index_scores_kernel<2>), grid, dim3(kBlock), args, 0, s)
-            : hipLaunchKernel(reinterpret_cast<const void*>(&index_scores_kernel<1>), grid, dim3(kBlock), args, 0, s);
+        const void* fn = ik.is_bf16 ? (nh == 2 ? reinterpret_cast<const void*>(&index_scores_kernel<2, true>)
+                                               : reinterpret_cast<const void*>(&index_scores_kernel<1, true>))
+                                    : (nh == 2 ? reinterpret_cast<const void*>(&index_scores_kernel<2, false>)
+                                               : reinterpret_cast<const void*>(&index_scores_kernel<1, false>));
+        const hipError_t e = hipLaunchKernel(fn, grid, dim3(kBlock), args, 0, s);
         if (e != hipSuccess) return MSA_ERR_LAUNCH;
         h0 += nh;
     }
@@ -320,8 +396,9 @@ msa_status msa_index_topk(const double* block_scores, int32_t rows, int32_t max_
     if (!aligned(block_scores, 8) || !aligned(block_ids, 4) || !aligned(counts, 4)) return MSA_ERR_ALIGNMENT;
     const dim3 grid((unsigned)(((int64_t)rows + kWavesPerBlock - 1) / kWavesPerBlock));
     void* args[] = {const_cast<double**>(&block_scores), &rows, &max_blocks, &top_k, &block_ids, &counts};
-    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&index_topk_kernel), grid, dim3(kBlock), args, 0,
-                                         static_cast<hipStream_t>(stream));
+    const void* fn = max_blocks <= kRankRowBlocks ? reinterpret_cast<const void*>(&index_topk_rank_kernel)
+                                                  : reinterpret_cast<const void*>(&index_topk_kernel);
+    const hipError_t e = hipLaunchKernel(fn, grid, dim3(kBlock), args, 0, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MSA_OK : MSA_ERR_LAUNCH;
 }
 

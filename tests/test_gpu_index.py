@@ -133,16 +133,19 @@ def test_index_head_groups(hiq, hik):
     compare(f"groups {hiq}/{hik}", got, oracle_index(wl, iq, fill, nb))
 
 
-def test_topk_rows_with_ties_and_gaps():
-    """Rows of up to 4096 blocks with repeated scores, -inf gaps and NaN entries."""
-    rng = np.random.default_rng(8)
-    rows, nb = 64, 4096
+@pytest.mark.parametrize("nb", [100, 512, 513, 4096])
+def test_topk_rows_with_ties_and_gaps(nb):
+    """Rows with repeated scores, -inf gaps and NaN entries; row lengths on both sides of the switch
+    between the rank-based (<= 512 blocks) and the round-based selection."""
+    rng = np.random.default_rng(8 + nb)
+    rows = 64
     bs = rng.integers(-20, 20, (rows, nb)).astype(np.float64)      # many exact ties
     bs[rng.random((rows, nb)) < 0.3] = -np.inf
     bs[rng.random((rows, nb)) < 0.01] = np.nan
     bs[5, :] = -np.inf                                              # nothing selectable
-    bs[6, :10] = 1.0                                                # fewer than k candidates
+    bs[6, :10] = 1.0                                                # fewer than k candidates, all tied
     bs[6, 10:] = -np.inf
+    bs[7, :] = 3.0                                                  # one long tie
     for k in (1, 16, 64):
         d = torch.from_numpy(bs).cuda()
         ids = torch.full((rows, k), -9, dtype=torch.int32, device="cuda")
