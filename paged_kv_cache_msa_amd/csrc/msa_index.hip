@@ -139,10 +139,12 @@ __device__ __forceinline__ void decode_key(const KeyRaw<kBf16>& r, double* k)
 // One wavefront per (token, block); heads [head0, head0 + NH).  The keys of a block are fetched in
 // batches of BATCH steps (8 keys per step): every page-table entry of a batch first, then every
 // key, then the arithmetic, so a wave waits on two memory round trips per batch, not two per step.
-template <int NH, bool kBf16>
+// kStepInPage: page_size and block_tokens are multiples of 8, so the 8 keys of a step always share
+// one page: the page lookup and the 64-bit page base are then wave-uniform (scalar) per step.
+template <int NH, bool kBf16, bool kStepInPage>
 __global__ __launch_bounds__(kBlock) void index_scores_kernel(const ScoreArgs a)
 {
-    constexpr int BATCH = kBf16 ? 8 : 16;
+    constexpr int BATCH = 8;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const uint32_t item = blockIdx.x * kWavesPerBlock + wave;
@@ -184,8 +186,18 @@ __global__ __launch_bounds__(kBlock) void index_scores_kernel(const ScoreArgs a)
 #pragma unroll
             for (int i = 0; i < BATCH; ++i) {
                 const int32_t p = pb + i * kKeysPerStep + ks;
+                int64_t pg;
                 int32_t off = 0;
-                const int64_t pg = p < p_end ? page_of(a, sq, p, &off) : -1;
+                if (kStepInPage) {
+                    // the step's first position decides the page for all 8 keys (wave-uniform)
+                    const int32_t ps = pb + i * kKeysPerStep;
+                    int32_t off0 = 0;
+                    const int64_t pgs = ps < p_end ? page_of(a, sq, ps, &off0) : -1;
+                    pg = p < p_end ? pgs : -1;
+                    off = off0 + ks;
+                } else {
+                    pg = p < p_end ? page_of(a, sq, p, &off) : -1;
+                }
                 // A key outside the block or without a valid page reads the pool's first row (a
                 // valid address) and is discarded.
                 e[i] = pg >= 0 ? pg * a.ik.sp + head_off + (int64_t)off * a.ik.st : 0;
@@ -263,6 +275,7 @@ __global__ __launch_bounds__(kBlock) void index_topk_rank_kernel(const double* s
         const double si = sh[i];
         if (!(si > -INFINITY)) continue;
         int32_t rank = 0;
+#pragma unroll 8
         for (int32_t j = 0; j < nb; ++j) {
             const double sj = sh[j];
             rank += (sj > si || (sj == si && j < i)) ? 1 : 0;   // -inf entries never count
@@ -375,10 +388,18 @@ msa_status msa_index_scores(const uint16_t* iq, int32_t num_tokens, int32_t head
         const int nh = (group_end - h0 >= kMaxHeadsPerLaunch) ? kMaxHeadsPerLaunch : 1;
         a.head0 = h0;
         void* args[] = {&a};
-        const void* fn = ik.is_bf16 ? (nh == 2 ? reinterpret_cast<const void*>(&index_scores_kernel<2, true>)
-                                               : reinterpret_cast<const void*>(&index_scores_kernel<1, true>))
-                                    : (nh == 2 ? reinterpret_cast<const void*>(&index_scores_kernel<2, false>)
-                                               : reinterpret_cast<const void*>(&index_scores_kernel<1, false>));
+        const bool in_page = page_size % kKeysPerStep == 0 && block_tokens % kKeysPerStep == 0;
+        const void* fn;
+        if (in_page)
+            fn = ik.is_bf16 ? (nh == 2 ? reinterpret_cast<const void*>(&index_scores_kernel<2, true, true>)
+                                       : reinterpret_cast<const void*>(&index_scores_kernel<1, true, true>))
+                            : (nh == 2 ? reinterpret_cast<const void*>(&index_scores_kernel<2, false, true>)
+                                       : reinterpret_cast<const void*>(&index_scores_kernel<1, false, true>));
+        else
+            fn = ik.is_bf16 ? (nh == 2 ? reinterpret_cast<const void*>(&index_scores_kernel<2, true, false>)
+                                       : reinterpret_cast<const void*>(&index_scores_kernel<1, true, false>))
+                            : (nh == 2 ? reinterpret_cast<const void*>(&index_scores_kernel<2, false, false>)
+                                       : reinterpret_cast<const void*>(&index_scores_kernel<1, false, false>));
         const hipError_t e = hipLaunchKernel(fn, grid, dim3(kBlock), args, 0, s);
         if (e != hipSuccess) return MSA_ERR_LAUNCH;
         h0 += nh;

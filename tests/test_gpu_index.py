@@ -44,21 +44,22 @@ def ik_device(wl, fill):
     return st, view, scale
 
 
-def gpu_index(wl, iq_dev, pos, seq, pt, ik_view, ik_scale, nb):
+def gpu_index(wl, iq_dev, pos, seq, pt, ik_view, ik_scale, nb, block_tokens=128):
     bs = torch.full((iq_dev.shape[1], wl.T, nb), 7.0, dtype=torch.float64, device="cuda")
     ids = torch.full((iq_dev.shape[1], wl.T, TOPK), -9, dtype=torch.int32, device="cuda")
     counts = torch.full((iq_dev.shape[1], wl.T), -9, dtype=torch.int32, device="cuda")
-    msa.msa_index_scores(iq_dev, pos, seq, pt, ik_view, bs, ik_scale=ik_scale, num_pages=wl.num_pages)
+    msa.msa_index_scores(iq_dev, pos, seq, pt, ik_view, bs, ik_scale=ik_scale, num_pages=wl.num_pages,
+                         block_tokens=block_tokens)
     msa.msa_index_topk(bs, ids, counts)
     torch.cuda.synchronize()
     return bs.cpu().numpy(), ids.cpu().numpy(), counts.cpu().numpy()
 
 
-def oracle_index(wl, iq_bits, ik_storage, nb):
+def oracle_index(wl, iq_bits, ik_storage, nb, block_tokens=128):
     c = wl.caches[2]
     bs = oracle.index_scores(iq_bits, wl.positions, wl.seq_idx, wl.page_table, wl.max_pages, wl.num_seqs,
                              wl.max_pages, wl.page_size, wl.num_pages, ik_storage, c.strides, c.heads, c.dtype,
-                             c.scale, 128, nb)
+                             c.scale, block_tokens, nb)
     ids, counts = oracle.index_topk(bs, TOPK)
     return bs, ids, counts
 
@@ -131,6 +132,21 @@ def test_index_head_groups(hiq, hik):
     got = gpu_index(wl, torch.from_numpy(iq.view(np.int16)).cuda(), dev.positions, dev.seq_idx, dev.page_table,
                     view, scale, nb)
     compare(f"groups {hiq}/{hik}", got, oracle_index(wl, iq, fill, nb))
+
+
+@pytest.mark.parametrize("block_tokens", [100, 36, 256])
+def test_index_other_block_sizes(block_tokens):
+    """Block sizes that are not multiples of the 8-key step (steps straddle pages: per-key page
+    lookups) and a larger one."""
+    wl = W.ragged(48, seed=block_tokens, pad_frac=0.1)
+    fill = W.index_cache_fill(wl, seed=block_tokens)
+    iq = W.index_queries(wl.T, wl.hiq, seed=block_tokens)
+    nb = int(wl.positions.max()) // block_tokens + 1
+    st, view, scale = ik_device(wl, fill)
+    dev = W.to_device(wl)
+    got = gpu_index(wl, torch.from_numpy(iq.view(np.int16)).cuda(), dev.positions, dev.seq_idx, dev.page_table,
+                    view, scale, nb, block_tokens=block_tokens)
+    compare(f"block {block_tokens}", got, oracle_index(wl, iq, fill, nb, block_tokens=block_tokens))
 
 
 @pytest.mark.parametrize("nb", [100, 512, 513, 4096])
