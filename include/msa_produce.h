@@ -30,8 +30,9 @@
  *     device-side faults surface at the caller's next synchronisation.
  *   - Every argument check runs on the host before any launch: on any status other than MSA_OK
  *     nothing was launched and no output byte changed.
- *   - The library holds no global mutable state; concurrent calls from several host threads are
- *     safe as long as their outputs do not overlap.
+ *   - The only state the library keeps between calls is a per-host-thread memo of the RoPE
+ *     inverse frequencies for the last theta (a pure function of theta); concurrent calls from
+ *     several host threads are safe as long as their outputs do not overlap.
  */
 #ifndef MSA_PRODUCE_H
 #define MSA_PRODUCE_H
