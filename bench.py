@@ -11,6 +11,8 @@ The metric has two parts, measured on two workloads:
     heads, fp8 caches of 10,240 pages per layer; 60 layer calls (each with its own input row, norm
     weights, scales and caches) captured once in a HIP graph and replayed.  Reported as
     `us_per_layer_call` and `us_per_decode_step`, with their own roofline under `decode`.
+Also reported: the indexer at decode batch 64 (`indexer`), and the same decode step and prefill
+chunk through the unfused path (`unfused`: 14 launches per layer instead of one, identical bytes).
 Inputs are resident in HBM before every timed region.  `cpu_baseline` is the CPU oracle on a
 bounded sample of the prefill workload.
 
@@ -31,7 +33,9 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "producer HBM GB/s (% of peak) + µs per layer call at decode batch 64"
-KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_msa_amd", "csrc", "msa_produce.hip")
+# sources the fused producer kernel is compiled from (the counters are tied to their digest)
+KERNEL_SRCS = [os.path.join(ROOT, "paged_kv_cache_msa_amd", "csrc", n)
+               for n in ("msa_produce.hip", "msa_device.h", "msa_common.h")]
 COUNTERS = os.path.join(ROOT, "profiles", "produce_kernel_hbm_counters.json")
 
 
@@ -40,8 +44,11 @@ def log(*a):
 
 
 def kernel_digest() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def counter_traffic(workload_key: str):
@@ -100,7 +107,60 @@ def bench_decode(msa, W, torch, layers, steps, warmup):
                 bytes_per_step=bytes_per_call * layers, launches=steps * layers, wls=wls, devs=devs)
 
 
-def bench_prefill(msa, W, torch, iters, warmup):
+def unfused_call(msa, wl, d, slots, ws, stream=None):
+    msa.msa_produce_unfused(d.x, d.positions, slots, *d.weights, d.q_out, d.iq_out, d.caches[0], d.caches[1],
+                            d.caches[2], workspace=ws, k_scale=d.scales[0], v_scale=d.scales[1],
+                            ik_scale=d.scales[2], num_pages=wl.num_pages, rms_eps=wl.eps, rope_theta=wl.theta,
+                            stream=stream)
+
+
+def unfused_launches(wl):
+    """Launches of one msa_produce_unfused call: two norm/RoPE producers plus four per cache."""
+    prods = int(wl.hq + wl.hkv > 0) + int(wl.hiq + wl.hik > 0)
+    return prods + 4 * (2 * int(wl.hkv > 0) + int(wl.hik > 0))
+
+
+def bench_decode_unfused(msa, torch, wls, devs, steps, warmup):
+    """The same decode step through the unfused path: one msa_slots launch, then per layer the main
+    and index norm/RoPE producers and division, remainder, index cast and scatter for each of K, V
+    and index-K, all captured in one HIP graph.  One workspace serves every layer (stream order)."""
+    ws = torch.empty(msa.msa_produce_unfused_workspace_size(wls[0].T, wls[0].hkv, wls[0].hik), dtype=torch.uint8,
+                     device="cuda")
+    slots = devs[0].slots
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+
+    def step():
+        msa.msa_slots(devs[0].positions, devs[0].seq_idx, devs[0].page_table, slots, page_size=wls[0].page_size,
+                      num_pages=wls[0].num_pages)
+        for wl, d in zip(wls, devs):
+            unfused_call(msa, wl, d, slots, ws)
+
+    with torch.cuda.stream(s):
+        step()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.synchronize()
+    launches = 1 + sum(unfused_launches(wl) for wl in wls)
+    log(f"[bench] unfused decode graph captured ({launches} launches); warmup {warmup}, timing {steps} steps")
+    with torch.cuda.stream(s):
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(steps):
+            g.replay()
+        e1.record(s)
+        torch.cuda.synchronize()
+    us_step = e0.elapsed_time(e1) * 1000 / steps
+    return dict(us_per_step=us_step, us_per_layer_call=us_step / len(wls), launches_per_step=launches,
+                steps=steps, warmup=warmup)
+
+
+def bench_prefill(msa, W, torch, iters, warmup, unfused_iters=0):
     log("[bench] staging the 65,536-token prefill chunk (two input sets)")
     sets = [W.config3(variant=v) for v in range(2)]
     devs = [W.to_device(wl) for wl in sets]
@@ -120,6 +180,21 @@ def bench_prefill(msa, W, torch, iters, warmup):
     us = ms * 1000 / iters
     gbs = b / (us * 1e-6) / 1e9
     out = dict(us_per_call=us, bytes=b, gbs=gbs, launches=iters)
+    if unfused_iters:
+        # the same chunk through the unfused path (slots from the fused calls above)
+        ws = torch.empty(msa.msa_produce_unfused_workspace_size(sets[0].T, sets[0].hkv, sets[0].hik),
+                         dtype=torch.uint8, device="cuda")
+        for i in range(10):
+            unfused_call(msa, sets[i % 2], devs[i % 2], devs[i % 2].slots, ws)
+        torch.cuda.synchronize()
+        e0.record(s)
+        for i in range(unfused_iters):
+            unfused_call(msa, sets[i % 2], devs[i % 2], devs[i % 2].slots, ws)
+        e1.record(s)
+        torch.cuda.synchronize()
+        out["unfused_us_per_call"] = e0.elapsed_time(e1) * 1000 / unfused_iters
+        out["unfused_launches_per_call"] = unfused_launches(sets[0])
+        del ws
     del devs
     torch.cuda.empty_cache()
     return out
@@ -216,6 +291,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-indexer", action="store_true", help="skip the indexer measurement")
+    ap.add_argument("--no-unfused", action="store_true", help="skip the unfused-path comparison")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run three plain 1 GiB device-to-device copies (the reference kernel that "
                          "scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
@@ -248,13 +324,16 @@ def main():
     us_call = us_step / args.layers
     launch_us = dec["ms_total"] * 1000 / dec["launches"]
     launch_gbs = dec["bytes_per_call"] / (launch_us * 1e-6) / 1e9
+    unf = None
+    if not args.no_unfused:
+        unf = bench_decode_unfused(msa, torch, dec["wls"], dec["devs"], args.decode_steps, args.decode_warmup)
     del dec["devs"]
     torch.cuda.empty_cache()
 
     import numpy as np
     idx = None if args.no_indexer else bench_indexer(msa, W, torch, np, 50)
     torch.cuda.empty_cache()
-    pre = bench_prefill(msa, W, torch, args.steps, args.warmup)
+    pre = bench_prefill(msa, W, torch, args.steps, args.warmup, 0 if args.no_unfused else 50)
     cpu = None if args.no_cpu_baseline else cpu_baseline(W, args.cpu_seconds)
 
     line = {
@@ -298,6 +377,14 @@ def main():
                 "frac": launch_gbs / HBM_PEAK_GBS, "traffic": counter_traffic("decode_64"),
                 "kernel": "produce_kernel<1, 16, 2, 2, 1> (decode batch 64)", "avg_launch_us": launch_us,
             },
+        },
+        "unfused": None if unf is None else {
+            "path": "msa_slots once per step, then per layer: main and index norm/RoPE producers, and division, "
+                    "remainder, index cast and scatter for each of K, V and index-K (identical output bytes)",
+            "decode": dict(unf, fused_launches_per_step=args.layers, fused_us_per_step=us_step),
+            "prefill": {"us_per_call": pre.get("unfused_us_per_call"),
+                        "launches_per_call": pre.get("unfused_launches_per_call"),
+                        "fused_us_per_call": pre["us_per_call"]},
         },
         "indexer": idx,
         "cpu_baseline": cpu,

@@ -52,7 +52,8 @@ typedef enum msa_status {
     MSA_ERR_ALIGNMENT = 5,      /* a pointer not aligned as documented */
     MSA_ERR_DTYPE = 6,          /* unknown cache dtype, or an fp8 cache without a scale */
     MSA_ERR_OVERFLOW = 7,       /* a cache element offset does not fit in int64 */
-    MSA_ERR_LAUNCH = 8          /* the HIP runtime refused the launch */
+    MSA_ERR_LAUNCH = 8,         /* the HIP runtime refused the launch */
+    MSA_ERR_WORKSPACE = 9       /* a caller-provided workspace is too small or misaligned */
 } msa_status;
 
 typedef enum msa_cache_dtype {

@@ -15,6 +15,11 @@ Entry points (same names as the C ABI):
   msa_index_scores(...) indexer: block max of the exact dot products of index-Q with the visible keys
                         of the index-K cache (include/msa_index.h).
   msa_index_topk(...)   indexer: the top-k blocks of every (index-Q head, token) row.
+  msa_slots(...)        the cache slot of every token (include/msa_unfused.h).
+  msa_produce_unfused(...)  the same outputs as msa_produce through the unfused path: separate
+                        main and index norm/RoPE producers, then division, remainder, index cast
+                        and scatter per cache (14 launches per layer); takes any positive,
+                        non-overlapping cache strides.
 """
 from __future__ import annotations
 
@@ -31,7 +36,7 @@ MSA_CACHE_BF16 = 1
 STATUS = {
     0: "MSA_OK", 1: "MSA_ERR_NULL_POINTER", 2: "MSA_ERR_UNSUPPORTED", 3: "MSA_ERR_SHAPE",
     4: "MSA_ERR_STRIDE", 5: "MSA_ERR_ALIGNMENT", 6: "MSA_ERR_DTYPE", 7: "MSA_ERR_OVERFLOW",
-    8: "MSA_ERR_LAUNCH",
+    8: "MSA_ERR_LAUNCH", 9: "MSA_ERR_WORKSPACE",
 }
 
 
@@ -78,6 +83,14 @@ def lib() -> ctypes.CDLL:
         L.msa_index_scores.restype = ctypes.c_int
         L.msa_index_topk.argtypes = [p, i32, i32, i32, p, p, p]
         L.msa_index_topk.restype = ctypes.c_int
+        u64 = ctypes.c_uint64
+        L.msa_slots.argtypes = [p, p, i32, p, i64, i32, i32, i32, i64, p, p]
+        L.msa_slots.restype = ctypes.c_int
+        L.msa_produce_unfused_workspace_size.argtypes = [i32, i32, i32, ctypes.POINTER(u64)]
+        L.msa_produce_unfused_workspace_size.restype = ctypes.c_int
+        L.msa_produce_unfused.argtypes = [p, i64, i32, i32, i32, i32, i32, i32, p, p, i32, i64,
+                                          p, p, p, p, f32, f64, p, p, cv, cv, cv, p, u64, p]
+        L.msa_produce_unfused.restype = ctypes.c_int
         L.msa_status_string.argtypes = [ctypes.c_int]
         L.msa_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -195,3 +208,49 @@ def msa_index_topk(block_scores, block_ids, counts=None, stream=None) -> None:
                               _stream(stream))
     if st != 0:
         raise MsaError(st, "msa_index_topk")
+
+
+def msa_slots(positions, seq_idx, page_table, slots_out, *, page_size: int, num_pages: int, stream=None) -> None:
+    """slots_out[t] = page_table[seq][pos // page_size] * page_size + pos % page_size, or -1."""
+    st = lib().msa_slots(_ptr(positions), _ptr(seq_idx), positions.numel(), _ptr(page_table), page_table.stride(0),
+                         page_table.shape[0], page_table.shape[1], int(page_size), int(num_pages), _ptr(slots_out),
+                         _stream(stream))
+    if st != 0:
+        raise MsaError(st, "msa_slots")
+
+
+def msa_produce_unfused_workspace_size(num_tokens: int, num_kv_heads: int, num_ik_heads: int) -> int:
+    n = ctypes.c_uint64(0)
+    st = lib().msa_produce_unfused_workspace_size(int(num_tokens), int(num_kv_heads), int(num_ik_heads),
+                                                  ctypes.byref(n))
+    if st != 0:
+        raise MsaError(st, "msa_produce_unfused_workspace_size")
+    return n.value
+
+
+def msa_produce_unfused(x, positions, slots, q_norm_weight, k_norm_weight, iq_norm_weight, ik_norm_weight,
+                        q_out, iq_out, k_cache, v_cache, ik_cache=None, *, workspace, k_scale=None, v_scale=None,
+                        ik_scale=None, num_pages: Optional[int] = None, rms_eps: float = 1e-6,
+                        rope_theta: float = 1e4, stream=None) -> None:
+    """msa_produce's outputs through the unfused path.  slots int64 [T] (msa_slots); workspace a
+    device byte tensor of at least msa_produce_unfused_workspace_size bytes, 256-byte aligned."""
+    T = x.shape[0]
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    hq, hiq = q_out.shape[1], iq_out.shape[1]
+    hkv = k_cache.shape[1] if k_cache is not None else 0
+    hik = ik_cache.shape[1] if ik_cache is not None else 0
+    ref = k_cache if k_cache is not None else ik_cache
+    pages = ref.shape[0] if num_pages is None else num_pages
+    kv = cache_view(k_cache, k_scale)
+    vv = cache_view(v_cache, v_scale)
+    iv = cache_view(ik_cache, ik_scale)
+    st = lib().msa_produce_unfused(
+        _ptr(x), x.stride(0), T, 128, hq, hkv, hiq, hik, _ptr(positions), _ptr(slots), ref.shape[2], pages,
+        _ptr(q_norm_weight), _ptr(k_norm_weight), _ptr(iq_norm_weight), _ptr(ik_norm_weight),
+        float(rms_eps), float(rope_theta), _ptr(q_out), _ptr(iq_out),
+        None if kv is None else ctypes.byref(kv), None if vv is None else ctypes.byref(vv),
+        None if iv is None else ctypes.byref(iv), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    if st != 0:
+        raise MsaError(st, "msa_produce_unfused")

@@ -1,9 +1,10 @@
-// Host-side pieces shared by the producer and the indexer sources: the device form of a cache view
-// and its validation.  Internal to the library (not part of the C ABI).
+// Host-side pieces shared by the library sources: the device form of a cache view, its validation
+// and the RoPE inverse frequencies.  Internal to the library (not part of the C ABI).
 #pragma once
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 
@@ -26,8 +27,11 @@ struct CacheDev {
 inline bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
 // Validates a cache view of `heads` heads over `num_pages` pages of `page_size` tokens and fills its
-// device form.  heads == 0: nothing to check, the descriptor may be NULL.
-inline msa_status check_cache(const msa_cache_view* v, int32_t heads, int32_t page_size, int64_t num_pages, CacheDev* out)
+// device form.  heads == 0: nothing to check, the descriptor may be NULL.  `vec`: the fused
+// producer's layout (16-byte aligned base, strides multiples of 8 elements); otherwise any positive
+// strides and a base aligned to the element size.
+inline msa_status check_cache(const msa_cache_view* v, int32_t heads, int32_t page_size, int64_t num_pages, CacheDev* out,
+                              bool vec = true)
 {
     std::memset(out, 0, sizeof(*out));
     if (heads == 0) return MSA_OK;
@@ -35,11 +39,11 @@ inline msa_status check_cache(const msa_cache_view* v, int32_t heads, int32_t pa
     if (v->num_heads != heads) return MSA_ERR_SHAPE;
     if (v->dtype != MSA_CACHE_FP8_E4M3 && v->dtype != MSA_CACHE_BF16) return MSA_ERR_DTYPE;
     if (v->dtype == MSA_CACHE_FP8_E4M3 && !v->scale) return MSA_ERR_DTYPE;
-    if (!aligned(v->data, 16)) return MSA_ERR_ALIGNMENT;
+    if (!aligned(v->data, vec ? 16 : v->dtype == MSA_CACHE_BF16 ? 2 : 1)) return MSA_ERR_ALIGNMENT;
     if (v->dtype == MSA_CACHE_FP8_E4M3 && !aligned(v->scale, 4)) return MSA_ERR_ALIGNMENT;
     const int64_t s[3] = {v->stride_page, v->stride_head, v->stride_token};
     for (int i = 0; i < 3; ++i)
-        if (s[i] <= 0 || s[i] % 8) return MSA_ERR_STRIDE;
+        if (s[i] <= 0 || (vec && s[i] % 8)) return MSA_ERR_STRIDE;
     // Non-overlap: with the dims ordered by stride, each stride must exceed the largest offset
     // the smaller dims can reach.  The walk also yields the largest element offset of the view.
     int64_t ord_s[4] = {1, s[2], s[1], s[0]};
@@ -68,6 +72,19 @@ inline msa_status check_cache(const msa_cache_view* v, int32_t heads, int32_t pa
     out->heads = heads;
     out->is_bf16 = v->dtype == MSA_CACHE_BF16;
     return MSA_OK;
+}
+
+// inv_freq_i = 1 / theta^(2i/D) in binary64 (one rounding each for the exponent, pow and the
+// division), memoised per host thread for the last theta.
+inline void fill_inv_freq(double theta, double* out)
+{
+    thread_local double last_theta = 0.0;
+    thread_local double table[kHeadDim / 2];
+    if (theta != last_theta) {
+        for (int i = 0; i < kHeadDim / 2; ++i) table[i] = 1.0 / std::pow(theta, (double)(2 * i) / (double)kHeadDim);
+        last_theta = theta;
+    }
+    std::memcpy(out, table, sizeof(table));
 }
 
 }  // namespace msa_internal

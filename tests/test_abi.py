@@ -1,5 +1,5 @@
 """C-ABI checks that need no GPU: the library loads, exports every entry point that
-include/msa_produce.h declares, and rejects invalid arguments on the host before any launch
+the headers under include/ declare, and rejects invalid arguments on the host before any launch
 (so no call here reaches the device; every pointer below is a never-dereferenced address)."""
 import ctypes
 import os
@@ -14,7 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADERS = [os.path.join(ROOT, "include", n) for n in sorted(os.listdir(os.path.join(ROOT, "include")))
            if n.endswith(".h")]
 
-OK, NULLP, UNSUP, SHAPE, STRIDE, ALIGN, DTYPE, OVERFLOW = 0, 1, 2, 3, 4, 5, 6, 7
+OK, NULLP, UNSUP, SHAPE, STRIDE, ALIGN, DTYPE, OVERFLOW, LAUNCH, WORKSPACE = range(10)
 
 
 @pytest.fixture(scope="module")
@@ -35,13 +35,14 @@ def declared_functions():
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert set(names) >= {"msa_produce", "msa_rope_table", "msa_quantize", "msa_rms_scale", "msa_status_string",
-                          "msa_index_scores", "msa_index_topk"}
+                          "msa_index_scores", "msa_index_topk", "msa_slots", "msa_produce_unfused",
+                          "msa_produce_unfused_workspace_size"}
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_status_strings(L):
-    for code in range(9):
+    for code in range(10):
         assert msa.string(code) and msa.string(code) != "unknown status"
     assert msa.string(99) == "unknown status"
 
@@ -178,3 +179,69 @@ def test_index_entry_points_validate(L):
     assert L.msa_index_topk(SLOTS, 10, 5000, 16, Q, None, None) == SHAPE
     assert L.msa_index_topk(SLOTS + 4, 10, 72, 16, Q, None, None) == ALIGN
     assert L.msa_index_topk(SLOTS, 0, 72, 16, Q, None, None) == OK
+
+
+# ------------------------------------------------------------------ unfused path
+
+WS = 0x200000
+
+
+def call_unfused(L, **kw):
+    a = dict(x=X, xs=2944, T=0, D=128, hq=16, hkv=2, hiq=2, hik=1, pos=POS, slots=SLOTS, P=64, pages=10240,
+             wq=W, wk=W, wiq=W, wik=W, eps=1e-6, theta=1e4, q=Q, iq=IQ, k=view(), v=view(),
+             ik=view(sp=64 * 128, heads=1), ws=WS, wsb=1 << 30, stream=None)
+    a.update(kw)
+    ref = lambda v: None if v is None else ctypes.byref(v)
+    return L.msa_produce_unfused(a["x"], a["xs"], a["T"], a["D"], a["hq"], a["hkv"], a["hiq"], a["hik"], a["pos"],
+                                 a["slots"], a["P"], a["pages"], a["wq"], a["wk"], a["wiq"], a["wik"], a["eps"],
+                                 a["theta"], a["q"], a["iq"], ref(a["k"]), ref(a["v"]), ref(a["ik"]), a["ws"],
+                                 a["wsb"], a["stream"])
+
+
+def test_unfused_workspace_size(L):
+    n = ctypes.c_uint64(0)
+    assert L.msa_produce_unfused_workspace_size(64, 2, 1, ctypes.byref(n)) == OK
+    # binary32 K (64 x 2 x 128) and index-K (64 x 1 x 128) rows, nine int64 [64] arrays, 256-B regions
+    assert n.value == 64 * 2 * 128 * 4 + 64 * 1 * 128 * 4 + 9 * 512
+    assert L.msa_produce_unfused_workspace_size(0, 2, 1, ctypes.byref(n)) == OK and n.value == 0
+    assert L.msa_produce_unfused_workspace_size(-1, 2, 1, ctypes.byref(n)) == SHAPE
+    assert L.msa_produce_unfused_workspace_size(1, 2, 1, None) == NULLP
+
+
+@pytest.mark.parametrize("layout", [
+    dict(st=132, sh=64 * 132, sp=2 * 64 * 132),     # token stride not a multiple of 8 elements
+    dict(sp=2 * 65 * 128 + 1, sh=65 * 128 + 3),     # odd page and head strides
+    dict(data=DATA + 1),                            # fp8 base aligned to its 1-byte element only
+])
+def test_unfused_takes_layouts_the_fused_kernel_rejects(L, layout):
+    k = view(**layout)
+    assert call(L, k=k) in (STRIDE, ALIGN)
+    assert call_unfused(L, k=k) == OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=64), UNSUP),
+    (dict(T=-1), SHAPE),
+    (dict(P=0), SHAPE),
+    (dict(xs=2948), STRIDE),
+    (dict(k=view(st=64)), STRIDE),                  # overlapping rows are still rejected
+    (dict(k=view(data=DATA + 1, dtype=1, scale=None)), ALIGN),   # bf16 base must be 2-byte aligned
+    (dict(k=view(scale=None)), DTYPE),
+    (dict(wk=None), NULLP),
+    (dict(T=64, slots=None), NULLP),
+    (dict(T=64, ws=None), WORKSPACE),
+    (dict(T=64, ws=WS + 64), WORKSPACE),
+    (dict(T=64, wsb=1000), WORKSPACE),
+    (dict(pages=1 << 50), OVERFLOW),
+])
+def test_unfused_rejects_invalid_arguments(L, kw, status):
+    assert call_unfused(L, **kw) == status
+
+
+def test_slots_entry_point_validates(L):
+    assert L.msa_slots(POS, SEQ, 0, PT, 160, 64, 160, 64, 10240, SLOTS, None) == OK
+    assert L.msa_slots(POS, SEQ, -1, PT, 160, 64, 160, 64, 10240, SLOTS, None) == SHAPE
+    assert L.msa_slots(POS, SEQ, 4, PT, 100, 64, 160, 64, 10240, SLOTS, None) == STRIDE
+    assert L.msa_slots(POS, SEQ, 4, PT, 160, 64, 160, 0, 10240, SLOTS, None) == SHAPE
+    assert L.msa_slots(POS, SEQ, 4, PT, 160, 64, 160, 64, 10240, None, None) == NULLP
+    assert L.msa_slots(POS, SEQ, 4, PT, 160, 64, 160, 64, 10240, SLOTS + 4, None) == ALIGN
