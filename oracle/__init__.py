@@ -4,8 +4,9 @@ TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the CPU-baseline
 leg of the benchmark may use this package; the product path never does.
 
 The oracle follows the AFTER figure and change list of the page "Fuse MiniMax-M3
-QKV and index projection" (per-head Q/K RMSNorm + neox RoPE on Q, K, index-Q and
-index-K, compact Q/index-Q, paged HND cache writes with invalid slots skipped),
+QKV and index projection" (the packed projection of the hidden states, per-head
+Q/K RMSNorm + neox RoPE on Q, K, index-Q and index-K, compact Q/index-Q, paged
+HND cache writes with invalid slots skipped),
 and the slot rule page = slot / page_size, offset = slot % page_size of "Fuse
 MiniMax-M3 MSA per-layer KV-cache writes into one kernel" ("The problem").
 
@@ -77,6 +78,10 @@ def lib() -> ctypes.CDLL:
         L.msa_oracle_index_scores.restype = ctypes.c_int
         L.msa_oracle_index_topk.argtypes = [p, i32, i64, i32, i32, p, p]
         L.msa_oracle_index_topk.restype = ctypes.c_int
+        L.msa_oracle_bf16_of_f64.argtypes = [f64]
+        L.msa_oracle_bf16_of_f64.restype = ctypes.c_uint16
+        L.msa_oracle_project.argtypes = [p, i64, i64, i64, p, i64, i64, p, i64, p, p, i32]
+        L.msa_oracle_project.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -233,3 +238,28 @@ def index_topk(block_scores, top_k):
     if rc != 0:
         raise OracleError(f"msa_oracle_index_topk returned {rc}")
     return ids, counts
+
+
+def bf16_of_f64(v: float) -> int:
+    """One binary64 value rounded once to bf16 (bits)."""
+    return int(lib().msa_oracle_bf16_of_f64(float(v)))
+
+
+def project(h, w, num_threads: int = 1, want_sums: bool = False):
+    """x = bf16(h @ w.T) with a binary64 ascending-k sum per element (msa_oracle_project).
+    h: uint16 bf16 bits [T, K]; w: uint16 bf16 bits [N, K].  Returns x (uint16 [T, N]) or, with
+    want_sums, (x, sum, abs_sum) where sum is the binary64 sum and abs_sum = sum_k |h w|."""
+    h = _c(h, np.uint16)
+    w = _c(w, np.uint16)
+    T, K = h.shape
+    N, K2 = w.shape
+    if K2 != K:
+        raise OracleError("h and w disagree on K")
+    x = np.empty((T, N), np.uint16)
+    sm = np.empty((T, N), np.float64) if want_sums else None
+    ab = np.empty((T, N), np.float64) if want_sums else None
+    rc = lib().msa_oracle_project(_ptr(h), K, T, K, _ptr(w), K, N, _ptr(x), N, _ptr(sm), _ptr(ab),
+                                  int(num_threads))
+    if rc != 0:
+        raise OracleError(f"msa_oracle_project returned {rc}")
+    return (x, sm, ab) if want_sums else x

@@ -108,6 +108,28 @@ uint8_t msa_oracle_e4m3(float v)
     return (uint8_t)(sign | (uint8_t)(exp_field << 3) | (uint8_t)frac);
 }
 
+/*
+ * binary64 -> bf16 in one rounding (round to nearest, ties to even, overflow
+ * to infinity), on the same per-binade grid as above.  Rounding a binary64 sum
+ * through binary32 first would round twice; this does not.  NaN -> the quiet
+ * NaN 0x7fc0 with the sign.
+ */
+uint16_t msa_oracle_bf16_of_f64(double d)
+{
+    uint16_t sign = signbit(d) ? 0x8000u : 0x0000u;
+    if (isnan(d)) return (uint16_t)(sign | 0x7fc0u);
+    if (isinf(d)) return (uint16_t)(sign | 0x7f80u);
+    if (d == 0.0) return sign;
+    int e;
+    frexp(fabs(d), &e);
+    int qexp = e - 8;
+    if (qexp < -133) qexp = -133;
+    double r = ldexp(nearbyint(ldexp(d, -qexp)), qexp);   /* scalings exact; nearbyint is RNE */
+    if (fabs(r) >= ldexp(1.0, 128)) return (uint16_t)(sign | 0x7f80u);
+    if (r == 0.0) return sign;
+    return (uint16_t)(bits_of_f32((float)r) >> 16);       /* r has <= 8 significant bits: exact */
+}
+
 void msa_oracle_encode_bf16(const float* v, int64_t n, uint16_t* out)
 {
     for (int64_t i = 0; i < n; ++i) out[i] = msa_oracle_bf16(v[i]);
@@ -467,6 +489,46 @@ int msa_oracle_index_topk(const double* block_scores, int32_t hiq, int64_t T, in
         }
         for (int32_t k = n; k < top_k; ++k) out[k] = -1;
         if (counts) counts[r] = n;
+    }
+    return ORC_OK;
+}
+
+/*
+ * The packed projection that feeds the producer (page "Fuse MiniMax-M3 QKV and
+ * index projection", AFTER figure: one wider GEMM produces the row
+ * [Q | K | V | index-Q | index-K] from the hidden states):
+ *
+ *   x[t, c] = bf16( sum_k h[t, k] * w[c, k] )      t < T, c < N, k < K
+ *
+ * h is bf16 [T, K] (row stride h_stride), w is bf16 [N, K] (one row per output
+ * column, row stride w_stride), x is bf16 [T, N] (row stride x_stride).  Each
+ * product of two bf16 values is exact in binary64; the sum runs in binary64 in
+ * ascending k and is rounded once to bf16.  Optional outputs: the binary64 sum
+ * itself and sum_k |h[t, k] * w[c, k]| (both [T, N] dense), from which a test
+ * bounds what a binary32 accumulation in any order can reach.
+ */
+int msa_oracle_project(const uint16_t* h, int64_t h_stride, int64_t T, int64_t K,
+                       const uint16_t* w, int64_t w_stride, int64_t N,
+                       uint16_t* x_out, int64_t x_stride, double* sum_out, double* abs_out,
+                       int32_t num_threads)
+{
+    if (T < 0 || K < 0 || N < 0 || h_stride < K || w_stride < K || x_stride < N) return ORC_ERR_ARG;
+    if (num_threads < 1) num_threads = 1;
+    #pragma omp parallel for num_threads(num_threads) schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        const uint16_t* hr = h + t * h_stride;
+        for (int64_t c = 0; c < N; ++c) {
+            const uint16_t* wr = w + c * w_stride;
+            double acc = 0.0, mag = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double p = (double)bf16_value(hr[k]) * (double)bf16_value(wr[k]);
+                acc += p;
+                mag += fabs(p);
+            }
+            x_out[t * x_stride + c] = msa_oracle_bf16_of_f64(acc);
+            if (sum_out) sum_out[t * N + c] = acc;
+            if (abs_out) abs_out[t * N + c] = mag;
+        }
     }
     return ORC_OK;
 }
