@@ -1,0 +1,107 @@
+/*
+ * msa_project.h — C ABI of the packed projection for AMD Instinct MI355X (gfx950), alone and with
+ * the producer fused into its epilogue.
+ *
+ * The projection (page "Fuse MiniMax-M3 QKV and index projection", AFTER figure: one wider GEMM of
+ * the hidden states produces the packed row [Q | K | V | index-Q | index-K]):
+ *
+ *   x[t, c] = bf16( sum_k h[t, k] * w[c, k] )
+ *
+ * h: bf16 hidden states [T, K]; w: bf16 packed weight [N, K] (one row per output column, the
+ * layout of a linear layer's weight); x: bf16 [T, N].  The sum runs on the matrix cores (bf16
+ * products, binary32 accumulation) in an order fixed by the kernel: the same inputs always give
+ * the same bits, but not the bits of an exact sum.  For any accumulation order the binary32 sum
+ * lies within K * 2^-24 / (1 - K * 2^-24) * sum_k |h[t, k] w[c, k]| of the exact one, before the
+ * final rounding to bf16.
+ *
+ * msa_project_produce runs the same GEMM (same kernel, same accumulation order) and, instead of
+ * storing x, hands each head's bf16-rounded row to the producer's arithmetic (msa_produce.h):
+ * per-head RMSNorm + neox RoPE on Q, K, index-Q and index-K, compact Q and index-Q, and K, V,
+ * index-K into the paged caches.  Its outputs equal msa_produce applied to msa_project's x, except
+ * where a head's binary64 sum of squares is inexact (a head spanning more than about 2^15 in
+ * magnitude), where the two sum orders may differ in the last binary64 bit.  The packed row never
+ * touches memory.  The pages fuse only up to "one wider GEMM" feeding "one fused producer"; this
+ * entry point goes one step further.
+ *
+ * Kernels: a split-K kernel for up to 1,024 tokens (the decode and verify batches: heads x token
+ * chunks x K slices, partial sums in the workspace, the last slice of each (head, chunk) reduces
+ * them in a fixed order and runs the epilogue), and a 256 x 256 tiled kernel for larger batches
+ * (prefill), both on v_mfma_f32_32x32x16_bf16.
+ *
+ * Conventions are those of msa_produce.h (device pointers unchecked for residency, no allocation,
+ * no synchronisation, all checks on the host before any launch, MSA_OK means enqueued,
+ * graph-capture safe), plus the workspace rule below.
+ */
+#ifndef MSA_PROJECT_H
+#define MSA_PROJECT_H
+
+#include <stdint.h>
+
+#include "msa_produce.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * msa_project_workspace_size — bytes of workspace a projection of num_tokens rows of width hidden
+ * onto num_heads heads of 128 columns needs (both entry points take the same).  Zero for batches
+ * above 1,024 tokens.
+ *
+ * Workspace rule: the workspace (device memory, 256-byte aligned) must be zero-filled before its
+ * first use by either entry point; every call leaves the bytes it uses as counters at zero again,
+ * so one zero-fill serves any number of calls.  Calls that share a workspace must not overlap in
+ * time (same stream, or ordered).
+ */
+msa_status msa_project_workspace_size(int32_t num_tokens, int32_t hidden, int32_t num_heads, uint64_t* bytes);
+
+/*
+ * msa_project — the packed projection alone.
+ *
+ * h            device bf16 [T, hidden], row stride h_row_stride (>= hidden, multiple of 8), 16-B aligned.
+ * num_tokens   T >= 0 (0: nothing launched).
+ * hidden       K: a positive multiple of 64.
+ * w            device bf16 [num_cols, hidden], row stride w_row_stride (>= hidden, multiple of 8), 16-B aligned.
+ * num_cols     N: a positive multiple of 128, at most 4096 * 128.
+ * x_out        device bf16 [T, num_cols], row stride x_row_stride (>= num_cols, multiple of 8), 16-B aligned.
+ * workspace    see the workspace rule; may be NULL when msa_project_workspace_size gives 0.
+ */
+msa_status msa_project(const uint16_t* h, int64_t h_row_stride, int32_t num_tokens, int32_t hidden,
+                       const uint16_t* w, int64_t w_row_stride, int32_t num_cols,
+                       uint16_t* x_out, int64_t x_row_stride,
+                       void* workspace, uint64_t workspace_bytes, void* stream);
+
+/*
+ * msa_project_produce — the projection with the producer as its epilogue.
+ *
+ * h, h_row_stride, num_tokens, hidden, w, w_row_stride   as in msa_project; w has
+ *              (num_q_heads + 2 num_kv_heads + num_iq_heads + num_ik_heads) * head_dim rows in the
+ *              packed order Q, K, V, index-Q, index-K.
+ * head_dim, num_*_heads, *_norm_weight, rms_eps, q_out, iq_out, k_cache, v_cache, ik_cache
+ *              as in msa_produce (same requirements).
+ * rope_cos, rope_sin   device float [T, head_dim / 2], 16-B aligned: the RoPE coefficients of each
+ *              token, as msa_rope_table computes them from the positions (once per step; every
+ *              layer of the step reads the same table).
+ * slots        device int64 [T], 8-B aligned: the cache slot of each token (msa_slots, or
+ *              msa_produce's slots_out); < 0, or a page outside [0, num_pages): no cache write.
+ *              Valid slots must be distinct.
+ * page_size    > 0; num_pages >= 0.
+ * workspace    see the workspace rule.
+ */
+msa_status msa_project_produce(const uint16_t* h, int64_t h_row_stride, int32_t num_tokens, int32_t hidden,
+                               const uint16_t* w, int64_t w_row_stride, int32_t head_dim,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t num_iq_heads,
+                               int32_t num_ik_heads, const float* rope_cos, const float* rope_sin,
+                               const int64_t* slots, int32_t page_size, int64_t num_pages,
+                               const uint16_t* q_norm_weight, const uint16_t* k_norm_weight,
+                               const uint16_t* iq_norm_weight, const uint16_t* ik_norm_weight,
+                               float rms_eps, uint16_t* q_out, uint16_t* iq_out,
+                               const msa_cache_view* k_cache, const msa_cache_view* v_cache,
+                               const msa_cache_view* ik_cache,
+                               void* workspace, uint64_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_PROJECT_H */

@@ -15,6 +15,9 @@ Entry points (same names as the C ABI):
   msa_index_scores(...) indexer: block max of the exact dot products of index-Q with the visible keys
                         of the index-K cache (include/msa_index.h).
   msa_index_topk(...)   indexer: the top-k blocks of every (index-Q head, token) row.
+  msa_project(...)      the packed projection x = bf16(h w^T) on the matrix cores (include/msa_project.h).
+  msa_project_produce(...)  the same projection with the producer as its epilogue: the packed row
+                        never touches memory.
   msa_slots(...)        the cache slot of every token (include/msa_unfused.h).
   msa_produce_unfused(...)  the same outputs as msa_produce through the unfused path: separate
                         main and index norm/RoPE producers, then division, remainder, index cast
@@ -91,6 +94,13 @@ def lib() -> ctypes.CDLL:
         L.msa_produce_unfused.argtypes = [p, i64, i32, i32, i32, i32, i32, i32, p, p, i32, i64,
                                           p, p, p, p, f32, f64, p, p, cv, cv, cv, p, u64, p]
         L.msa_produce_unfused.restype = ctypes.c_int
+        L.msa_project_workspace_size.argtypes = [i32, i32, i32, ctypes.POINTER(u64)]
+        L.msa_project_workspace_size.restype = ctypes.c_int
+        L.msa_project.argtypes = [p, i64, i32, i32, p, i64, i32, p, i64, p, u64, p]
+        L.msa_project.restype = ctypes.c_int
+        L.msa_project_produce.argtypes = [p, i64, i32, i32, p, i64, i32, i32, i32, i32, i32, p, p, p, i32, i64,
+                                          p, p, p, p, f32, p, p, cv, cv, cv, p, u64, p]
+        L.msa_project_produce.restype = ctypes.c_int
         L.msa_status_string.argtypes = [ctypes.c_int]
         L.msa_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -254,3 +264,59 @@ def msa_produce_unfused(x, positions, slots, q_norm_weight, k_norm_weight, iq_no
         _stream(stream))
     if st != 0:
         raise MsaError(st, "msa_produce_unfused")
+
+
+def msa_project_workspace_size(num_tokens: int, hidden: int, num_heads: int) -> int:
+    """Bytes of (zero-filled, 256-byte aligned) workspace the projection needs; 0 above 1,024 tokens."""
+    n = ctypes.c_uint64(0)
+    st = lib().msa_project_workspace_size(int(num_tokens), int(hidden), int(num_heads), ctypes.byref(n))
+    if st != 0:
+        raise MsaError(st, "msa_project_workspace_size")
+    return n.value
+
+
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def msa_project(h, w, x_out, *, workspace=None, stream=None) -> None:
+    """x_out[T, N] = bf16(h[T, K] @ w[N, K]^T); row strides taken from the tensors (unit column stride)."""
+    for name, t in (("h", h), ("w", w), ("x_out", x_out)):
+        if t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError(f"{name} must be 2-D with unit column stride")
+    wp, wb = _ws(workspace)
+    st = lib().msa_project(_ptr(h), h.stride(0), h.shape[0], h.shape[1], _ptr(w), w.stride(0), w.shape[0],
+                           _ptr(x_out), x_out.stride(0), wp, wb, _stream(stream))
+    if st != 0:
+        raise MsaError(st, "msa_project")
+
+
+def msa_project_produce(h, w, rope_cos, rope_sin, slots, q_norm_weight, k_norm_weight, iq_norm_weight,
+                        ik_norm_weight, q_out, iq_out, k_cache, v_cache, ik_cache=None, *, workspace=None,
+                        k_scale=None, v_scale=None, ik_scale=None, num_pages: Optional[int] = None,
+                        rms_eps: float = 1e-6, stream=None) -> None:
+    """The projection with the producer as its epilogue.  h [T, K] bf16; w [W, K] bf16 (packed rows Q,
+    K, V, index-Q, index-K); rope_cos / rope_sin float32 [T, 64] (msa_rope_table); slots int64 [T]
+    (msa_slots); the rest as in msa_produce.  Head counts come from q_out, iq_out and the caches."""
+    for name, t in (("h", h), ("w", w)):
+        if t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError(f"{name} must be 2-D with unit column stride")
+    hq, hiq = q_out.shape[1], iq_out.shape[1]
+    hkv = k_cache.shape[1] if k_cache is not None else 0
+    hik = ik_cache.shape[1] if ik_cache is not None else 0
+    ref = k_cache if k_cache is not None else ik_cache
+    pages = ref.shape[0] if num_pages is None else num_pages
+    kv = cache_view(k_cache, k_scale)
+    vv = cache_view(v_cache, v_scale)
+    iv = cache_view(ik_cache, ik_scale)
+    wp, wb = _ws(workspace)
+    st = lib().msa_project_produce(
+        _ptr(h), h.stride(0), h.shape[0], h.shape[1], _ptr(w), w.stride(0), 128, hq, hkv, hiq, hik,
+        _ptr(rope_cos), _ptr(rope_sin), _ptr(slots), ref.shape[2], pages,
+        _ptr(q_norm_weight), _ptr(k_norm_weight), _ptr(iq_norm_weight), _ptr(ik_norm_weight), float(rms_eps),
+        _ptr(q_out), _ptr(iq_out), None if kv is None else ctypes.byref(kv), None if vv is None else ctypes.byref(vv),
+        None if iv is None else ctypes.byref(iv), wp, wb, _stream(stream))
+    if st != 0:
+        raise MsaError(st, "msa_project_produce")

@@ -6,7 +6,7 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", n) for n in ("msa_produce.hip", "msa_index.hip", "msa_unfused.hip")]
+SRCS = [os.path.join(PKG, "csrc", n) for n in ("msa_produce.hip", "msa_index.hip", "msa_unfused.hip", "msa_project.hip")]
 LIB = os.path.join(PKG, "libmsa_produce.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -401,3 +401,33 @@ def index_queries(T: int, hiq: int, seed: int = 98) -> np.ndarray:
 def index_blocks(wl: Workload, block_tokens: int = 128) -> int:
     """Row length of the block-score table: enough blocks for the largest position."""
     return int(wl.positions.max()) // block_tokens + 1 if wl.T else 0
+
+
+# ------------------------------------------------------------------ projection inputs
+
+PROJECTION_HIDDEN = 3072   # hidden size of the projection workloads (the pages do not state one)
+
+
+def projection_inputs(T: int, hidden: int = PROJECTION_HIDDEN, n_cols: int = 2944, seed: int = 0,
+                      dyadic: bool = False):
+    """Hidden states h [T, hidden] and a packed projection weight w [n_cols, hidden], bf16 bits.
+
+    Default: h ~ N(0, 1) and w ~ N(0, 1/hidden), so the packed row x = h w^T is about N(0, 1) like
+    the producer workloads' rows.  dyadic=True draws h from {k/16 : |k| <= 64} and w from
+    {k/64 : |k| <= 32}: every product is a multiple of 2^-10 and every partial sum stays below
+    2^14 in magnitude for hidden <= 8192, so a binary32 accumulation in any order is exact and the
+    projection has one correct answer bit for bit."""
+    rng = np.random.Generator(np.random.PCG64([seed, 4242]))
+    if dyadic:
+        h = rng.integers(-64, 65, (T, hidden)).astype(np.float32) / np.float32(16)
+        w = rng.integers(-32, 33, (n_cols, hidden)).astype(np.float32) / np.float32(64)
+    else:
+        h = rng.standard_normal((T, hidden), dtype=np.float32)
+        w = rng.standard_normal((n_cols, hidden), dtype=np.float32) * np.float32(1.0 / np.sqrt(hidden))
+    return to_bf16_bits(h), to_bf16_bits(w)
+
+
+def with_projection(wl: Workload, hidden: int = PROJECTION_HIDDEN, seed: int = 0, dyadic: bool = False):
+    """(h, w) for a producer workload: the packed row of wl becomes bf16(h w^T); wl.x is left as is
+    (the caller replaces it with the oracle's projection where a row is needed)."""
+    return projection_inputs(wl.T, hidden, wl.W, seed=seed, dyadic=dyadic)
