@@ -38,14 +38,19 @@ using namespace msa_internal;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kSplitMaxTokens = 1024;
 constexpr int kChunk = 64;                 // tokens per split-K work-group (two MFMA token blocks)
-constexpr int kPartFloats = 4 * 2 * 64 * 16;   // one work-group's partial sums: [wave][tb][lane][16]
+constexpr int kPartFloats = 4 * 2 * 4 * 64 * 4;   // one work-group's partial sums: [wave][tb][q][lane][4]
+constexpr int kRawBufferFormat = 0x00020000;   // buffer descriptor word 3: 32-bit elements
+constexpr int kAgentCoherent = 16;             // buffer cache policy: sc1 (agent-scope coherent)
 constexpr int kTile = 256;                 // tiled kernel: features and tokens per work-group
 constexpr int kBK = 64;                    // K per pipeline stage
 constexpr int kPitch = 72;                 // LDS row pitch in bf16 elements (144 B)
 constexpr uint64_t kAlign = 256;
+constexpr int kSliceMax = 384;             // split-K: K per slice at most (LDS: (128 + 64) rows x 384 bf16)
+constexpr int kSplitLds = (128 + kChunk) * kSliceMax * 2;
 
 enum Stream { kQ = 0, kK = 1, kV = 2, kIQ = 3, kIK = 4 };
 
@@ -196,106 +201,169 @@ struct SplitArgs {
     Epi e;
 };
 
-template <bool kProduce>
-__global__ __launch_bounds__(256) void project_splitk_kernel(const SplitArgs a)
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS image of a K slice: 64-column planes (one per 64 columns of the slice), each holding every
+// row's 128 bytes as 8 chunks of 16 bytes, chunk c of row r at position c ^ (r & 7): the 8 rows read
+// by 8 consecutive lanes at one chunk fall in 8 different bank groups.
+__device__ __forceinline__ int plane_slot(int rows, int plane, int row, int chunk)
 {
+    return (plane * rows + row) * 8 + (chunk ^ (row & 7));
+}
+
+// Moves plane g (64 columns) of rows [0, rows) of a K slice (row r at src_row(r)) into LDS at `dst`
+// with the direct global -> LDS path: each lane of each wave fills one 16-byte slot per instruction
+// (64 consecutive slots per wave).  rows is 64 or 128: rows / 32 instructions per wave.
+template <typename RowPtr>
+__device__ __forceinline__ void plane_to_lds(uint8_t* dst, int rows, int g, RowPtr src_row)
+{
+    const int tid = threadIdx.x, wave = tid >> 6;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (j * 256 >= rows * 8) break;
+        const int p = j * 256 + tid;                               // slot within the plane
+        const int row = p >> 3;
+        const int chunk = (p & 7) ^ (row & 7);                     // logical chunk stored at this slot
+        const uint16_t* gsrc = src_row(row) + g * 64 + chunk * 8;
+        uint8_t* l = dst + ((size_t)(g * rows * 8 + j * 256 + wave * 64)) * 16;
+        __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)l, 16, 0, 0);
+    }
+}
+
+template <bool kProduce>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void project_splitk_kernel(const SplitArgs a)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kSplitLds];
     __shared__ int s_last;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // 32-feature block of the head
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);       // 32-feature block of the head
     const int hh = lane >> 5;
     const int split = (int)(blockIdx.x % (uint32_t)a.splits);
     const int pair = (int)(blockIdx.x / (uint32_t)a.splits);         // head * n_tc + chunk
     const int tc = pair % a.n_tc;
     const int head = pair / a.n_tc;
     const int k_begin = split * a.kc;
-    const int k_end = min(a.K, k_begin + a.kc);
+    const int planes = (min(a.K, k_begin + a.kc) - k_begin) / kBK;
 
-    const uint16_t* ap = a.w + (int64_t)(head * kHeadDim + wave * 32 + (lane & 31)) * a.w_stride + 8 * hh;
-    const int32_t t0 = min(tc * kChunk + (lane & 31), a.e.T - 1);           // rows past T: read row T-1, unused
-    const int32_t t1 = min(tc * kChunk + 32 + (lane & 31), a.e.T - 1);
-    const uint16_t* bp0 = a.h + (int64_t)t0 * a.h_stride + 8 * hh;
-    const uint16_t* bp1 = a.h + (int64_t)t1 * a.h_stride + 8 * hh;
-
-    f32x16_t c0 = {}, c1 = {};
-    uint4 av[4], b0[4], b1[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        av[s] = *reinterpret_cast<const uint4*>(ap + k_begin + 16 * s);
-        b0[s] = *reinterpret_cast<const uint4*>(bp0 + k_begin + 16 * s);
-        b1[s] = *reinterpret_cast<const uint4*>(bp1 + k_begin + 16 * s);
-    }
-    for (int k = k_begin; k < k_end; k += kBK) {
-        uint4 na[4], n0[4], n1[4];
-        const bool more = k + kBK < k_end;
-        if (more) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                na[s] = *reinterpret_cast<const uint4*>(ap + k + kBK + 16 * s);
-                n0[s] = *reinterpret_cast<const uint4*>(bp0 + k + kBK + 16 * s);
-                n1[s] = *reinterpret_cast<const uint4*>(bp1 + k + kBK + 16 * s);
-            }
-        }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            c0 = mfma(av[s], b0[s], c0);
-            c1 = mfma(av[s], b1[s], c1);
-        }
-        if (more) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                av[s] = na[s];
-                b0[s] = n0[s];
-                b1[s] = n1[s];
-            }
-        }
+    // The whole slice of w (128 rows) and h (64 rows) in flight at once.
+    uint8_t* lds_a = smem;
+    uint8_t* lds_b = smem + (size_t)128 * planes * 8 * 16;
+    const uint16_t* wrow = a.w + (int64_t)head * kHeadDim * a.w_stride + k_begin;
+    const uint16_t* hrow = a.h + k_begin;
+    const int64_t ws = a.w_stride, hs = a.h_stride;
+    const int t_first = tc * kChunk, t_last = a.e.T - 1;
+    for (int g = 0; g < planes; ++g) {                              // the whole slice in flight at once
+        plane_to_lds(lds_a, 128, g, [&](int r) { return wrow + r * ws; });
+        plane_to_lds(lds_b, kChunk, g, [&](int r) { return hrow + (int64_t)min(t_first + r, t_last) * hs; });
     }
 
-    float* pp = a.part + (int64_t)blockIdx.x * kPartFloats;
-    float4* p0 = reinterpret_cast<float4*>(pp + ((wave * 2 + 0) * 64 + lane) * 16);
-    float4* p1 = reinterpret_cast<float4*>(pp + ((wave * 2 + 1) * 64 + lane) * 16);
+    __builtin_amdgcn_s_waitcnt(0x3f70);                              // vmcnt(0): this wave's slots landed
+    __syncthreads();
+
+    // Four independent accumulation chains (two token blocks x even / odd 16-column steps).
+    f32x16_t c0 = {}, c1 = {}, d0 = {}, d1 = {};
+    const int ra = wave * 32 + (lane & 31), rb0 = lane & 31, rb1 = 32 + (lane & 31);
+    for (int g = 0; g < planes; ++g) {
+        uint4 av[4], b0[4], b1[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int c = 2 * q + hh;
+            av[q] = *reinterpret_cast<const uint4*>(lds_a + plane_slot(128, g, ra, c) * 16);
+            b0[q] = *reinterpret_cast<const uint4*>(lds_b + plane_slot(kChunk, g, rb0, c) * 16);
+            b1[q] = *reinterpret_cast<const uint4*>(lds_b + plane_slot(kChunk, g, rb1, c) * 16);
+        }
+        c0 = mfma(av[0], b0[0], c0);
+        c1 = mfma(av[0], b1[0], c1);
+        d0 = mfma(av[1], b0[1], d0);
+        d1 = mfma(av[1], b1[1], d1);
+        c0 = mfma(av[2], b0[2], c0);
+        c1 = mfma(av[2], b1[2], c1);
+        d0 = mfma(av[3], b0[3], d0);
+        d1 = mfma(av[3], b1[3], d1);
+    }
+    c0 += d0;
+    c1 += d1;
+
+    // Partial sums of this slice, [slice][wave][tb][q][lane] x 4 floats within the (head, chunk)
+    // region, stored with agent-scope coherence (sc1) so that the slice that reduces them (maybe on
+    // another XCD, behind another L2) reads them without a cache-wide write-back: a device-scope
+    // fence would write back the whole L2 in every work-group.
+    const int region_bytes = a.splits * kPartFloats * (int)sizeof(float);
+    float* region = a.part + (int64_t)pair * a.splits * kPartFloats;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(region, (short)0, region_bytes, kRawBufferFormat);
+    const int wbase = (split * 4 + wave) * 2 * 4 * 64 * 16 + lane * 16;   // bytes; tb = 0, q = 0
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        p0[q] = make_float4(c0[4 * q], c0[4 * q + 1], c0[4 * q + 2], c0[4 * q + 3]);
-        p1[q] = make_float4(c1[4 * q], c1[4 * q + 1], c1[4 * q + 2], c1[4 * q + 3]);
+        const f32x4_t v0 = {c0[4 * q], c0[4 * q + 1], c0[4 * q + 2], c0[4 * q + 3]};
+        const f32x4_t v1 = {c1[4 * q], c1[4 * q + 1], c1[4 * q + 2], c1[4 * q + 3]};
+        __builtin_amdgcn_raw_buffer_store_b128(v0, rs, wbase + q * 1024, 0, kAgentCoherent);
+        __builtin_amdgcn_raw_buffer_store_b128(v1, rs, wbase + 4096 + q * 1024, 0, kAgentCoherent);
     }
-    __threadfence();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // this wave's stores have completed
     __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t prev = atomicAdd(&a.counters[pair], 1u);
+    if (tid == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(&a.counters[pair], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const int last = prev == (uint32_t)(a.splits - 1);
-        if (last) atomicExch(&a.counters[pair], 0u);     // ready for the next call
+        if (last) __hip_atomic_store(&a.counters[pair], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // next call
         s_last = last;
     }
     __syncthreads();
-    if (!s_last || wave >= 2) return;
-    __threadfence();
+    if (!s_last) return;
 
-    // Last slice of this (head, chunk): waves 0 and 1 each take one 32-token block, add the slices'
-    // partial sums in slice order and run the epilogue.
-    const int tb = wave;
-    const float* base = a.part + (int64_t)pair * a.splits * kPartFloats;
+    // Last slice of this (head, chunk).  Wave w adds, in slice order, token block w & 1 of feature
+    // blocks 2 (w >> 1) and 2 (w >> 1) + 1, with the agent-scope loads of four slices in flight at a
+    // time.  (Loads straight into LDS are not used here: they do not bypass the caches for data
+    // another XCD wrote.)  Waves 2 and 3 then hand their half to waves 0 and 1, which hold whole
+    // head rows and run the epilogue.
+    const int tb = wave & 1, bh = wave >> 1;
+    float half[2][16] = {};
+    for (int s0 = 0; s0 < a.splits; s0 += 4) {
+        f32x4_t v[4][2][4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int sl = min(s0 + u, a.splits - 1);             // past the last slice: reread it, unused
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    v[u][bb][q] = __builtin_amdgcn_raw_buffer_load_b128(
+                        rs, ((((sl * 4 + 2 * bh + bb) * 2 + tb) * 4 + q) * 64 + lane) * 16, 0, kAgentCoherent);
+        }
+        __builtin_amdgcn_sched_barrier(0);                    // all loads above issue before any add
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const bool live = s0 + u < a.splits, first = s0 + u == 0;
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float x = v[u][bb][q][e];
+                        const float sum = first ? x : half[bb][4 * q + e] + x;
+                        half[bb][4 * q + e] = live ? sum : half[bb][4 * q + e];
+                    }
+        }
+    }
+    float* xchg = reinterpret_cast<float*>(smem);             // [tb][feature block - 2][i][lane]
+    if (bh == 1) {
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) xchg[((tb * 2 + bb) * 16 + i) * 64 + lane] = half[bb][i];
+    }
+    __syncthreads();
+    if (bh == 1) return;
     float acc[4][16];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const float4* src = reinterpret_cast<const float4*>(base + ((b * 2 + tb) * 64 + lane) * 16);
+    for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float4 v = src[q];
-            acc[b][4 * q] = v.x; acc[b][4 * q + 1] = v.y; acc[b][4 * q + 2] = v.z; acc[b][4 * q + 3] = v.w;
+        for (int i = 0; i < 16; ++i) {
+            acc[bb][i] = half[bb][i];
+            acc[2 + bb][i] = xchg[((tb * 2 + bb) * 16 + i) * 64 + lane];
         }
-    }
-    for (int s = 1; s < a.splits; ++s) {
-        const float* ps = base + (int64_t)s * kPartFloats;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const float4* src = reinterpret_cast<const float4*>(ps + ((b * 2 + tb) * 64 + lane) * 16);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float4 v = src[q];
-                acc[b][4 * q] += v.x; acc[b][4 * q + 1] += v.y; acc[b][4 * q + 2] += v.z; acc[b][4 * q + 3] += v.w;
-            }
-        }
-    }
     epilogue<kProduce>(a.e, head, tc * kChunk + tb * 32 + (lane & 31), acc);
 }
 
@@ -422,19 +490,15 @@ struct SplitPlan {
     uint64_t counter_bytes, bytes;
 };
 
-// K slices per (head, chunk): enough work-groups to cover the chip about once, at most 8 slices
-// (the last slice reads every slice's partials through one compute unit), each slice a multiple
-// of 64.
+// K slices per (head, chunk): as few as the LDS allows (a slice of at most kSliceMax columns of w
+// and h is staged whole), the slice width a multiple of 64.
 SplitPlan split_plan(int32_t T, int32_t K, int32_t heads)
 {
     SplitPlan p;
     p.n_tc = (T + kChunk - 1) / kChunk;
     const int64_t groups = (int64_t)heads * p.n_tc;
-    int64_t want = (256 + groups - 1) / groups;
     const int64_t steps = K / kBK;
-    if (want > 8) want = 8;
-    if (want > steps) want = steps;
-    if (want < 1) want = 1;
+    const int64_t want = (K + kSliceMax - 1) / kSliceMax;
     p.kc = (int32_t)(((steps + want - 1) / want) * kBK);
     p.splits = (K + p.kc - 1) / p.kc;
     p.counter_bytes = round_up((uint64_t)groups * sizeof(uint32_t));
