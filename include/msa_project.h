@@ -23,14 +23,14 @@
  * touches memory.  The pages fuse only up to "one wider GEMM" feeding "one fused producer"; this
  * entry point goes one step further.
  *
- * Kernels: a split-K kernel for up to 1,024 tokens (the decode and verify batches: heads x token
- * chunks x K slices, partial sums in the workspace, the last slice of each (head, chunk) reduces
- * them in a fixed order and runs the epilogue), and a 256 x 256 tiled kernel for larger batches
- * (prefill), both on v_mfma_f32_32x32x16_bf16.
+ * Kernels: for up to 1,024 tokens (the decode and verify batches) two launches, a split-K kernel
+ * (heads x 64-token chunks x K slices, partial sums in the workspace) and a kernel that adds the
+ * slices in a fixed order and runs the epilogue; for larger batches (prefill) one 256 x 256 tiled
+ * kernel.  All on v_mfma_f32_32x32x16_bf16.
  *
  * Conventions are those of msa_produce.h (device pointers unchecked for residency, no allocation,
  * no synchronisation, all checks on the host before any launch, MSA_OK means enqueued,
- * graph-capture safe), plus the workspace rule below.
+ * graph-capture safe).
  */
 #ifndef MSA_PROJECT_H
 #define MSA_PROJECT_H
@@ -44,14 +44,11 @@ extern "C" {
 #endif
 
 /*
- * msa_project_workspace_size — bytes of workspace a projection of num_tokens rows of width hidden
- * onto num_heads heads of 128 columns needs (both entry points take the same).  Zero for batches
- * above 1,024 tokens.
- *
- * Workspace rule: the workspace (device memory, 256-byte aligned) must be zero-filled before its
- * first use by either entry point; every call leaves the bytes it uses as counters at zero again,
- * so one zero-fill serves any number of calls.  Calls that share a workspace must not overlap in
- * time (same stream, or ordered).
+ * msa_project_workspace_size — bytes of workspace (device memory, 256-byte aligned) a projection of
+ * num_tokens rows of width hidden onto num_heads heads of 128 columns needs (both entry points
+ * take the same): the split-K partial sums.  Zero for batches above 1,024 tokens.  Its contents on
+ * entry do not matter; calls that share a workspace must not overlap in time (same stream, or
+ * ordered).
  */
 msa_status msa_project_workspace_size(int32_t num_tokens, int32_t hidden, int32_t num_heads, uint64_t* bytes);
 
@@ -64,7 +61,7 @@ msa_status msa_project_workspace_size(int32_t num_tokens, int32_t hidden, int32_
  * w            device bf16 [num_cols, hidden], row stride w_row_stride (>= hidden, multiple of 8), 16-B aligned.
  * num_cols     N: a positive multiple of 128, at most 4096 * 128.
  * x_out        device bf16 [T, num_cols], row stride x_row_stride (>= num_cols, multiple of 8), 16-B aligned.
- * workspace    see the workspace rule; may be NULL when msa_project_workspace_size gives 0.
+ * workspace    as msa_project_workspace_size states; may be NULL when it gives 0.
  */
 msa_status msa_project(const uint16_t* h, int64_t h_row_stride, int32_t num_tokens, int32_t hidden,
                        const uint16_t* w, int64_t w_row_stride, int32_t num_cols,
@@ -86,7 +83,7 @@ msa_status msa_project(const uint16_t* h, int64_t h_row_stride, int32_t num_toke
  *              msa_produce's slots_out); < 0, or a page outside [0, num_pages): no cache write.
  *              Valid slots must be distinct.
  * page_size    > 0; num_pages >= 0.
- * workspace    see the workspace rule.
+ * workspace    as msa_project_workspace_size states.
  */
 msa_status msa_project_produce(const uint16_t* h, int64_t h_row_stride, int32_t num_tokens, int32_t hidden,
                                const uint16_t* w, int64_t w_row_stride, int32_t head_dim,

@@ -267,7 +267,7 @@ def msa_produce_unfused(x, positions, slots, q_norm_weight, k_norm_weight, iq_no
 
 
 def msa_project_workspace_size(num_tokens: int, hidden: int, num_heads: int) -> int:
-    """Bytes of (zero-filled, 256-byte aligned) workspace the projection needs; 0 above 1,024 tokens."""
+    """Bytes of (256-byte aligned) workspace the projection needs; 0 above 1,024 tokens."""
     n = ctypes.c_uint64(0)
     st = lib().msa_project_workspace_size(int(num_tokens), int(hidden), int(num_heads), ctypes.byref(n))
     if st != 0:

@@ -12,16 +12,21 @@
 // rotate-half partners (f, f + 64) sit in the same lane (row blocks b and b + 2, same register).
 //
 // Kernels.
-//   project_splitk_kernel  up to 1,024 tokens: one work-group per (head, 64-token chunk, K slice);
-//                          each wave owns 32 of the head's features for the chunk and streams its
-//                          slice of w and h straight from memory into MFMA operands.  Partial sums go
-//                          to the workspace; the last slice to finish for a (head, chunk) (a counter
-//                          per pair) adds the slices in slice order and runs the epilogue.
+//   project_split_kernel   up to 1,024 tokens: one work-group per (head, 64-token chunk, K slice of
+//                          at most 384 columns).  The slice of w (128 rows) and h (64 rows) is
+//                          requested into LDS at once with direct global -> LDS loads (the latency
+//                          of the whole slice is paid once), then each wave multiplies 32 of the
+//                          head's features against the chunk; partial sums go to the workspace.
+//   project_reduce_kernel  one work-group per (head, chunk, 32-token block): adds the slices'
+//                          partial sums in slice order (the same order on every call) and runs the
+//                          epilogue.  The kernel boundary between the two makes the partial sums
+//                          visible across XCDs; no device-scope fence is needed.
 //   project_tile_kernel    larger batches: 256 features (2 heads) x 256 tokens per work-group, four
-//                          waves of one head x 128 tokens each, 64-wide K steps double-buffered
-//                          through LDS (row pitch 144 bytes: conflict-free 16-byte fragment reads),
-//                          the tile order chosen so that the work-groups of one XCD walk the feature
-//                          tiles of the same token rows (their h panel stays in that XCD's L2).
+//                          waves of one head x 128 tokens each, 64-wide K steps through two LDS
+//                          buffers (row pitch 144 bytes: conflict-free 16-byte fragment reads),
+//                          with the global loads of each stage issued two steps ahead, and the tile
+//                          order chosen so that the work-groups of one XCD walk the feature tiles of
+//                          the same token rows (their h panel stays in that XCD's L2).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -43,8 +48,6 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kSplitMaxTokens = 1024;
 constexpr int kChunk = 64;                 // tokens per split-K work-group (two MFMA token blocks)
 constexpr int kPartFloats = 4 * 2 * 4 * 64 * 4;   // one work-group's partial sums: [wave][tb][q][lane][4]
-constexpr int kRawBufferFormat = 0x00020000;   // buffer descriptor word 3: 32-bit elements
-constexpr int kAgentCoherent = 16;             // buffer cache policy: sc1 (agent-scope coherent)
 constexpr int kTile = 256;                 // tiled kernel: features and tokens per work-group
 constexpr int kBK = 64;                    // K per pipeline stage
 constexpr int kPitch = 72;                 // LDS row pitch in bf16 elements (144 B)
@@ -196,7 +199,6 @@ struct SplitArgs {
     const uint16_t* w;
     int64_t w_stride;
     float* part;               // [head][chunk][slice] x kPartFloats
-    uint32_t* counters;        // [head][chunk]
     int32_t K, kc, splits, n_tc;
     Epi e;
 };
@@ -230,12 +232,10 @@ __device__ __forceinline__ void plane_to_lds(uint8_t* dst, int rows, int g, RowP
     }
 }
 
-template <bool kProduce>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void project_splitk_kernel(const SplitArgs a)
+void project_split_kernel(const SplitArgs a)
 {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kSplitLds];
-    __shared__ int s_last;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);       // 32-feature block of the head
@@ -254,11 +254,10 @@ void project_splitk_kernel(const SplitArgs a)
     const uint16_t* hrow = a.h + k_begin;
     const int64_t ws = a.w_stride, hs = a.h_stride;
     const int t_first = tc * kChunk, t_last = a.e.T - 1;
-    for (int g = 0; g < planes; ++g) {                              // the whole slice in flight at once
+    for (int g = 0; g < planes; ++g) {
         plane_to_lds(lds_a, 128, g, [&](int r) { return wrow + r * ws; });
         plane_to_lds(lds_b, kChunk, g, [&](int r) { return hrow + (int64_t)min(t_first + r, t_last) * hs; });
     }
-
     __builtin_amdgcn_s_waitcnt(0x3f70);                              // vmcnt(0): this wave's slots landed
     __syncthreads();
 
@@ -286,85 +285,69 @@ void project_splitk_kernel(const SplitArgs a)
     c0 += d0;
     c1 += d1;
 
-    // Partial sums of this slice, [slice][wave][tb][q][lane] x 4 floats within the (head, chunk)
-    // region, stored with agent-scope coherence (sc1) so that the slice that reduces them (maybe on
-    // another XCD, behind another L2) reads them without a cache-wide write-back: a device-scope
-    // fence would write back the whole L2 in every work-group.
-    const int region_bytes = a.splits * kPartFloats * (int)sizeof(float);
-    float* region = a.part + (int64_t)pair * a.splits * kPartFloats;
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(region, (short)0, region_bytes, kRawBufferFormat);
-    const int wbase = (split * 4 + wave) * 2 * 4 * 64 * 16 + lane * 16;   // bytes; tb = 0, q = 0
+    // Partial sums of this slice: [pair][slice][wave][tb][q][lane] x 4 floats.  The reduction runs
+    // in the next kernel, after the kernel boundary has made these stores visible device-wide.
+    f32x4_t* pp = reinterpret_cast<f32x4_t*>(a.part + ((int64_t)pair * a.splits + split) * kPartFloats) +
+                  (wave * 2 * 4) * 64 + lane;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const f32x4_t v0 = {c0[4 * q], c0[4 * q + 1], c0[4 * q + 2], c0[4 * q + 3]};
-        const f32x4_t v1 = {c1[4 * q], c1[4 * q + 1], c1[4 * q + 2], c1[4 * q + 3]};
-        __builtin_amdgcn_raw_buffer_store_b128(v0, rs, wbase + q * 1024, 0, kAgentCoherent);
-        __builtin_amdgcn_raw_buffer_store_b128(v1, rs, wbase + 4096 + q * 1024, 0, kAgentCoherent);
+        pp[q * 64] = f32x4_t{c0[4 * q], c0[4 * q + 1], c0[4 * q + 2], c0[4 * q + 3]};
+        pp[(4 + q) * 64] = f32x4_t{c1[4 * q], c1[4 * q + 1], c1[4 * q + 2], c1[4 * q + 3]};
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // this wave's stores have completed
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t prev = __hip_atomic_fetch_add(&a.counters[pair], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int last = prev == (uint32_t)(a.splits - 1);
-        if (last) __hip_atomic_store(&a.counters[pair], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // next call
-        s_last = last;
-    }
-    __syncthreads();
-    if (!s_last) return;
+}
 
-    // Last slice of this (head, chunk).  Wave w adds, in slice order, token block w & 1 of feature
-    // blocks 2 (w >> 1) and 2 (w >> 1) + 1, with the agent-scope loads of four slices in flight at a
-    // time.  (Loads straight into LDS are not used here: they do not bypass the caches for data
-    // another XCD wrote.)  Waves 2 and 3 then hand their half to waves 0 and 1, which hold whole
-    // head rows and run the epilogue.
-    const int tb = wave & 1, bh = wave >> 1;
-    float half[2][16] = {};
-    for (int s0 = 0; s0 < a.splits; s0 += 4) {
-        f32x4_t v[4][2][4];
+// One work-group per (head, chunk, 32-token block): wave w adds, in slice order, the partial sums of
+// feature block w and hands them to wave 0 through LDS; wave 0 holds the head rows and runs the
+// epilogue.
+template <bool kProduce>
+__global__ __launch_bounds__(256) void project_reduce_kernel(const SplitArgs a)
+{
+    __shared__ float xchg[4][16][64];                          // [feature block][i][lane]
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tb = (int)(blockIdx.x & 1);
+    const int pair = (int)(blockIdx.x >> 1);
+    const int tc = pair % a.n_tc;
+    const int head = pair / a.n_tc;
+    const f32x4_t* base = reinterpret_cast<const f32x4_t*>(a.part + (int64_t)pair * a.splits * kPartFloats) +
+                          ((wave * 2 + tb) * 4) * 64 + lane;
+    float part[16] = {};
+    for (int s0 = 0; s0 < a.splits; s0 += 8) {
+        f32x4_t v[8][4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int sl = min(s0 + u, a.splits - 1);             // past the last slice: reread it, unused
+        for (int u = 0; u < 8; ++u) {
+            const int sl = min(s0 + u, a.splits - 1);              // past the last slice: reread it, unused
 #pragma unroll
-            for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    v[u][bb][q] = __builtin_amdgcn_raw_buffer_load_b128(
-                        rs, ((((sl * 4 + 2 * bh + bb) * 2 + tb) * 4 + q) * 64 + lane) * 16, 0, kAgentCoherent);
+            for (int q = 0; q < 4; ++q) v[u][q] = base[(int64_t)sl * (kPartFloats / 4) + q * 64];
         }
-        __builtin_amdgcn_sched_barrier(0);                    // all loads above issue before any add
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 8; ++u) {
             const bool live = s0 + u < a.splits, first = s0 + u == 0;
 #pragma unroll
-            for (int bb = 0; bb < 2; ++bb)
+            for (int q = 0; q < 4; ++q)
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float x = v[u][bb][q][e];
-                        const float sum = first ? x : half[bb][4 * q + e] + x;
-                        half[bb][4 * q + e] = live ? sum : half[bb][4 * q + e];
-                    }
+                for (int e = 0; e < 4; ++e) {
+                    const float x = v[u][q][e];
+                    const float sum = first ? x : part[4 * q + e] + x;
+                    part[4 * q + e] = live ? sum : part[4 * q + e];
+                }
         }
     }
-    float* xchg = reinterpret_cast<float*>(smem);             // [tb][feature block - 2][i][lane]
-    if (bh == 1) {
+    if (wave > 0) {
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) xchg[((tb * 2 + bb) * 16 + i) * 64 + lane] = half[bb][i];
+        for (int i = 0; i < 16; ++i) xchg[wave][i][lane] = part[i];
     }
     __syncthreads();
-    if (bh == 1) return;
+    if (wave > 0) return;
     float acc[4][16];
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            acc[bb][i] = half[bb][i];
-            acc[2 + bb][i] = xchg[((tb * 2 + bb) * 16 + i) * 64 + lane];
-        }
-    epilogue<kProduce>(a.e, head, tc * kChunk + tb * 32 + (lane & 31), acc);
+    for (int i = 0; i < 16; ++i) {
+        acc[0][i] = part[i];
+        acc[1][i] = xchg[1][i][lane];
+        acc[2][i] = xchg[2][i][lane];
+        acc[3][i] = xchg[3][i][lane];
+    }
+    epilogue<kProduce>(a.e, head, tc * kChunk + tb * 32 + lane % 32, acc);
 }
 
 // ------------------------------------------------------------------ tiled kernel (prefill)
@@ -392,7 +375,7 @@ template <bool kProduce>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void project_tile_kernel(const TileArgs a)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][kTile][kPitch];   // [stage][w | h][row][k]
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][kTile][kPitch];   // [buffer][w | h][row][k]
     const uint32_t L = xcd_tile(blockIdx.x, (uint32_t)(a.n_tt * a.n_tf));
     const int tile_t = (int)(L / (uint32_t)a.n_tf);
     const int tile_f = (int)(L - (uint32_t)tile_t * (uint32_t)a.n_tf);
@@ -403,70 +386,88 @@ void project_tile_kernel(const TileArgs a)
     const int hh = lane >> 5;
     const int f_base = tile_f * kTile, t_base = tile_t * kTile;
 
-    // Global -> LDS: thread `tid` moves 16 B (8 k) at column 8 (tid & 7) of rows (tid >> 3) + 32 j.
+    // Global -> LDS: thread `tid` moves 16 B (8 k) at column 8 (tid & 7) of rows (tid >> 3) + 32 j,
+    // j < 8, of the w tile and of the h tile (rows past the matrix read its last row, unused).  Two
+    // named register sets (no private arrays) carry stages two steps ahead of the products: the
+    // loads for stage k + 2 are issued at the start of step k and written to LDS at the end of
+    // step k + 1, so each has two steps of matrix work to arrive.
     const int r0 = tid >> 3, c8 = (tid & 7) * 8;
-    const uint16_t* ga[8];
-    const uint16_t* gb[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        ga[j] = a.w + (int64_t)min(f_base + r0 + 32 * j, a.N - 1) * a.w_stride + c8;
-        gb[j] = a.h + (int64_t)min(t_base + r0 + 32 * j, a.e.T - 1) * a.h_stride + c8;
-    }
+    const uint16_t* wa = a.w + c8;
+    const uint16_t* hb = a.h + c8;
+    const int64_t ws = a.w_stride, hs = a.h_stride;
+#define ROW_A(j) (wa + (int64_t)min(f_base + r0 + 32 * (j), a.N - 1) * ws)
+#define ROW_B(j) (hb + (int64_t)min(t_base + r0 + 32 * (j), a.e.T - 1) * hs)
+    const uint16_t *ga0 = ROW_A(0), *ga1 = ROW_A(1), *ga2 = ROW_A(2), *ga3 = ROW_A(3), *ga4 = ROW_A(4),
+                   *ga5 = ROW_A(5), *ga6 = ROW_A(6), *ga7 = ROW_A(7);
+    const uint16_t *gb0 = ROW_B(0), *gb1 = ROW_B(1), *gb2 = ROW_B(2), *gb3 = ROW_B(3), *gb4 = ROW_B(4),
+                   *gb5 = ROW_B(5), *gb6 = ROW_B(6), *gb7 = ROW_B(7);
+#undef ROW_A
+#undef ROW_B
+#define LD(p, k) (*reinterpret_cast<const uint4*>((p) + (k)))
+#define ST(st, m, j, v) (*reinterpret_cast<uint4*>(&lds[st][m][r0 + 32 * (j)][c8]) = (v))
+#define LOAD_SET(X, k)                                                                                    \
+    X##a0 = LD(ga0, k); X##a1 = LD(ga1, k); X##a2 = LD(ga2, k); X##a3 = LD(ga3, k); X##a4 = LD(ga4, k);     \
+    X##a5 = LD(ga5, k); X##a6 = LD(ga6, k); X##a7 = LD(ga7, k); X##b0 = LD(gb0, k); X##b1 = LD(gb1, k);     \
+    X##b2 = LD(gb2, k); X##b3 = LD(gb3, k); X##b4 = LD(gb4, k); X##b5 = LD(gb5, k); X##b6 = LD(gb6, k);     \
+    X##b7 = LD(gb7, k)
+#define STORE_SET(X, st)                                                                                  \
+    ST(st, 0, 0, X##a0); ST(st, 0, 1, X##a1); ST(st, 0, 2, X##a2); ST(st, 0, 3, X##a3); ST(st, 0, 4, X##a4); \
+    ST(st, 0, 5, X##a5); ST(st, 0, 6, X##a6); ST(st, 0, 7, X##a7); ST(st, 1, 0, X##b0); ST(st, 1, 1, X##b1); \
+    ST(st, 1, 2, X##b2); ST(st, 1, 3, X##b3); ST(st, 1, 4, X##b4); ST(st, 1, 5, X##b5); ST(st, 1, 6, X##b6); \
+    ST(st, 1, 7, X##b7)
+    uint4 Pa0, Pa1, Pa2, Pa3, Pa4, Pa5, Pa6, Pa7, Pb0, Pb1, Pb2, Pb3, Pb4, Pb5, Pb6, Pb7;
+    uint4 Qa0, Qa1, Qa2, Qa3, Qa4, Qa5, Qa6, Qa7, Qb0, Qb1, Qb2, Qb3, Qb4, Qb5, Qb6, Qb7;
+
     f32x16_t acc[4][4];
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) acc[b][tb] = f32x16_t{};
 
-    const int nk = a.K / kBK;
-    {
-        uint4 ra[8], rb[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            ra[j] = *reinterpret_cast<const uint4*>(ga[j]);
-            rb[j] = *reinterpret_cast<const uint4*>(gb[j]);
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            *reinterpret_cast<uint4*>(&lds[0][0][r0 + 32 * j][c8]) = ra[j];
-            *reinterpret_cast<uint4*>(&lds[0][1][r0 + 32 * j][c8]) = rb[j];
-        }
-    }
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int s = kt & 1;
-        // Next stage's slice, in flight during this stage's MFMAs (the last step re-reads its own
-        // slice, unused, so the loads stay unconditional).
-        const int kn = (kt + 1 < nk ? kt + 1 : kt) * kBK;
-        uint4 ra[8], rb[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            ra[j] = *reinterpret_cast<const uint4*>(ga[j] + kn);
-            rb[j] = *reinterpret_cast<const uint4*>(gb[j] + kn);
-        }
+    // The products of the stage in LDS buffer st.
+    auto compute = [&](int st) {
 #pragma unroll
         for (int ks = 0; ks < kBK / 16; ++ks) {
             uint4 af[4], bf[4];
 #pragma unroll
             for (int b = 0; b < 4; ++b)
-                af[b] = *reinterpret_cast<const uint4*>(&lds[s][0][wf * 128 + b * 32 + (lane & 31)][ks * 16 + 8 * hh]);
+                af[b] = *reinterpret_cast<const uint4*>(&lds[st][0][wf * 128 + b * 32 + (lane & 31)][ks * 16 + 8 * hh]);
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb)
-                bf[tb] = *reinterpret_cast<const uint4*>(&lds[s][1][wt * 128 + tb * 32 + (lane & 31)][ks * 16 + 8 * hh]);
+                bf[tb] = *reinterpret_cast<const uint4*>(&lds[st][1][wt * 128 + tb * 32 + (lane & 31)][ks * 16 + 8 * hh]);
 #pragma unroll
             for (int b = 0; b < 4; ++b)
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb) acc[b][tb] = mfma(af[b], bf[tb], acc[b][tb]);
         }
-        if (kt + 1 < nk) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                *reinterpret_cast<uint4*>(&lds[s ^ 1][0][r0 + 32 * j][c8]) = ra[j];
-                *reinterpret_cast<uint4*>(&lds[s ^ 1][1][r0 + 32 * j][c8]) = rb[j];
-            }
-        }
+    };
+
+    const int nk = a.K / kBK;
+    const int last = (nk - 1) * kBK;
+    LOAD_SET(P, 0);
+    STORE_SET(P, 0);
+    LOAD_SET(Q, min(kBK, last));                                  // stage 1 waits in Q
+    __syncthreads();
+    // Step k: buffer k & 1 holds stage k; the other set holds stage k + 1.  Loads past the last
+    // stage re-read it (unused), keeping every load and LDS write unconditional.
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+        LOAD_SET(P, min((kt + 2) * kBK, last));
+        __builtin_amdgcn_sched_group_barrier(0x020, 16, 0);      // the 16 global loads first
+        compute(0);
+        STORE_SET(Q, 1);
+        __syncthreads();
+        LOAD_SET(Q, min((kt + 3) * kBK, last));
+        __builtin_amdgcn_sched_group_barrier(0x020, 16, 0);
+        compute(1);
+        STORE_SET(P, 0);
         __syncthreads();
     }
+    if (kt < nk) compute(0);                                      // odd number of stages: the last one
+#undef LD
+#undef ST
+#undef LOAD_SET
+#undef STORE_SET
 
     const int head = tile_f * 2 + wf;
     if (head >= a.heads) return;
@@ -487,7 +488,7 @@ uint64_t round_up(uint64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct SplitPlan {
     int32_t splits, kc, n_tc;
-    uint64_t counter_bytes, bytes;
+    uint64_t bytes;
 };
 
 // K slices per (head, chunk): as few as the LDS allows (a slice of at most kSliceMax columns of w
@@ -501,8 +502,7 @@ SplitPlan split_plan(int32_t T, int32_t K, int32_t heads)
     const int64_t want = (K + kSliceMax - 1) / kSliceMax;
     p.kc = (int32_t)(((steps + want - 1) / want) * kBK);
     p.splits = (K + p.kc - 1) / p.kc;
-    p.counter_bytes = round_up((uint64_t)groups * sizeof(uint32_t));
-    p.bytes = p.counter_bytes + (uint64_t)groups * p.splits * kPartFloats * sizeof(float);
+    p.bytes = round_up((uint64_t)groups * p.splits * kPartFloats * sizeof(float));
     return p;
 }
 
@@ -535,17 +535,19 @@ msa_status launch_projection(const uint16_t* h, int64_t h_row_stride, int32_t T,
         a.h_stride = h_row_stride;
         a.w = w;
         a.w_stride = w_row_stride;
-        a.counters = static_cast<uint32_t*>(workspace);
-        a.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + p.counter_bytes);
+        a.part = static_cast<float*>(workspace);
         a.K = K;
         a.kc = p.kc;
         a.splits = p.splits;
         a.n_tc = p.n_tc;
         a.e = e;
         void* args[] = {&a};
-        const dim3 grid((unsigned)((int64_t)heads * p.n_tc * p.splits));
-        err = hipLaunchKernel(reinterpret_cast<const void*>(&project_splitk_kernel<kProduce>), grid, dim3(256), args,
-                              0, s);
+        const int64_t pairs = (int64_t)heads * p.n_tc;
+        err = hipLaunchKernel(reinterpret_cast<const void*>(&project_split_kernel), dim3((unsigned)(pairs * p.splits)),
+                              dim3(256), args, 0, s);
+        if (err == hipSuccess)
+            err = hipLaunchKernel(reinterpret_cast<const void*>(&project_reduce_kernel<kProduce>),
+                                  dim3((unsigned)(pairs * 2)), dim3(256), args, 0, s);
     } else {
         TileArgs a;
         a.h = h;

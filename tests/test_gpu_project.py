@@ -47,7 +47,7 @@ def dev16(a):
 
 
 def workspace(T, K, heads):
-    return torch.zeros(max(msa.msa_project_workspace_size(T, K, heads), 256), dtype=torch.uint8, device="cuda")
+    return torch.empty(max(msa.msa_project_workspace_size(T, K, heads), 256), dtype=torch.uint8, device="cuda")
 
 
 def gpu_project(h, w, ws=None):
@@ -196,9 +196,9 @@ def test_project_produce_normal(name):
     assert min(fr) >= 0.95
 
 
-def test_workspace_counters_reset_between_calls():
-    """Two decode calls on one workspace: the second (after the outputs are cleared) writes the
-    same bytes, which it can only do if the first left every counter at zero."""
+def test_workspace_contents_do_not_matter():
+    """Two decode calls on one workspace, the second after the outputs are cleared and the workspace
+    is filled with garbage: both write the same bytes."""
     wl = W.config1()
     h, w = W.with_projection(wl, seed=9)
     ws = workspace(wl.T, h.shape[1], wl.W // 128)
@@ -208,12 +208,11 @@ def test_workspace_counters_reset_between_calls():
     d.iq_out.zero_()
     for s in d.storages:
         s.fill_(W.SENTINEL_BYTE)
+    ws.fill_(0xA5)
     fused(wl, h, w, d=d, ws=ws)
     assert torch.equal(first[0], d.q_out) and torch.equal(first[1], d.iq_out)
     for a, b in zip(first[2], d.storages):
         assert torch.equal(a, b)
-    n_pairs = (wl.W // 128) * ((wl.T + 63) // 64)
-    assert int(ws[: 4 * n_pairs].count_nonzero()) == 0
 
 
 def test_graph_replay_decode_layers():
@@ -259,6 +258,7 @@ def test_graph_replay_decode_layers():
             for d in devs:
                 d.q_out.fill_(3)
                 d.iq_out.fill_(3)
+            ws.fill_(0x5A)
             torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
