@@ -11,8 +11,10 @@ The metric has two parts, measured on two workloads:
     heads, fp8 caches of 10,240 pages per layer; 60 layer calls (each with its own input row, norm
     weights, scales and caches) captured once in a HIP graph and replayed.  Reported as
     `us_per_layer_call` and `us_per_decode_step`, with their own roofline under `decode`.
-Also reported: the indexer at decode batch 64 (`indexer`), and the same decode step and prefill
-chunk through the unfused path (`unfused`: 14 launches per layer instead of one, identical bytes).
+Also reported: the indexer at decode batch 64 (`indexer`); the same decode step and prefill chunk
+through the unfused path (`unfused`: 14 launches per layer instead of one, identical bytes); and
+the packed projection of hidden states (hidden 3072) alone and with the producer as its epilogue,
+against torch.mm (hipBLASLt) followed by the producer (`projection`).
 Inputs are resident in HBM before every timed region.  `cpu_baseline` is the CPU oracle on a
 bounded sample of the prefill workload.
 
@@ -253,6 +255,134 @@ def bench_indexer(msa, W, torch, np, reps):
                               traffic=None, kernel="index_scores_kernel<2> + index_topk_kernel"))
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def bench_projection(msa, W, torch, np, layers, steps, warmup):
+    """The packed projection x = bf16(h w^T) (hidden 3072, 2,944 packed columns) alone and with the
+    producer as its epilogue, against the same projection through torch.mm (hipBLASLt) followed by
+    msa_produce.  Prefill: the 65,536-token chunk, eager launches timed with HIP events.  Decode
+    batch 64: `layers` layers per step captured in one HIP graph (RoPE table and slots once per
+    step for the fused path)."""
+    def dev16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+
+    def timed(fn, n, warm, stream=None):
+        s = stream or torch.cuda.current_stream()
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(n):
+            fn()
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1000 / n
+
+    out = {"hidden": W.PROJECTION_HIDDEN, "inputs": "h ~ N(0, 1), w ~ N(0, 1/hidden), bf16"}
+    # ---- prefill
+    wl = W.config3()
+    d = W.to_device(wl)
+    h, w = W.with_projection(wl, seed=1)
+    hd, wd = dev16(h), dev16(w)
+    T, K = h.shape
+    x = torch.empty((T, wl.W), dtype=torch.int16, device="cuda")
+    cos = torch.empty((T, 64), dtype=torch.float32, device="cuda")
+    sin = torch.empty_like(cos)
+    msa.msa_rope_table(d.positions, cos, sin, wl.theta)
+    msa.msa_slots(d.positions, d.seq_idx, d.page_table, d.slots, page_size=wl.page_size, num_pages=wl.num_pages)
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+
+    def produce():
+        call(msa, wl, d)
+
+    def fused():
+        msa.msa_project_produce(hd, wd, cos, sin, d.slots, *d.weights, d.q_out, d.iq_out, d.caches[0], d.caches[1],
+                                d.caches[2], workspace=ws, k_scale=d.scales[0], v_scale=d.scales[1],
+                                ik_scale=d.scales[2], num_pages=wl.num_pages, rms_eps=wl.eps)
+
+    d.x = x                                                   # produce() reads the projected row
+    n, warm = max(steps // 10, 5), max(warmup // 30, 5)
+    gemm_us = timed(lambda: msa.msa_project(hd, wd, x, workspace=ws), n, warm)
+    torch_us = timed(lambda: torch.mm(hd.view(torch.bfloat16), wd.view(torch.bfloat16).t(), out=x.view(torch.bfloat16)),
+                     n, warm)
+    prod_us = timed(produce, n, warm)
+    fused_us = timed(fused, n, warm)
+    flops = 2.0 * T * wl.W * K
+    tf = flops / (gemm_us * 1e-6) / 1e12
+    out["prefill"] = {
+        "tokens": T, "fused_us": fused_us, "msa_project_us": gemm_us, "msa_produce_us": prod_us,
+        "msa_project_plus_produce_us": gemm_us + prod_us, "torch_mm_us": torch_us,
+        "torch_mm_plus_produce_us": torch_us + prod_us,
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "project_tile_kernel<false> (msa_project, 65,536 x 3,072 x 2,944)"},
+    }
+    log(f"[bench] projection prefill: fused {fused_us:.1f} us, msa_project {gemm_us:.1f} us ({tf:.0f} TFLOP/s), "
+        f"torch.mm {torch_us:.1f} us, msa_produce {prod_us:.1f} us")
+    del d, x, hd, wd
+    torch.cuda.empty_cache()
+    # ---- decode batch 64, one graph per composition
+    wls = [W.config1(layer=i) for i in range(layers)]
+    devs = [W.to_device(x) for x in wls]
+    for dd in devs[1:]:
+        dd.positions, dd.seq_idx, dd.page_table = devs[0].positions, devs[0].seq_idx, devs[0].page_table
+    hws = [W.with_projection(x, seed=10 + i) for i, x in enumerate(wls)]
+    hds = [(dev16(a), dev16(b)) for a, b in hws]
+    d0, wl0 = devs[0], wls[0]
+    Tt = wl0.T
+    cos = torch.empty((Tt, 64), dtype=torch.float32, device="cuda")
+    sin = torch.empty_like(cos)
+    ws = torch.empty(msa.msa_project_workspace_size(Tt, K, wl0.W // 128), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((Tt, wl0.W), dtype=torch.int16, device="cuda")
+
+    def step_fused():
+        msa.msa_rope_table(d0.positions, cos, sin, wl0.theta)
+        msa.msa_slots(d0.positions, d0.seq_idx, d0.page_table, d0.slots, page_size=wl0.page_size,
+                      num_pages=wl0.num_pages)
+        for wl_, dd, (a_, b_) in zip(wls, devs, hds):
+            msa.msa_project_produce(a_, b_, cos, sin, d0.slots, *dd.weights, dd.q_out, dd.iq_out, dd.caches[0],
+                                    dd.caches[1], dd.caches[2], workspace=ws, k_scale=dd.scales[0],
+                                    v_scale=dd.scales[1], ik_scale=dd.scales[2], num_pages=wl_.num_pages)
+
+    def step_ours():
+        for wl_, dd, (a_, b_) in zip(wls, devs, hds):
+            msa.msa_project(a_, b_, xs, workspace=ws)
+            dd.x = xs
+            call(msa, wl_, dd)
+
+    def step_torch():
+        for wl_, dd, (a_, b_) in zip(wls, devs, hds):
+            torch.mm(a_.view(torch.bfloat16), b_.view(torch.bfloat16).t(), out=xs.view(torch.bfloat16))
+            dd.x = xs
+            call(msa, wl_, dd)
+
+    res = {"layers": layers, "tokens": Tt}
+    for name, fn in (("fused", step_fused), ("msa_project_plus_produce", step_ours),
+                     ("torch_mm_plus_produce", step_torch)):
+        s_ = torch.cuda.Stream()
+        s_.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s_):
+            fn()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=s_):
+                fn()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s_):
+            us = timed(g.replay, 50, 10, stream=s_)
+        res[name + "_us_per_step"] = us
+        res[name + "_us_per_layer"] = us / layers
+    out["decode"] = res
+    log(f"[bench] projection decode-64: fused {res['fused_us_per_layer']:.2f} us/layer, "
+        f"msa_project + produce {res['msa_project_plus_produce_us_per_layer']:.2f}, "
+        f"torch.mm + produce {res['torch_mm_plus_produce_us_per_layer']:.2f}")
+    del devs, hds
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(W, seconds: float):
     """The CPU oracle as it stands, on leading slices of the prefill workload for about `seconds`."""
     import oracle
@@ -292,6 +422,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-indexer", action="store_true", help="skip the indexer measurement")
     ap.add_argument("--no-unfused", action="store_true", help="skip the unfused-path comparison")
+    ap.add_argument("--no-projection", action="store_true", help="skip the projection (GEMM + producer) measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run three plain 1 GiB device-to-device copies (the reference kernel that "
                          "scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
@@ -332,6 +463,8 @@ def main():
 
     import numpy as np
     idx = None if args.no_indexer else bench_indexer(msa, W, torch, np, 50)
+    torch.cuda.empty_cache()
+    proj = None if args.no_projection else bench_projection(msa, W, torch, np, args.layers, args.steps, args.warmup)
     torch.cuda.empty_cache()
     pre = bench_prefill(msa, W, torch, args.steps, args.warmup, 0 if args.no_unfused else 50)
     cpu = None if args.no_cpu_baseline else cpu_baseline(W, args.cpu_seconds)
@@ -386,6 +519,7 @@ def main():
                         "launches_per_call": pre.get("unfused_launches_per_call"),
                         "fused_us_per_call": pre["us_per_call"]},
         },
+        "projection": proj,
         "indexer": idx,
         "cpu_baseline": cpu,
     }
