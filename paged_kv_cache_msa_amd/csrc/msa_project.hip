@@ -17,9 +17,9 @@
 //                          requested into LDS at once with direct global -> LDS loads (the latency
 //                          of the whole slice is paid once), then each wave multiplies 32 of the
 //                          head's features against the chunk; partial sums go to the workspace.
-//   project_reduce_kernel  one work-group per (head, chunk, 32-token block): adds the slices'
-//                          partial sums in slice order (the same order on every call) and runs the
-//                          epilogue.  The kernel boundary between the two makes the partial sums
+//   project_reduce_kernel  one work-group per (head, chunk, 32-token block): four waves add the
+//                          slices' partial sums in slice order (the same order on every call) while
+//                          a fifth fetches the epilogue's inputs, then runs the epilogue.  The kernel boundary between the two makes the partial sums
 //                          visible across XCDs; no device-scope fence is needed.
 //   project_tile_kernel    larger batches: 256 features (2 heads) x 256 tokens per work-group, four
 //                          waves of one head x 128 tokens each, 64-wide K steps through two LDS
@@ -81,11 +81,59 @@ struct Epi {
     float eps;
 };
 
+// The epilogue's per-lane inputs for one (head, token): the head's norm weights at this lane's 64
+// features, the token's RoPE coefficients at this lane's 32 frequencies, and its cache slot.
+struct EpiIn {
+    float w[4][16];
+    float c[2][16];
+    float s[2][16];
+    int64_t slot;
+};
+
+__device__ __forceinline__ int stream_of(const Epi& e, int head)
+{
+    const int h_k = e.hq, h_v = e.hq + e.hkv, h_iq = e.hq + 2 * e.hkv, h_ik = h_iq + e.hiq;
+    return head < h_k ? kQ : head < h_v ? kK : head < h_iq ? kV : head < h_ik ? kIQ : kIK;
+}
+
+// Loads EpiIn (produce mode only).  Lanes of tokens past T read token T - 1 and no slot.
+__device__ __forceinline__ void epilogue_load(const Epi& e, int head, int32_t t, EpiIn& in)
+{
+    const int hh = (threadIdx.x & 63) >> 5;
+    const int st = stream_of(e, head);
+    const bool tok = t < e.T;
+    in.slot = tok && (st == kK || st == kV || st == kIK) ? e.slots[t] : -1;
+    if (st == kV) return;
+    const uint16_t* wp = e.w[st == kQ ? 0 : st == kK ? 1 : st == kIQ ? 2 : 3] + 4 * hh;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const uint2 wv = *reinterpret_cast<const uint2*>(wp + 32 * b + 8 * g);
+            in.w[b][4 * g] = bf16_lo(wv.x);
+            in.w[b][4 * g + 1] = bf16_hi(wv.x);
+            in.w[b][4 * g + 2] = bf16_lo(wv.y);
+            in.w[b][4 * g + 3] = bf16_hi(wv.y);
+        }
+    const int32_t tl = tok ? t : e.T - 1;
+    const float* cp = e.cos + (int64_t)tl * kHalf + 4 * hh;
+    const float* sp = e.sin + (int64_t)tl * kHalf + 4 * hh;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const float4 c4 = *reinterpret_cast<const float4*>(cp + 32 * b + 8 * g);
+            const float4 s4 = *reinterpret_cast<const float4*>(sp + 32 * b + 8 * g);
+            in.c[b][4 * g] = c4.x; in.c[b][4 * g + 1] = c4.y; in.c[b][4 * g + 2] = c4.z; in.c[b][4 * g + 3] = c4.w;
+            in.s[b][4 * g] = s4.x; in.s[b][4 * g + 1] = s4.y; in.s[b][4 * g + 2] = s4.z; in.s[b][4 * g + 3] = s4.w;
+        }
+}
+
 // One head's row for one token per lane pair: a[b][i] is feature 32 b + 8 (i / 4) + 4 hh + i % 4
 // (hh = lane / 32) of `head`, token t.  Rounds the row to bf16 (the packed row's values), then
-// either stores it (plain) or runs the producer arithmetic on it.
+// either stores it (plain) or runs the producer arithmetic on it with the inputs `in`.
 template <bool kProduce>
-__device__ __forceinline__ void epilogue(const Epi& e, int head, int32_t t, float (&a)[4][16])
+__device__ __forceinline__ void epilogue_run(const Epi& e, int head, int32_t t, float (&a)[4][16], const EpiIn& in)
 {
     const int lane = threadIdx.x & 63;
     const int hh = lane >> 5;
@@ -111,7 +159,7 @@ __device__ __forceinline__ void epilogue(const Epi& e, int head, int32_t t, floa
     }
 
     const int h_k = e.hq, h_v = e.hq + e.hkv, h_iq = e.hq + 2 * e.hkv, h_ik = h_iq + e.hiq;
-    const int st = head < h_k ? kQ : head < h_v ? kK : head < h_iq ? kV : head < h_ik ? kIQ : kIK;
+    const int st = stream_of(e, head);
     if (st != kV) {
         // RMSNorm: binary64 sum of squares over the lane's 64 features plus the partner lane's.
         double ss = 0.0;
@@ -121,33 +169,18 @@ __device__ __forceinline__ void epilogue(const Epi& e, int head, int32_t t, floa
             for (int i = 0; i < 16; ++i) ss = __builtin_fma((double)a[b][i], (double)a[b][i], ss);
         ss += __shfl_xor(ss, 32);
         const float r = rms_from_ss(ss, e.eps);
-        const uint16_t* wp = e.w[st == kQ ? 0 : st == kK ? 1 : st == kIQ ? 2 : 3] + 4 * hh;
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const uint2 wv = *reinterpret_cast<const uint2*>(wp + 32 * b + 8 * g);
-                const float w4[4] = {bf16_lo(wv.x), bf16_hi(wv.x), bf16_lo(wv.y), bf16_hi(wv.y)};
-#pragma unroll
-                for (int q = 0; q < 4; ++q) a[b][4 * g + q] = (a[b][4 * g + q] * r) * w4[q];
-            }
+            for (int i = 0; i < 16; ++i) a[b][i] = (a[b][i] * r) * in.w[b][i];
         // RoPE, neox rotate-half: frequency f < 64 pairs feature f (block b) with f + 64 (block b + 2).
-        const int32_t tl = tok ? t : e.T - 1;
-        const float* cp = e.cos + (int64_t)tl * kHalf + 4 * hh;
-        const float* sp = e.sin + (int64_t)tl * kHalf + 4 * hh;
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const float4 c4 = *reinterpret_cast<const float4*>(cp + 32 * b + 8 * g);
-                const float4 s4 = *reinterpret_cast<const float4*>(sp + 32 * b + 8 * g);
-                const float c[4] = {c4.x, c4.y, c4.z, c4.w}, s[4] = {s4.x, s4.y, s4.z, s4.w};
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float y0 = a[b][4 * g + q], y1 = a[b + 2][4 * g + q];
-                    a[b][4 * g + q] = y0 * c[q] - y1 * s[q];
-                    a[b + 2][4 * g + q] = y1 * c[q] + y0 * s[q];
-                }
+            for (int i = 0; i < 16; ++i) {
+                const float y0 = a[b][i], y1 = a[b + 2][i];
+                a[b][i] = y0 * in.c[b][i] - y1 * in.s[b][i];
+                a[b + 2][i] = y1 * in.c[b][i] + y0 * in.s[b][i];
             }
     }
     if (!tok) return;
@@ -162,7 +195,7 @@ __device__ __forceinline__ void epilogue(const Epi& e, int head, int32_t t, floa
                     make_uint2(bf16x2(a[b][4 * g], a[b][4 * g + 1]), bf16x2(a[b][4 * g + 2], a[b][4 * g + 3]));
         return;
     }
-    const int64_t slot = e.slots[t];
+    const int64_t slot = in.slot;
     if (slot < 0) return;
     const int64_t page = slot / e.page_size;
     if (page >= e.num_pages) return;
@@ -189,6 +222,14 @@ __device__ __forceinline__ void epilogue(const Epi& e, int head, int32_t t, floa
                 *reinterpret_cast<uint32_t*>(dst + 32 * b + 8 * g) =
                     e4m3x4(a[b][4 * g] * m, a[b][4 * g + 1] * m, a[b][4 * g + 2] * m, a[b][4 * g + 3] * m);
     }
+}
+
+template <bool kProduce>
+__device__ __forceinline__ void epilogue(const Epi& e, int head, int32_t t, float (&a)[4][16])
+{
+    EpiIn in;
+    if (kProduce) epilogue_load(e, head, t, in);
+    epilogue_run<kProduce>(e, head, t, a, in);
 }
 
 // ------------------------------------------------------------------ split-K kernel (<= 1,024 tokens)
@@ -296,11 +337,12 @@ void project_split_kernel(const SplitArgs a)
     }
 }
 
-// One work-group per (head, chunk, 32-token block): wave w adds, in slice order, the partial sums of
-// feature block w and hands them to wave 0 through LDS; wave 0 holds the head rows and runs the
+// One work-group per (head, chunk, 32-token block).  Waves 0..3 add, in slice order, the partial
+// sums of feature block w and leave them in LDS; meanwhile wave 4 fetches the epilogue's inputs
+// (norm weights, RoPE coefficients, slots), then takes the head rows from LDS and runs the
 // epilogue.
 template <bool kProduce>
-__global__ __launch_bounds__(256) void project_reduce_kernel(const SplitArgs a)
+__global__ __launch_bounds__(320) void project_reduce_kernel(const SplitArgs a)
 {
     __shared__ float xchg[4][16][64];                          // [feature block][i][lane]
     const int lane = threadIdx.x & 63;
@@ -309,45 +351,46 @@ __global__ __launch_bounds__(256) void project_reduce_kernel(const SplitArgs a)
     const int pair = (int)(blockIdx.x >> 1);
     const int tc = pair % a.n_tc;
     const int head = pair / a.n_tc;
-    const f32x4_t* base = reinterpret_cast<const f32x4_t*>(a.part + (int64_t)pair * a.splits * kPartFloats) +
-                          ((wave * 2 + tb) * 4) * 64 + lane;
-    float part[16] = {};
-    for (int s0 = 0; s0 < a.splits; s0 += 8) {
-        f32x4_t v[8][4];
+    const int32_t t = tc * kChunk + tb * 32 + lane % 32;
+    if (wave < 4) {
+        const f32x4_t* base = reinterpret_cast<const f32x4_t*>(a.part + (int64_t)pair * a.splits * kPartFloats) +
+                              ((wave * 2 + tb) * 4) * 64 + lane;
+        float part[16] = {};
+        for (int s0 = 0; s0 < a.splits; s0 += 8) {
+            f32x4_t v[8][4];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int sl = min(s0 + u, a.splits - 1);              // past the last slice: reread it, unused
+            for (int u = 0; u < 8; ++u) {
+                const int sl = min(s0 + u, a.splits - 1);          // past the last slice: reread it, unused
 #pragma unroll
-            for (int q = 0; q < 4; ++q) v[u][q] = base[(int64_t)sl * (kPartFloats / 4) + q * 64];
+                for (int q = 0; q < 4; ++q) v[u][q] = base[(int64_t)sl * (kPartFloats / 4) + q * 64];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const bool live = s0 + u < a.splits, first = s0 + u == 0;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float x = v[u][q][e];
+                        const float sum = first ? x : part[4 * q + e] + x;
+                        part[4 * q + e] = live ? sum : part[4 * q + e];
+                    }
+            }
         }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const bool live = s0 + u < a.splits, first = s0 + u == 0;
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float x = v[u][q][e];
-                    const float sum = first ? x : part[4 * q + e] + x;
-                    part[4 * q + e] = live ? sum : part[4 * q + e];
-                }
-        }
-    }
-    if (wave > 0) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) xchg[wave][i][lane] = part[i];
+        __syncthreads();
+        return;
     }
+    EpiIn in;
+    if (kProduce) epilogue_load(a.e, head, t, in);
     __syncthreads();
-    if (wave > 0) return;
     float acc[4][16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        acc[0][i] = part[i];
-        acc[1][i] = xchg[1][i][lane];
-        acc[2][i] = xchg[2][i][lane];
-        acc[3][i] = xchg[3][i][lane];
-    }
-    epilogue<kProduce>(a.e, head, tc * kChunk + tb * 32 + lane % 32, acc);
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[b][i] = xchg[b][i][lane];
+    epilogue_run<kProduce>(a.e, head, t, acc, in);
 }
 
 // ------------------------------------------------------------------ tiled kernel (prefill)
@@ -371,11 +414,43 @@ __device__ __forceinline__ uint32_t xcd_tile(uint32_t bid, uint32_t total)
     return prefix + (bid >> 3);
 }
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// One 16-byte LDS read, issued as written: the compiler neither reorders it nor makes it wait for
+// the direct global -> LDS loads in flight into the other buffer (it cannot see which buffer an
+// inline read touches).  Completion is awaited explicitly with lgkm_wait below.
+__device__ __forceinline__ u32x4_t lds_read16(uint32_t addr)
+{
+    u32x4_t v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+    return v;
+}
+
+// Waits until at most N LDS reads are in flight; the eight fragments passed are tied to the wait so
+// that no use of them is scheduled above it.
+template <int N>
+__device__ __forceinline__ void lgkm_wait(u32x4_t (&a)[4], u32x4_t (&b)[4])
+{
+    asm volatile("s_waitcnt lgkmcnt(%8)"
+                 : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3])
+                 : "n"(N));
+}
+
+__device__ __forceinline__ f32x16_t mfma4(const u32x4_t& a, const u32x4_t& b, const f32x16_t& c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                    c, 0, 0, 0);
+}
+
 template <bool kProduce>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void project_tile_kernel(const TileArgs a)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][kTile][kPitch];   // [buffer][w | h][row][k]
+    // [buffer][w | h] tiles of 256 rows x 64 columns: each row 8 chunks of 16 B, chunk c of row r at
+    // position c ^ ((r >> 1) & 7) (fragment reads of 32 rows at one chunk are free of bank
+    // conflicts; measured), no padding.
+    constexpr int kTileBytes = kTile * 8 * 16;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kTileBytes];
     const uint32_t L = xcd_tile(blockIdx.x, (uint32_t)(a.n_tt * a.n_tf));
     const int tile_t = (int)(L / (uint32_t)a.n_tf);
     const int tile_f = (int)(L - (uint32_t)tile_t * (uint32_t)a.n_tf);
@@ -386,37 +461,36 @@ void project_tile_kernel(const TileArgs a)
     const int hh = lane >> 5;
     const int f_base = tile_f * kTile, t_base = tile_t * kTile;
 
-    // Global -> LDS: thread `tid` moves 16 B (8 k) at column 8 (tid & 7) of rows (tid >> 3) + 32 j,
-    // j < 8, of the w tile and of the h tile (rows past the matrix read its last row, unused).  Two
-    // named register sets (no private arrays) carry stages two steps ahead of the products: the
-    // loads for stage k + 2 are issued at the start of step k and written to LDS at the end of
-    // step k + 1, so each has two steps of matrix work to arrive.
-    const int r0 = tid >> 3, c8 = (tid & 7) * 8;
-    const uint16_t* wa = a.w + c8;
-    const uint16_t* hb = a.h + c8;
+    // Direct global -> LDS copy of one stage: instruction j of wave w fills slots j * 256 + 64 w +
+    // lane of each tile; slot p holds row p >> 3 and logical chunk (p & 7) ^ ((row >> 1) & 7), the
+    // same chunk for all eight instructions of a thread.  Rows past the matrix read its last row.
+    const int prow = tid >> 3;
+    const int pchunk = (tid & 7) ^ ((tid >> 4) & 7);
+    const uint16_t* ga = a.w + pchunk * 8;
+    const uint16_t* gb = a.h + pchunk * 8;
     const int64_t ws = a.w_stride, hs = a.h_stride;
-#define ROW_A(j) (wa + (int64_t)min(f_base + r0 + 32 * (j), a.N - 1) * ws)
-#define ROW_B(j) (hb + (int64_t)min(t_base + r0 + 32 * (j), a.e.T - 1) * hs)
-    const uint16_t *ga0 = ROW_A(0), *ga1 = ROW_A(1), *ga2 = ROW_A(2), *ga3 = ROW_A(3), *ga4 = ROW_A(4),
-                   *ga5 = ROW_A(5), *ga6 = ROW_A(6), *ga7 = ROW_A(7);
-    const uint16_t *gb0 = ROW_B(0), *gb1 = ROW_B(1), *gb2 = ROW_B(2), *gb3 = ROW_B(3), *gb4 = ROW_B(4),
-                   *gb5 = ROW_B(5), *gb6 = ROW_B(6), *gb7 = ROW_B(7);
-#undef ROW_A
-#undef ROW_B
-#define LD(p, k) (*reinterpret_cast<const uint4*>((p) + (k)))
-#define ST(st, m, j, v) (*reinterpret_cast<uint4*>(&lds[st][m][r0 + 32 * (j)][c8]) = (v))
-#define LOAD_SET(X, k)                                                                                    \
-    X##a0 = LD(ga0, k); X##a1 = LD(ga1, k); X##a2 = LD(ga2, k); X##a3 = LD(ga3, k); X##a4 = LD(ga4, k);     \
-    X##a5 = LD(ga5, k); X##a6 = LD(ga6, k); X##a7 = LD(ga7, k); X##b0 = LD(gb0, k); X##b1 = LD(gb1, k);     \
-    X##b2 = LD(gb2, k); X##b3 = LD(gb3, k); X##b4 = LD(gb4, k); X##b5 = LD(gb5, k); X##b6 = LD(gb6, k);     \
-    X##b7 = LD(gb7, k)
-#define STORE_SET(X, st)                                                                                  \
-    ST(st, 0, 0, X##a0); ST(st, 0, 1, X##a1); ST(st, 0, 2, X##a2); ST(st, 0, 3, X##a3); ST(st, 0, 4, X##a4); \
-    ST(st, 0, 5, X##a5); ST(st, 0, 6, X##a6); ST(st, 0, 7, X##a7); ST(st, 1, 0, X##b0); ST(st, 1, 1, X##b1); \
-    ST(st, 1, 2, X##b2); ST(st, 1, 3, X##b3); ST(st, 1, 4, X##b4); ST(st, 1, 5, X##b5); ST(st, 1, 6, X##b6); \
-    ST(st, 1, 7, X##b7)
-    uint4 Pa0, Pa1, Pa2, Pa3, Pa4, Pa5, Pa6, Pa7, Pb0, Pb1, Pb2, Pb3, Pb4, Pb5, Pb6, Pb7;
-    uint4 Qa0, Qa1, Qa2, Qa3, Qa4, Qa5, Qa6, Qa7, Qb0, Qb1, Qb2, Qb3, Qb4, Qb5, Qb6, Qb7;
+    auto dma_stage = [&](int st, int k0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint16_t* pa = ga + (int64_t)min(f_base + prow + 32 * j, a.N - 1) * ws + k0;
+            const uint16_t* pb = gb + (int64_t)min(t_base + prow + 32 * j, a.e.T - 1) * hs + k0;
+            __builtin_amdgcn_global_load_lds(pa, (lds_void*)(&lds[st][0][(j * 256 + wave * 64) * 16]), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(pb, (lds_void*)(&lds[st][1][(j * 256 + wave * 64) * 16]), 16, 0, 0);
+        }
+    };
+    // LDS byte addresses of this lane's fragments: row block b (or token block tb), 16-column step ks.
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)&lds[0][0][0];
+    auto frag_addr = [&](int st, int m, int row, int ks) {
+        const int chunk = 2 * ks + hh;
+        return lds0 + (uint32_t)(((st * 2 + m) * kTileBytes) + (row * 8 + (chunk ^ ((row >> 1) & 7))) * 16);
+    };
+    const int arow = wf * 128 + (lane & 31), brow = wt * 128 + (lane & 31);
+    auto read_frags = [&](int st, int ks, u32x4_t (&af)[4], u32x4_t (&bf)[4]) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) af[b] = lds_read16(frag_addr(st, 0, arow + b * 32, ks));
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) bf[tb] = lds_read16(frag_addr(st, 1, brow + tb * 32, ks));
+    };
 
     f32x16_t acc[4][4];
 #pragma unroll
@@ -424,50 +498,45 @@ void project_tile_kernel(const TileArgs a)
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) acc[b][tb] = f32x16_t{};
 
-    // The products of the stage in LDS buffer st.
-    auto compute = [&](int st) {
-#pragma unroll
-        for (int ks = 0; ks < kBK / 16; ++ks) {
-            uint4 af[4], bf[4];
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-                af[b] = *reinterpret_cast<const uint4*>(&lds[st][0][wf * 128 + b * 32 + (lane & 31)][ks * 16 + 8 * hh]);
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
-                bf[tb] = *reinterpret_cast<const uint4*>(&lds[st][1][wt * 128 + tb * 32 + (lane & 31)][ks * 16 + 8 * hh]);
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-#pragma unroll
-                for (int tb = 0; tb < 4; ++tb) acc[b][tb] = mfma(af[b], bf[tb], acc[b][tb]);
-        }
-    };
-
     const int nk = a.K / kBK;
-    const int last = (nk - 1) * kBK;
-    LOAD_SET(P, 0);
-    STORE_SET(P, 0);
-    LOAD_SET(Q, min(kBK, last));                                  // stage 1 waits in Q
+    dma_stage(0, 0);
+    __builtin_amdgcn_s_waitcnt(0x3f70);                          // vmcnt(0)
     __syncthreads();
-    // Step k: buffer k & 1 holds stage k; the other set holds stage k + 1.  Loads past the last
-    // stage re-read it (unused), keeping every load and LDS write unconditional.
-    int kt = 0;
-    for (; kt + 1 < nk; kt += 2) {
-        LOAD_SET(P, min((kt + 2) * kBK, last));
-        __builtin_amdgcn_sched_group_barrier(0x020, 16, 0);      // the 16 global loads first
-        compute(0);
-        STORE_SET(Q, 1);
-        __syncthreads();
-        LOAD_SET(Q, min((kt + 3) * kBK, last));
-        __builtin_amdgcn_sched_group_barrier(0x020, 16, 0);
-        compute(1);
-        STORE_SET(P, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+        const int s = kt & 1;
+        // The next stage into the other buffer (every wave finished reading it before the barrier
+        // that ended the previous step; the last step reloads its own columns there, unused).
+        dma_stage(s ^ 1, (kt + 1 < nk ? kt + 1 : kt) * kBK);
+        // Fragments one 16-column step ahead of the products.
+        u32x4_t a0[4], b0[4], a1[4], b1[4];
+        read_frags(s, 0, a0, b0);
+        read_frags(s, 1, a1, b1);
+        lgkm_wait<8>(a0, b0);
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) acc[b][tb] = mfma4(a0[b], b0[tb], acc[b][tb]);
+        read_frags(s, 2, a0, b0);
+        lgkm_wait<8>(a1, b1);
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) acc[b][tb] = mfma4(a1[b], b1[tb], acc[b][tb]);
+        read_frags(s, 3, a1, b1);
+        lgkm_wait<8>(a0, b0);
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) acc[b][tb] = mfma4(a0[b], b0[tb], acc[b][tb]);
+        lgkm_wait<0>(a1, b1);
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) acc[b][tb] = mfma4(a1[b], b1[tb], acc[b][tb]);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0x3f70);                      // vmcnt(0): this wave's share landed
         __syncthreads();
     }
-    if (kt < nk) compute(0);                                      // odd number of stages: the last one
-#undef LD
-#undef ST
-#undef LOAD_SET
-#undef STORE_SET
 
     const int head = tile_f * 2 + wf;
     if (head >= a.heads) return;
@@ -547,7 +616,7 @@ msa_status launch_projection(const uint16_t* h, int64_t h_row_stride, int32_t T,
                               dim3(256), args, 0, s);
         if (err == hipSuccess)
             err = hipLaunchKernel(reinterpret_cast<const void*>(&project_reduce_kernel<kProduce>),
-                                  dim3((unsigned)(pairs * 2)), dim3(256), args, 0, s);
+                                  dim3((unsigned)(pairs * 2)), dim3(320), args, 0, s);
     } else {
         TileArgs a;
         a.h = h;
