@@ -19,14 +19,17 @@
 //                          head's features against the chunk; partial sums go to the workspace.
 //   project_reduce_kernel  one work-group per (head, chunk, 32-token block): four waves add the
 //                          slices' partial sums in slice order (the same order on every call) while
-//                          a fifth fetches the epilogue's inputs, then runs the epilogue.  The kernel boundary between the two makes the partial sums
-//                          visible across XCDs; no device-scope fence is needed.
-//   project_tile_kernel    larger batches: 256 features (2 heads) x 256 tokens per work-group, four
-//                          waves of one head x 128 tokens each, 64-wide K steps through two LDS
-//                          buffers (row pitch 144 bytes: conflict-free 16-byte fragment reads),
-//                          with the global loads of each stage issued two steps ahead, and the tile
-//                          order chosen so that the work-groups of one XCD walk the feature tiles of
-//                          the same token rows (their h panel stays in that XCD's L2).
+//                          a fifth fetches the epilogue's inputs, then runs the epilogue.  The
+//                          kernel boundary between the two makes the partial sums visible across
+//                          XCDs; no device-scope fence is needed.
+//   project_tile_kernel    larger batches: 256 features (2 heads) x 256 tokens per work-group, eight
+//                          waves (two per SIMD) of one head x 64 tokens each, 64-wide K steps
+//                          through two LDS buffers filled by direct global -> LDS loads one step
+//                          ahead, fragments read one 16-column step ahead of the products.  The
+//                          output rows leave through LDS so that each store writes whole rows, and
+//                          the tile order is chosen so that the work-groups of one XCD walk the
+//                          feature tiles of the same token rows (their h panel stays in that XCD's
+//                          L2).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -50,7 +53,6 @@ constexpr int kChunk = 64;                 // tokens per split-K work-group (two
 constexpr int kPartFloats = 4 * 2 * 4 * 64 * 4;   // one work-group's partial sums: [wave][tb][q][lane][4]
 constexpr int kTile = 256;                 // tiled kernel: features and tokens per work-group
 constexpr int kBK = 64;                    // K per pipeline stage
-constexpr int kPitch = 72;                 // LDS row pitch in bf16 elements (144 B)
 constexpr uint64_t kAlign = 256;
 constexpr int kSliceMax = 384;             // split-K: K per slice at most (LDS: (128 + 64) rows x 384 bf16)
 constexpr int kSplitLds = (128 + kChunk) * kSliceMax * 2;
@@ -129,14 +131,23 @@ __device__ __forceinline__ void epilogue_load(const Epi& e, int head, int32_t t,
         }
 }
 
+// Where one token's head row goes: dst == nullptr means nowhere (a token past T, or a cache row
+// without a valid slot); fp8 rows are 128 bytes (e4m3 of value * m), the others 256 bytes of bf16.
+struct RowOut {
+    uint8_t* dst;
+    bool fp8;
+    float m;
+};
+
 // One head's row for one token per lane pair: a[b][i] is feature 32 b + 8 (i / 4) + 4 hh + i % 4
-// (hh = lane / 32) of `head`, token t.  Rounds the row to bf16 (the packed row's values), then
-// either stores it (plain) or runs the producer arithmetic on it with the inputs `in`.
-template <bool kProduce>
-__device__ __forceinline__ void epilogue_run(const Epi& e, int head, int32_t t, float (&a)[4][16], const EpiIn& in)
+// (hh = lane / 32) of `head`, token t.  Rounds the row to bf16 (the packed row's values), then, in
+// produce mode, runs the producer arithmetic on it; returns the row's destination.  The norm
+// weights, RoPE coefficients and slot come from `in` (kInline false: fetched ahead by
+// epilogue_load) or are loaded here where they are used (kInline true: fewer live registers).
+template <bool kProduce, bool kInline>
+__device__ __forceinline__ RowOut epilogue_math(const Epi& e, int head, int32_t t, float (&a)[4][16], const EpiIn& in)
 {
-    const int lane = threadIdx.x & 63;
-    const int hh = lane >> 5;
+    const int hh = (threadIdx.x & 63) >> 5;
     const bool tok = t < e.T;
 #pragma unroll
     for (int b = 0; b < 4; ++b)
@@ -146,20 +157,19 @@ __device__ __forceinline__ void epilogue_run(const Epi& e, int head, int32_t t, 
             a[b][2 * j] = bf16_lo(w);
             a[b][2 * j + 1] = bf16_hi(w);
         }
+    RowOut o{nullptr, false, 1.0f};
     if (!kProduce) {
-        if (!tok) return;
-        uint16_t* dst = e.x_out + (int64_t)t * e.x_stride + head * kHeadDim + 4 * hh;
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-                *reinterpret_cast<uint2*>(dst + 32 * b + 8 * g) =
-                    make_uint2(bf16x2(a[b][4 * g], a[b][4 * g + 1]), bf16x2(a[b][4 * g + 2], a[b][4 * g + 3]));
-        return;
+        if (tok) o.dst = reinterpret_cast<uint8_t*>(e.x_out + (int64_t)t * e.x_stride + head * kHeadDim);
+        return o;
     }
 
     const int h_k = e.hq, h_v = e.hq + e.hkv, h_iq = e.hq + 2 * e.hkv, h_ik = h_iq + e.hiq;
     const int st = stream_of(e, head);
+    const bool cache_row = st == kK || st == kV || st == kIK;
+    const CacheDev& cd = e.cache[st == kK ? 0 : st == kV ? 1 : 2];
+    // The row format depends on the head only, so it is uniform over the wave (row_store_staged
+    // relies on it), whatever the token.
+    o.fp8 = cache_row && !cd.is_bf16;
     if (st != kV) {
         // RMSNorm: binary64 sum of squares over the lane's 64 features plus the partner lane's.
         double ss = 0.0;
@@ -169,67 +179,136 @@ __device__ __forceinline__ void epilogue_run(const Epi& e, int head, int32_t t, 
             for (int i = 0; i < 16; ++i) ss = __builtin_fma((double)a[b][i], (double)a[b][i], ss);
         ss += __shfl_xor(ss, 32);
         const float r = rms_from_ss(ss, e.eps);
+        const uint16_t* wp = e.w[st == kQ ? 0 : st == kK ? 1 : st == kIQ ? 2 : 3] + 4 * hh;
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) a[b][i] = (a[b][i] * r) * in.w[b][i];
+            for (int g = 0; g < 4; ++g) {
+                float w4[4];
+                if (kInline) {
+                    const uint2 wv = *reinterpret_cast<const uint2*>(wp + 32 * b + 8 * g);
+                    w4[0] = bf16_lo(wv.x); w4[1] = bf16_hi(wv.x); w4[2] = bf16_lo(wv.y); w4[3] = bf16_hi(wv.y);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) w4[q] = in.w[b][4 * g + q];
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) a[b][4 * g + q] = (a[b][4 * g + q] * r) * w4[q];
+            }
         // RoPE, neox rotate-half: frequency f < 64 pairs feature f (block b) with f + 64 (block b + 2).
+        const int32_t tl = tok ? t : e.T - 1;
+        const float* cp = e.cos + (int64_t)tl * kHalf + 4 * hh;
+        const float* sp = e.sin + (int64_t)tl * kHalf + 4 * hh;
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float y0 = a[b][i], y1 = a[b + 2][i];
-                a[b][i] = y0 * in.c[b][i] - y1 * in.s[b][i];
-                a[b + 2][i] = y1 * in.c[b][i] + y0 * in.s[b][i];
+            for (int g = 0; g < 4; ++g) {
+                float c[4], sn[4];
+                if (kInline) {
+                    const float4 c4 = *reinterpret_cast<const float4*>(cp + 32 * b + 8 * g);
+                    const float4 s4 = *reinterpret_cast<const float4*>(sp + 32 * b + 8 * g);
+                    c[0] = c4.x; c[1] = c4.y; c[2] = c4.z; c[3] = c4.w;
+                    sn[0] = s4.x; sn[1] = s4.y; sn[2] = s4.z; sn[3] = s4.w;
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) { c[q] = in.c[b][4 * g + q]; sn[q] = in.s[b][4 * g + q]; }
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int i = 4 * g + q;
+                    const float y0 = a[b][i], y1 = a[b + 2][i];
+                    a[b][i] = y0 * c[q] - y1 * sn[q];
+                    a[b + 2][i] = y1 * c[q] + y0 * sn[q];
+                }
             }
     }
-    if (!tok) return;
+    if (!tok) return o;
     if (st == kQ || st == kIQ) {
-        uint16_t* dst = (st == kQ ? e.q_out + ((int64_t)t * e.hq + head) * kHeadDim
-                                  : e.iq_out + ((int64_t)t * e.hiq + (head - h_iq)) * kHeadDim) + 4 * hh;
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-                *reinterpret_cast<uint2*>(dst + 32 * b + 8 * g) =
-                    make_uint2(bf16x2(a[b][4 * g], a[b][4 * g + 1]), bf16x2(a[b][4 * g + 2], a[b][4 * g + 3]));
-        return;
+        o.dst = reinterpret_cast<uint8_t*>(st == kQ ? e.q_out + ((int64_t)t * e.hq + head) * kHeadDim
+                                                    : e.iq_out + ((int64_t)t * e.hiq + (head - h_iq)) * kHeadDim);
+        return o;
     }
-    const int64_t slot = in.slot;
-    if (slot < 0) return;
+    const int64_t slot = kInline ? e.slots[t] : in.slot;
+    if (slot < 0) return o;
     const int64_t page = slot / e.page_size;
-    if (page >= e.num_pages) return;
+    if (page >= e.num_pages) return o;
     const int64_t off = slot - page * e.page_size;
-    const int ci = st == kK ? 0 : st == kV ? 1 : 2;
     const int hl = st == kK ? head - h_k : st == kV ? head - h_v : head - h_ik;
-    const CacheDev& cd = e.cache[ci];
-    const int64_t base = page * cd.sp + off * cd.st + (int64_t)hl * cd.sh + 4 * hh;
-    if (cd.is_bf16) {
-        uint16_t* dst = reinterpret_cast<uint16_t*>(cd.data) + base;
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-                *reinterpret_cast<uint2*>(dst + 32 * b + 8 * g) =
-                    make_uint2(bf16x2(a[b][4 * g], a[b][4 * g + 1]), bf16x2(a[b][4 * g + 2], a[b][4 * g + 3]));
-    } else {
-        const float m = inv_scale_of(cd.scale);
-        uint8_t* dst = cd.data + base;
+    const int64_t elem = page * cd.sp + off * cd.st + (int64_t)hl * cd.sh;
+    o.dst = cd.data + (o.fp8 ? elem : 2 * elem);
+    if (o.fp8) o.m = inv_scale_of(cd.scale);
+    return o;
+}
+
+// Stores the row of epilogue_math from each lane's registers (lane l holds 16 of the row's features
+// in four 4-feature groups per 32-feature block).
+__device__ __forceinline__ void row_store_direct(const RowOut& o, const float (&a)[4][16])
+{
+    if (o.dst == nullptr) return;
+    const int hh = (threadIdx.x & 63) >> 5;
+    if (o.fp8) {
+        uint8_t* dst = o.dst + 4 * hh;
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
             for (int g = 0; g < 4; ++g)
                 *reinterpret_cast<uint32_t*>(dst + 32 * b + 8 * g) =
-                    e4m3x4(a[b][4 * g] * m, a[b][4 * g + 1] * m, a[b][4 * g + 2] * m, a[b][4 * g + 3] * m);
+                    e4m3x4(a[b][4 * g] * o.m, a[b][4 * g + 1] * o.m, a[b][4 * g + 2] * o.m, a[b][4 * g + 3] * o.m);
+    } else {
+        uint16_t* dst = reinterpret_cast<uint16_t*>(o.dst) + 4 * hh;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *reinterpret_cast<uint2*>(dst + 32 * b + 8 * g) =
+                    make_uint2(bf16x2(a[b][4 * g], a[b][4 * g + 1]), bf16x2(a[b][4 * g + 2], a[b][4 * g + 3]));
     }
 }
 
-template <bool kProduce>
-__device__ __forceinline__ void epilogue(const Epi& e, int head, int32_t t, float (&a)[4][16])
+// Stores the rows of a 32-token block (lane l holds part of token l % 32's row, as above) through
+// this wave's 8 KiB of LDS: every lane first writes its pieces into the row-major block, then each
+// lane stores 16 contiguous bytes of one row, so that a store instruction writes whole rows.  In
+// the staging block the 16-byte chunk c of row r sits at position c ^ (r & 15) (256-byte rows) or
+// c ^ (r & 7) (128-byte rows).  o.fp8 must be uniform over the wave (one head): every lane takes
+// part in storing every row of the block.
+__device__ __forceinline__ void row_store_staged(const RowOut& o, const float (&a)[4][16], uint8_t* stage)
 {
-    EpiIn in;
-    if (kProduce) epilogue_load(e, head, t, in);
-    epilogue_run<kProduce>(e, head, t, a, in);
+    const int lane = threadIdx.x & 63;
+    const int hh = lane >> 5, r = lane & 31;
+    const uint32_t dlo = (uint32_t)reinterpret_cast<uintptr_t>(o.dst);
+    const uint32_t dhi = (uint32_t)(reinterpret_cast<uintptr_t>(o.dst) >> 32);
+    if (o.fp8) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *reinterpret_cast<uint32_t*>(stage + r * 128 + (((2 * b + (g >> 1)) ^ (r & 7)) * 16) + (g & 1) * 8 + 4 * hh) =
+                    e4m3x4(a[b][4 * g] * o.m, a[b][4 * g + 1] * o.m, a[b][4 * g + 2] * o.m, a[b][4 * g + 3] * o.m);
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rr = 8 * i + (lane >> 3), c = lane & 7;
+            const uint4 v = *reinterpret_cast<const uint4*>(stage + rr * 128 + ((c ^ (rr & 7)) * 16));
+            const uintptr_t d = ((uintptr_t)(uint32_t)__shfl((int)dhi, rr) << 32) | (uint32_t)__shfl((int)dlo, rr);
+            if (d != 0) *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(d) + c * 16) = v;
+        }
+    } else {
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *reinterpret_cast<uint2*>(stage + r * 256 + (((4 * b + g) ^ (r & 15)) * 16) + 8 * hh) =
+                    make_uint2(bf16x2(a[b][4 * g], a[b][4 * g + 1]), bf16x2(a[b][4 * g + 2], a[b][4 * g + 3]));
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int rr = 4 * i + (lane >> 4), c = lane & 15;
+            const uint4 v = *reinterpret_cast<const uint4*>(stage + rr * 256 + ((c ^ (rr & 15)) * 16));
+            const uintptr_t d = ((uintptr_t)(uint32_t)__shfl((int)dhi, rr) << 32) | (uint32_t)__shfl((int)dlo, rr);
+            if (d != 0) *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(d) + c * 16) = v;
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
 }
 
 // ------------------------------------------------------------------ split-K kernel (<= 1,024 tokens)
@@ -390,7 +469,8 @@ __global__ __launch_bounds__(320) void project_reduce_kernel(const SplitArgs a)
     for (int b = 0; b < 4; ++b)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[b][i] = xchg[b][i][lane];
-    epilogue_run<kProduce>(a.e, head, t, acc, in);
+    const RowOut o = epilogue_math<kProduce, false>(a.e, head, t, acc, in);
+    row_store_direct(o, acc);
 }
 
 // ------------------------------------------------------------------ tiled kernel (prefill)
@@ -426,13 +506,13 @@ __device__ __forceinline__ u32x4_t lds_read16(uint32_t addr)
     return v;
 }
 
-// Waits until at most N LDS reads are in flight; the eight fragments passed are tied to the wait so
+// Waits until at most N LDS reads are in flight; the six fragments passed are tied to the wait so
 // that no use of them is scheduled above it.
 template <int N>
-__device__ __forceinline__ void lgkm_wait(u32x4_t (&a)[4], u32x4_t (&b)[4])
+__device__ __forceinline__ void lgkm_wait(u32x4_t (&a)[4], u32x4_t (&b)[2])
 {
-    asm volatile("s_waitcnt lgkmcnt(%8)"
-                 : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3])
+    asm volatile("s_waitcnt lgkmcnt(%6)"
+                 : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1])
                  : "n"(N));
 }
 
@@ -443,27 +523,27 @@ __device__ __forceinline__ f32x16_t mfma4(const u32x4_t& a, const u32x4_t& b, co
 }
 
 template <bool kProduce>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void project_tile_kernel(const TileArgs a)
 {
-    // [buffer][w | h] tiles of 256 rows x 64 columns: each row 8 chunks of 16 B, chunk c of row r at
+    // [buffer][w | h] stages of 256 rows x 64 columns: each row 8 chunks of 16 B, chunk c of row r at
     // position c ^ ((r >> 1) & 7) (fragment reads of 32 rows at one chunk are free of bank
-    // conflicts; measured), no padding.
-    constexpr int kTileBytes = kTile * 8 * 16;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kTileBytes];
+    // conflicts; measured), no padding.  After the last step the same memory stages the output rows.
+    constexpr int kStageBytes = kTile * 8 * 16;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kStageBytes];
     const uint32_t L = xcd_tile(blockIdx.x, (uint32_t)(a.n_tt * a.n_tf));
     const int tile_t = (int)(L / (uint32_t)a.n_tf);
     const int tile_f = (int)(L - (uint32_t)tile_t * (uint32_t)a.n_tf);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wf = wave & 1, wt = wave >> 1;
+    const int wf = wave & 1, wt = wave >> 1;                  // head of the tile, 64-token slab
     const int hh = lane >> 5;
     const int f_base = tile_f * kTile, t_base = tile_t * kTile;
 
-    // Direct global -> LDS copy of one stage: instruction j of wave w fills slots j * 256 + 64 w +
-    // lane of each tile; slot p holds row p >> 3 and logical chunk (p & 7) ^ ((row >> 1) & 7), the
-    // same chunk for all eight instructions of a thread.  Rows past the matrix read its last row.
+    // Direct global -> LDS copy of one stage: instruction j of wave w fills slots j * 512 + 64 w +
+    // lane of each operand; slot p holds row p >> 3 and logical chunk (p & 7) ^ ((row >> 1) & 7),
+    // the same chunk for all four instructions of a thread.  Rows past the matrix read its last row.
     const int prow = tid >> 3;
     const int pchunk = (tid & 7) ^ ((tid >> 4) & 7);
     const uint16_t* ga = a.w + pchunk * 8;
@@ -471,32 +551,32 @@ void project_tile_kernel(const TileArgs a)
     const int64_t ws = a.w_stride, hs = a.h_stride;
     auto dma_stage = [&](int st, int k0) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint16_t* pa = ga + (int64_t)min(f_base + prow + 32 * j, a.N - 1) * ws + k0;
-            const uint16_t* pb = gb + (int64_t)min(t_base + prow + 32 * j, a.e.T - 1) * hs + k0;
-            __builtin_amdgcn_global_load_lds(pa, (lds_void*)(&lds[st][0][(j * 256 + wave * 64) * 16]), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(pb, (lds_void*)(&lds[st][1][(j * 256 + wave * 64) * 16]), 16, 0, 0);
+        for (int j = 0; j < 4; ++j) {
+            const uint16_t* pa = ga + (int64_t)min(f_base + prow + 64 * j, a.N - 1) * ws + k0;
+            const uint16_t* pb = gb + (int64_t)min(t_base + prow + 64 * j, a.e.T - 1) * hs + k0;
+            __builtin_amdgcn_global_load_lds(pa, (lds_void*)(&lds[st][0][(j * 512 + wave * 64) * 16]), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(pb, (lds_void*)(&lds[st][1][(j * 512 + wave * 64) * 16]), 16, 0, 0);
         }
     };
-    // LDS byte addresses of this lane's fragments: row block b (or token block tb), 16-column step ks.
+    // LDS byte addresses of this lane's fragments: feature block b (or token block tb), 16-column step ks.
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)&lds[0][0][0];
     auto frag_addr = [&](int st, int m, int row, int ks) {
         const int chunk = 2 * ks + hh;
-        return lds0 + (uint32_t)(((st * 2 + m) * kTileBytes) + (row * 8 + (chunk ^ ((row >> 1) & 7))) * 16);
+        return lds0 + (uint32_t)(((st * 2 + m) * kStageBytes) + (row * 8 + (chunk ^ ((row >> 1) & 7))) * 16);
     };
-    const int arow = wf * 128 + (lane & 31), brow = wt * 128 + (lane & 31);
-    auto read_frags = [&](int st, int ks, u32x4_t (&af)[4], u32x4_t (&bf)[4]) {
+    const int arow = wf * 128 + (lane & 31), brow = wt * 64 + (lane & 31);
+    auto read_frags = [&](int st, int ks, u32x4_t (&af)[4], u32x4_t (&bf)[2]) {
 #pragma unroll
         for (int b = 0; b < 4; ++b) af[b] = lds_read16(frag_addr(st, 0, arow + b * 32, ks));
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) bf[tb] = lds_read16(frag_addr(st, 1, brow + tb * 32, ks));
+        for (int tb = 0; tb < 2; ++tb) bf[tb] = lds_read16(frag_addr(st, 1, brow + tb * 32, ks));
     };
 
-    f32x16_t acc[4][4];
+    f32x16_t acc[4][2];
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) acc[b][tb] = f32x16_t{};
+        for (int tb = 0; tb < 2; ++tb) acc[b][tb] = f32x16_t{};
 
     const int nk = a.K / kBK;
     dma_stage(0, 0);
@@ -508,46 +588,52 @@ void project_tile_kernel(const TileArgs a)
         // that ended the previous step; the last step reloads its own columns there, unused).
         dma_stage(s ^ 1, (kt + 1 < nk ? kt + 1 : kt) * kBK);
         // Fragments one 16-column step ahead of the products.
-        u32x4_t a0[4], b0[4], a1[4], b1[4];
+        u32x4_t a0[4], b0[2], a1[4], b1[2];
         read_frags(s, 0, a0, b0);
         read_frags(s, 1, a1, b1);
-        lgkm_wait<8>(a0, b0);
+        lgkm_wait<6>(a0, b0);
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) acc[b][tb] = mfma4(a0[b], b0[tb], acc[b][tb]);
+            for (int tb = 0; tb < 2; ++tb) acc[b][tb] = mfma4(a0[b], b0[tb], acc[b][tb]);
         read_frags(s, 2, a0, b0);
-        lgkm_wait<8>(a1, b1);
+        lgkm_wait<6>(a1, b1);
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) acc[b][tb] = mfma4(a1[b], b1[tb], acc[b][tb]);
+            for (int tb = 0; tb < 2; ++tb) acc[b][tb] = mfma4(a1[b], b1[tb], acc[b][tb]);
         read_frags(s, 3, a1, b1);
-        lgkm_wait<8>(a0, b0);
+        lgkm_wait<6>(a0, b0);
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) acc[b][tb] = mfma4(a0[b], b0[tb], acc[b][tb]);
+            for (int tb = 0; tb < 2; ++tb) acc[b][tb] = mfma4(a0[b], b0[tb], acc[b][tb]);
         lgkm_wait<0>(a1, b1);
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) acc[b][tb] = mfma4(a1[b], b1[tb], acc[b][tb]);
+            for (int tb = 0; tb < 2; ++tb) acc[b][tb] = mfma4(a1[b], b1[tb], acc[b][tb]);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(0x3f70);                      // vmcnt(0): this wave's share landed
         __syncthreads();
     }
 
+    // Every wave has finished reading the stages (the barrier above) and the last copies have landed:
+    // the first 8 KiB per wave now stage its output rows.
     const int head = tile_f * 2 + wf;
     if (head >= a.heads) return;
+    uint8_t* stage = &lds[0][0][0] + wave * 8192;
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
+    for (int tb = 0; tb < 2; ++tb) {
         float v[4][16];
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
             for (int i = 0; i < 16; ++i) v[b][i] = acc[b][tb][i];
-        epilogue<kProduce>(a.e, head, t_base + wt * 128 + tb * 32 + (lane & 31), v);
+        const int32_t t = t_base + wt * 64 + tb * 32 + (lane & 31);
+        EpiIn unused;
+        const RowOut o = epilogue_math<kProduce, true>(a.e, head, t, v, unused);
+        row_store_staged(o, v, stage);
     }
 }
 
@@ -631,7 +717,7 @@ msa_status launch_projection(const uint16_t* h, int64_t h_row_stride, int32_t T,
         a.e = e;
         void* args[] = {&a};
         const dim3 grid((unsigned)((int64_t)a.n_tt * a.n_tf));
-        err = hipLaunchKernel(reinterpret_cast<const void*>(&project_tile_kernel<kProduce>), grid, dim3(256), args, 0,
+        err = hipLaunchKernel(reinterpret_cast<const void*>(&project_tile_kernel<kProduce>), grid, dim3(512), args, 0,
                               s);
     }
     return err == hipSuccess ? MSA_OK : MSA_ERR_LAUNCH;
