@@ -196,6 +196,56 @@ def test_project_produce_normal(name):
     assert min(fr) >= 0.95
 
 
+def test_project_produce_prefill_65536_sampled():
+    """The 65,536-token prefill chunk in the launch configuration the bench times (one tiled launch;
+    h ~ N(0, 1), w ~ N(0, 1/hidden)): on the device the fused outputs equal msa_project followed by
+    msa_produce everywhere; against the oracle's projection and producer on sampled tokens (tile
+    edges, chunk edges, the last token, random ones) at the normal-input bars."""
+    wl = W.config3()
+    h, w = W.with_projection(wl, seed=1)
+    T, K = h.shape
+    say(f"[gpu] msa_project_produce prefill T={T} W={wl.W} K={K}")
+    d = fused(wl, h, w)
+    d2 = W.to_device(wl)
+    x = torch.empty((T, wl.W), dtype=torch.int16, device="cuda")
+    msa.msa_project(dev16(h), dev16(w), x, workspace=workspace(T, K, wl.W // 128))
+    msa.msa_produce(x, d2.positions, d2.seq_idx, d2.page_table, *d2.weights, d2.q_out, d2.iq_out, d2.caches[0],
+                    d2.caches[1], d2.caches[2], k_scale=d2.scales[0], v_scale=d2.scales[1], ik_scale=d2.scales[2],
+                    num_pages=wl.num_pages, rms_eps=wl.eps, rope_theta=wl.theta)
+    torch.cuda.synchronize()
+    assert torch.equal(d.q_out, d2.q_out) and torch.equal(d.iq_out, d2.iq_out)
+    for a, b in zip(d.storages, d2.storages):
+        assert (a is None and b is None) or torch.equal(a, b)
+    del d2, x
+    torch.cuda.empty_cache()
+
+    rng = np.random.default_rng(65536)
+    edges = [0, 1, 31, 32, 63, 64, 255, 256, 257, 511, 512, 8191, 8192, 32767, 32768, 65279, 65280, 65535]
+    S = np.unique(np.concatenate([edges, rng.choice(T, 46, replace=False)])).astype(np.int64)
+    xs = oracle.project(h[S], w, num_threads=THREADS)
+    ref = oracle.produce_rows(xs, wl.W, S.size, wl.head_dim, wl.hq, wl.hkv, wl.hiq, wl.hik,
+                              np.ascontiguousarray(wl.positions[S]), np.ascontiguousarray(wl.seq_idx[S]),
+                              wl.page_table, wl.max_pages, wl.num_seqs, wl.max_pages, wl.page_size, wl.num_pages,
+                              *wl.weights, wl.eps, wl.theta, dtypes=[c.dtype for c in wl.caches],
+                              scales=[c.scale for c in wl.caches], num_threads=THREADS)
+    St = torch.from_numpy(S).cuda()
+    np.testing.assert_array_equal(d.slots[St].cpu().numpy(), ref["slots"])
+    fr = [_close_rows("q", H.bf16_bits_to_f32(d.q_out[St].cpu().numpy().view(np.uint16)),
+                      H.bf16_bits_to_f32(ref["q"]), 2.0 ** -6),
+          _close_rows("iq", H.bf16_bits_to_f32(d.iq_out[St].cpu().numpy().view(np.uint16)),
+                      H.bf16_bits_to_f32(ref["iq"]), 2.0 ** -6)]
+    valid = np.flatnonzero(ref["slots"] >= 0)
+    assert valid.size == S.size
+    pg = torch.from_numpy(ref["slots"][valid] // wl.page_size).cuda()
+    off = torch.from_numpy(ref["slots"][valid] % wl.page_size).cuda()
+    for nm, spec, view in zip(("k", "v", "ik"), wl.caches, d.caches):
+        rows = view[pg, :, off, :].cpu().numpy()
+        assert spec.dtype == W.FP8_E4M3
+        fr.append(_close_rows(nm, H.e4m3_decode(rows.view(np.uint8)), H.e4m3_decode(ref[nm][valid]), 2.0 ** -3))
+    say(f"  {S.size} sampled tokens; identical rows vs the oracle: " + ", ".join(f"{100 * f:.2f}%" for f in fr))
+    assert min(fr) >= 0.95
+
+
 def test_workspace_contents_do_not_matter():
     """Two decode calls on one workspace, the second after the outputs are cleared and the workspace
     is filled with garbage: both write the same bytes."""
