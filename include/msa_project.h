@@ -20,7 +20,7 @@
  * index-K into the paged caches.  Its outputs equal msa_produce applied to msa_project's x, except
  * where a head's binary64 sum of squares is inexact (a head spanning more than about 2^15 in
  * magnitude), where the two sum orders may differ in the last binary64 bit.  The packed row never
- * touches memory.  The pages fuse only up to "one wider GEMM" feeding "one fused producer"; this
+ * touches memory.  The pages stop at a single wider GEMM feeding a separate fused producer; this
  * entry point goes one step further.
  *
  * Kernels: for up to 1,024 tokens (the decode and verify batches) two launches, a split-K kernel

@@ -3,10 +3,11 @@
 This module only draws inputs; it contains none of the producer's arithmetic.
 Both the HIP path (tests, benchmark) and the CPU oracle consume what it returns.
 
-The workloads stand in for the serving workload the pages measure on ("random
-8k/1k" input/output lengths at concurrency 32/64 in "Fuse MiniMax-M3 MSA
-per-layer KV-cache writes into one kernel", "Measured impact"; 8K/1K at
-concurrency 256 in "Fuse MiniMax-M3 QKV and index projection", "Performance"):
+The workloads stand in for the serving workload the pages measure on (random
+prompts of about 8k input and 1k output tokens at concurrency 32/64 in "Fuse
+MiniMax-M3 MSA per-layer KV-cache writes into one kernel", "Measured impact";
+8K input / 1K output at concurrency 256 in "Fuse MiniMax-M3 QKV and index
+projection", "Performance"):
 decode positions around 8k context, batches of 64 and 256, 8192-token prefill
 chunks, and a mixed prefill+decode batch whose cache pool needs 64-bit offsets.
 
