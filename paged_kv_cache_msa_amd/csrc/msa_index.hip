@@ -141,10 +141,13 @@ __device__ __forceinline__ void decode_key(const KeyRaw<kBf16>& r, double* k)
 // key, then the arithmetic, so a wave waits on two memory round trips per batch, not two per step.
 // kStepInPage: page_size and block_tokens are multiples of 8, so the 8 keys of a step always share
 // one page: the page lookup and the 64-bit page base are then wave-uniform (scalar) per step.
+// Four waves per SIMD (at most 128 registers, no spills): batches of 4 steps (2 with bf16 keys,
+// whose raw rows are twice as wide) are the deepest that fit; measured 3% faster than 3 waves with
+// batches of 8.
 template <int NH, bool kBf16, bool kStepInPage>
-__global__ __launch_bounds__(kBlock) void index_scores_kernel(const ScoreArgs a)
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void index_scores_kernel(const ScoreArgs a)
 {
-    constexpr int BATCH = 8;
+    constexpr int BATCH = kBf16 ? 2 : 4;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const uint32_t item = blockIdx.x * kWavesPerBlock + wave;
