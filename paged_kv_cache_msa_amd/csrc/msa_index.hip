@@ -243,49 +243,51 @@ __device__ __forceinline__ bool before(double s1, int32_t i1, double s2, int32_t
     return s1 > s2 || (s1 == s2 && i1 < i2);
 }
 
-// Rows of up to kRankRowBlocks blocks: one wavefront per row stages the row in LDS, and every lane
-// computes the rank of each of its candidates (how many candidates are ordered before it); a
+// Rows of up to kRankRowBlocks blocks: one work-group per row stages the row in LDS, and every
+// thread computes the rank of each of its candidates (how many candidates are ordered before it); a
 // candidate of rank r < top_k is the r-th pick.  No serial rounds.
 constexpr int kRankRowBlocks = 512;
 
 __global__ __launch_bounds__(kBlock) void index_topk_rank_kernel(const double* scores, int32_t rows, int32_t nb,
                                                                  int32_t top_k, int32_t* ids, int32_t* counts)
 {
-    __shared__ double row_lds[kWavesPerBlock][kRankRowBlocks];
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int32_t r = (int32_t)(blockIdx.x * kWavesPerBlock + wave);
-    if (r >= rows) return;   // wave-uniform; only wave-level synchronisation below
+    __shared__ double row_lds[kRankRowBlocks];
+    __shared__ int32_t n_lds[kWavesPerBlock];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int32_t r = (int32_t)blockIdx.x;
+    if (r >= rows) return;   // uniform over the work-group
     const double* row = scores + (int64_t)r * nb;
-    double* sh = row_lds[wave];
     int n_local = 0;
-    for (int32_t i = lane; i < nb; i += kWave) {
+    for (int32_t i = tid; i < nb; i += kBlock) {
         const double v = row[i];
         const bool cand = v > -INFINITY;              // -inf and NaN are never picked
-        sh[i] = cand ? v : -INFINITY;
+        row_lds[i] = cand ? v : -INFINITY;
         n_local += cand;
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    int32_t n = n_local;
 #pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) n += __shfl_xor(n, m);
+    for (int m = 1; m < kWave; m <<= 1) n_local += __shfl_xor(n_local, m);
+    if (lane == 0) n_lds[wave] = n_local;
+    __syncthreads();
+    int32_t n = 0;
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w) n += n_lds[w];
     const int32_t picked = n < top_k ? n : top_k;
     int32_t* out = ids + (int64_t)r * top_k;
-    for (int32_t k = picked + lane; k < top_k; k += kWave) out[k] = -1;
-    for (int32_t i = lane; i < nb; i += kWave) {
-        const double si = sh[i];
+    for (int32_t k = picked + tid; k < top_k; k += kBlock) out[k] = -1;
+    for (int32_t i = tid; i < nb; i += kBlock) {
+        const double si = row_lds[i];
         if (!(si > -INFINITY)) continue;
         int32_t rank = 0;
 #pragma unroll 8
         for (int32_t j = 0; j < nb; ++j) {
-            const double sj = sh[j];
+            const double sj = row_lds[j];
             rank += (sj > si || (sj == si && j < i)) ? 1 : 0;   // -inf entries never count
         }
         if (rank < top_k) out[rank] = i;
     }
-    if (counts && lane == 0) counts[r] = picked;
+    if (counts && tid == 0) counts[r] = picked;
 }
 
 // Longer rows: one wavefront per row, top_k rounds of a wave-wide arg-max over the candidates ranked
@@ -418,10 +420,11 @@ msa_status msa_index_topk(const double* block_scores, int32_t rows, int32_t max_
     if (rows == 0) return MSA_OK;
     if (!block_ids || (max_blocks > 0 && !block_scores)) return MSA_ERR_NULL_POINTER;
     if (!aligned(block_scores, 8) || !aligned(block_ids, 4) || !aligned(counts, 4)) return MSA_ERR_ALIGNMENT;
-    const dim3 grid((unsigned)(((int64_t)rows + kWavesPerBlock - 1) / kWavesPerBlock));
+    const bool rank = max_blocks <= kRankRowBlocks;
+    const dim3 grid(rank ? (unsigned)rows : (unsigned)(((int64_t)rows + kWavesPerBlock - 1) / kWavesPerBlock));
     void* args[] = {const_cast<double**>(&block_scores), &rows, &max_blocks, &top_k, &block_ids, &counts};
-    const void* fn = max_blocks <= kRankRowBlocks ? reinterpret_cast<const void*>(&index_topk_rank_kernel)
-                                                  : reinterpret_cast<const void*>(&index_topk_kernel);
+    const void* fn = rank ? reinterpret_cast<const void*>(&index_topk_rank_kernel)
+                          : reinterpret_cast<const void*>(&index_topk_kernel);
     const hipError_t e = hipLaunchKernel(fn, grid, dim3(kBlock), args, 0, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MSA_OK : MSA_ERR_LAUNCH;
 }
