@@ -70,7 +70,7 @@ def bf16_spacing(v):
 
 @pytest.mark.parametrize("T,K,heads", [
     (1, 64, 1), (5, 3072, 23), (64, 3072, 23), (100, 640, 3), (256, 3072, 23), (1000, 1024, 5),
-    (1025, 512, 23), (3000, 256, 7), (4096, 3072, 23),
+    (1025, 512, 23), (1100, 64, 5), (3000, 256, 7), (4096, 3072, 23),
 ])
 def test_project_dyadic_exact(T, K, heads):
     h, w = W.projection_inputs(T, K, heads * 128, seed=T + K, dyadic=True)
