@@ -409,6 +409,33 @@ def cpu_baseline(W, seconds: float):
                        f"{per_call * 1e3:.1f} ms per {rows} tokens")
 
 
+def cpu_detail(W, seconds: float):
+    """The CPU oracle with one thread and with every host thread (at most 16), on the decode batch of
+    64 tokens and on the first 4,096 tokens of the prefill workload: about `seconds` per figure."""
+    import oracle
+    out = []
+    for name, wl, rows in (("decode batch 64", W.config1(), 64), ("prefill, first 4,096 tokens", W.config3(), 4096)):
+        args = (wl.x, wl.x_stride, rows, wl.head_dim, wl.hq, wl.hkv, wl.hiq, wl.hik, wl.positions[:rows],
+                wl.seq_idx[:rows], wl.page_table, wl.max_pages, wl.num_seqs, wl.max_pages, wl.page_size,
+                wl.num_pages, *wl.weights, wl.eps, wl.theta)
+        for threads in (1, min(16, os.cpu_count() or 1)):
+            kw = dict(dtypes=[c.dtype for c in wl.caches], scales=[c.scale for c in wl.caches], num_threads=threads)
+            oracle.produce_rows(*args, **kw)
+            n, t0 = 0, time.perf_counter()
+            while True:
+                oracle.produce_rows(*args, **kw)
+                n += 1
+                el = time.perf_counter() - t0
+                if el >= seconds:
+                    break
+            per_call = el / n
+            gbs = wl.algorithmic_bytes() * rows / wl.T / per_call / 1e9
+            out.append({"workload": name, "threads": threads, "calls": n, "ms_per_call": per_call * 1e3,
+                        "GB_per_s": gbs})
+            log(f"[bench] oracle {name}, {threads} threads: {per_call * 1e3:.3f} ms per call, {gbs:.2f} GB/s")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -423,6 +450,9 @@ def main():
     ap.add_argument("--no-indexer", action="store_true", help="skip the indexer measurement")
     ap.add_argument("--no-unfused", action="store_true", help="skip the unfused-path comparison")
     ap.add_argument("--no-projection", action="store_true", help="skip the projection (GEMM + producer) measurement")
+    ap.add_argument("--cpu-detail", action="store_true",
+                    help="only time the CPU oracle (one thread and every host thread, decode batch 64 and a "
+                         "4,096-token prefill slice), print one JSON line and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run three plain 1 GiB device-to-device copies (the reference kernel that "
                          "scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
@@ -431,6 +461,12 @@ def main():
         print(f"bench.py measures one GPU only: the producer runs on one tensor-parallel rank's local heads "
               f"and never communicates; --gpus {args.gpus} is not supported.", file=sys.stderr)
         sys.exit(2)
+
+    if args.cpu_detail:
+        from paged_kv_cache_msa_amd import workloads as W
+        print(json.dumps({"cpu_oracle": cpu_detail(W, args.cpu_seconds / 4), "host_threads": os.cpu_count()}),
+              flush=True)
+        return
 
     import torch
     import paged_kv_cache_msa_amd as msa
