@@ -245,3 +245,95 @@ def test_slots_entry_point_validates(L):
     assert L.msa_slots(POS, SEQ, 4, PT, 160, 64, 160, 0, 10240, SLOTS, None) == SHAPE
     assert L.msa_slots(POS, SEQ, 4, PT, 160, 64, 160, 64, 10240, None, None) == NULLP
     assert L.msa_slots(POS, SEQ, 4, PT, 160, 64, 160, 64, 10240, SLOTS + 4, None) == ALIGN
+
+
+# ------------------------------------------------------------------ projection
+
+HID, WMAT, XOUT, COS, SIN = (0x200000 + 0x10000 * i for i in range(5))
+
+
+def test_project_workspace_size(L):
+    n = ctypes.c_uint64(0)
+    by = ctypes.byref(n)
+    assert L.msa_project_workspace_size(64, 3072, 23, by) == OK
+    # decode batch 64 at hidden 3072: 8 K slices of 384 columns per head, 8,192 binary32 partial sums each
+    assert n.value == 23 * 8 * 8192 * 4
+    assert L.msa_project_workspace_size(1024, 3072, 23, by) == OK and n.value == 16 * 23 * 8 * 8192 * 4
+    assert L.msa_project_workspace_size(1025, 3072, 23, by) == OK and n.value == 0   # the tiled kernel needs none
+    assert L.msa_project_workspace_size(0, 3072, 23, by) == OK and n.value == 0
+    assert L.msa_project_workspace_size(64, 100, 23, by) == SHAPE
+    assert L.msa_project_workspace_size(-1, 3072, 23, by) == SHAPE
+    assert L.msa_project_workspace_size(64, 3072, 0, by) == SHAPE
+    assert L.msa_project_workspace_size(64, 3072, 4097, by) == SHAPE
+    assert L.msa_project_workspace_size(64, 3072, 23, None) == NULLP
+
+
+def call_project(L, **kw):
+    a = dict(h=HID, hs=3072, T=0, K=3072, w=WMAT, ws=3072, N=2944, x=XOUT, xs=2944, wsp=WS, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return L.msa_project(a["h"], a["hs"], a["T"], a["K"], a["w"], a["ws"], a["N"], a["x"], a["xs"], a["wsp"],
+                         a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), OK),
+    (dict(K=100), SHAPE),
+    (dict(K=0), SHAPE),
+    (dict(N=100), SHAPE),
+    (dict(N=4097 * 128), SHAPE),
+    (dict(T=-1), SHAPE),
+    (dict(hs=3000), STRIDE),
+    (dict(hs=3076), STRIDE),
+    (dict(ws=3071), STRIDE),
+    (dict(xs=2940), STRIDE),
+    (dict(xs=2948), STRIDE),
+    (dict(T=64, h=None), NULLP),
+    (dict(T=64, x=None), NULLP),
+    (dict(h=HID + 8), ALIGN),
+    (dict(x=XOUT + 8), ALIGN),
+    (dict(T=1 << 24, hs=1 << 40), OVERFLOW),
+    (dict(T=64, wsp=None), WORKSPACE),
+    (dict(T=64, wsp=WS + 64), WORKSPACE),
+    (dict(T=64, wsb=1000), WORKSPACE),
+])
+def test_project_rejects_invalid_arguments(L, kw, status):
+    assert call_project(L, **kw) == status
+
+
+def call_project_produce(L, **kw):
+    a = dict(h=HID, hs=3072, T=0, K=3072, w=WMAT, ws=3072, D=128, hq=16, hkv=2, hiq=2, hik=1, cos=COS, sin=SIN,
+             slots=SLOTS, P=64, pages=10240, wq=W, wk=W, wiq=W, wik=W, eps=1e-6, q=Q, iq=IQ, k=view(), v=view(),
+             ik=view(sp=64 * 128, heads=1), wsp=WS, wsb=1 << 30, stream=None)
+    a.update(kw)
+    ref = lambda v: None if v is None else ctypes.byref(v)
+    return L.msa_project_produce(a["h"], a["hs"], a["T"], a["K"], a["w"], a["ws"], a["D"], a["hq"], a["hkv"],
+                                 a["hiq"], a["hik"], a["cos"], a["sin"], a["slots"], a["P"], a["pages"], a["wq"],
+                                 a["wk"], a["wiq"], a["wik"], a["eps"], a["q"], a["iq"], ref(a["k"]), ref(a["v"]),
+                                 ref(a["ik"]), a["wsp"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), OK),
+    (dict(hik=0, ik=None, wik=None), OK),           # index-K is optional
+    (dict(D=64), UNSUP),
+    (dict(hq=-1), SHAPE),
+    (dict(hq=0, hkv=0, hiq=0, hik=0), SHAPE),
+    (dict(P=0), SHAPE),
+    (dict(eps=-1.0), SHAPE),
+    (dict(K=100), SHAPE),
+    (dict(hs=3076), STRIDE),
+    (dict(T=64, cos=None), NULLP),
+    (dict(T=64, slots=None), NULLP),
+    (dict(T=64, q=None), NULLP),
+    (dict(wk=None), NULLP),
+    (dict(cos=COS + 4), ALIGN),
+    (dict(slots=SLOTS + 4), ALIGN),
+    (dict(q=Q + 8), ALIGN),
+    (dict(k=view(scale=None)), DTYPE),
+    (dict(k=view(st=64)), STRIDE),                  # overlapping rows
+    (dict(ik=view(sp=64 * 128, heads=2)), SHAPE),   # head count of the view differs from the call's
+    (dict(T=64, wsp=None), WORKSPACE),
+    (dict(T=64, wsb=1000), WORKSPACE),
+])
+def test_project_produce_rejects_invalid_arguments(L, kw, status):
+    assert call_project_produce(L, **kw) == status
