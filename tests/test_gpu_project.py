@@ -316,3 +316,49 @@ def test_graph_replay_decode_layers():
             assert torch.equal(q, d.q_out) and torch.equal(iq, d.iq_out), rep
             for a, b in zip(sts, d.storages):
                 assert torch.equal(a, b), rep
+
+
+def test_graph_replay_prefill_tiled():
+    """Two 2,048-token layers on the tiled kernel captured in one HIP graph: every replay, with
+    eager work and cleared outputs between replays, writes what the eager calls wrote."""
+    layers = [W.ragged(2048, seed=40 + i, pad_frac=0.05) for i in range(2)]
+    hw = [W.with_projection(wl, seed=50 + i) for i, wl in enumerate(layers)]
+    devs = [W.to_device(wl) for wl in layers]
+    T, K = hw[0][0].shape
+    assert msa.msa_project_workspace_size(T, K, layers[0].W // 128) == 0      # tiled: no workspace
+    cos = [torch.empty((T, 64), dtype=torch.float32, device="cuda") for _ in layers]
+    sin = [torch.empty_like(c) for c in cos]
+    hd = [(dev16(h), dev16(w)) for h, w in hw]
+
+    def step():
+        for wl, d, (h, w), c, s_ in zip(layers, devs, hd, cos, sin):
+            msa.msa_rope_table(d.positions, c, s_, wl.theta)
+            msa.msa_slots(d.positions, d.seq_idx, d.page_table, d.slots, page_size=wl.page_size,
+                          num_pages=wl.num_pages)
+            msa.msa_project_produce(h, w, c, s_, d.slots, *d.weights, d.q_out, d.iq_out, d.caches[0], d.caches[1],
+                                    d.caches[2], k_scale=d.scales[0], v_scale=d.scales[1], ik_scale=d.scales[2],
+                                    num_pages=wl.num_pages, rms_eps=wl.eps)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [(d.q_out.clone(), d.iq_out.clone(), [s.clone() for s in d.storages]) for d in devs]
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            step()
+    torch.cuda.current_stream().wait_stream(st)
+    for rep in range(3):
+        for d in devs:
+            d.q_out.fill_(7)
+            d.iq_out.fill_(7)
+            for s in d.storages:
+                s.fill_(W.SENTINEL_BYTE)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for (q, iq, sts), d in zip(eager, devs):
+            assert torch.equal(q, d.q_out) and torch.equal(iq, d.iq_out), rep
+            for a, b in zip(sts, d.storages):
+                assert torch.equal(a, b), rep
