@@ -75,7 +75,7 @@ def call(msa, wl, d, stream=None):
 
 def bench_decode(msa, W, torch, layers, steps, warmup):
     log(f"[bench] staging {layers} decode-64 layers")
-    wls = [W.config1(layer=i) for i in range(layers)]
+    wls = [W.decode_batch64(layer=i) for i in range(layers)]
     devs = [W.to_device(wl) for wl in wls]
     # share the metadata buffers across layers (one batch, many layers)
     for d in devs[1:]:
@@ -164,7 +164,7 @@ def bench_decode_unfused(msa, torch, wls, devs, steps, warmup):
 
 def bench_prefill(msa, W, torch, iters, warmup, unfused_iters=0):
     log("[bench] staging the 65,536-token prefill chunk (two input sets)")
-    sets = [W.config3(variant=v) for v in range(2)]
+    sets = [W.prefill_65536(variant=v) for v in range(2)]
     devs = [W.to_device(wl) for wl in sets]
     torch.cuda.synchronize()
     s = torch.cuda.current_stream()
@@ -206,7 +206,7 @@ def bench_indexer(msa, W, torch, np, reps):
     """Indexer at decode batch 64 (positions 7000..9199, about 8k keys per sequence in a pre-populated
     fp8 index-K cache): msa_index_scores + msa_index_topk (top 16 of 128-token blocks), 20 calls per
     captured graph, `reps` graph replays timed after 5 warm ones."""
-    wl = W.config1()
+    wl = W.decode_batch64()
     fill = W.index_cache_fill(wl)
     iq = torch.from_numpy(W.index_queries(wl.T, wl.hiq).view(np.int16)).cuda()
     nb = W.index_blocks(wl)
@@ -282,7 +282,7 @@ def bench_projection(msa, W, torch, np, layers, steps, warmup):
 
     out = {"hidden": W.PROJECTION_HIDDEN, "inputs": "h ~ N(0, 1), w ~ N(0, 1/hidden), bf16"}
     # ---- prefill
-    wl = W.config3()
+    wl = W.prefill_65536()
     d = W.to_device(wl)
     h, w = W.with_projection(wl, seed=1)
     hd, wd = dev16(h), dev16(w)
@@ -324,7 +324,7 @@ def bench_projection(msa, W, torch, np, layers, steps, warmup):
     del d, x, hd, wd
     torch.cuda.empty_cache()
     # ---- decode batch 64, one graph per composition
-    wls = [W.config1(layer=i) for i in range(layers)]
+    wls = [W.decode_batch64(layer=i) for i in range(layers)]
     devs = [W.to_device(x) for x in wls]
     for dd in devs[1:]:
         dd.positions, dd.seq_idx, dd.page_table = devs[0].positions, devs[0].seq_idx, devs[0].page_table
@@ -387,7 +387,7 @@ def cpu_baseline(W, seconds: float):
     """The CPU oracle as it stands, on leading slices of the prefill workload for about `seconds`."""
     import oracle
     threads = min(16, os.cpu_count() or 1)
-    wl = W.config3()
+    wl = W.prefill_65536()
     rows = 4096
     args = (wl.x, wl.x_stride, rows, wl.head_dim, wl.hq, wl.hkv, wl.hiq, wl.hik, wl.positions[:rows],
             wl.seq_idx[:rows], wl.page_table, wl.max_pages, wl.num_seqs, wl.max_pages, wl.page_size, wl.num_pages,
@@ -414,7 +414,7 @@ def cpu_detail(W, seconds: float):
     64 tokens and on the first 4,096 tokens of the prefill workload: about `seconds` per figure."""
     import oracle
     out = []
-    for name, wl, rows in (("decode batch 64", W.config1(), 64), ("prefill, first 4,096 tokens", W.config3(), 4096)):
+    for name, wl, rows in (("decode batch 64", W.decode_batch64(), 64), ("prefill, first 4,096 tokens", W.prefill_65536(), 4096)):
         args = (wl.x, wl.x_stride, rows, wl.head_dim, wl.hq, wl.hkv, wl.hiq, wl.hik, wl.positions[:rows],
                 wl.seq_idx[:rows], wl.page_table, wl.max_pages, wl.num_seqs, wl.max_pages, wl.page_size,
                 wl.num_pages, *wl.weights, wl.eps, wl.theta)

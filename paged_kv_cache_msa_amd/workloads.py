@@ -142,7 +142,7 @@ def _hnd_cache(num_pages, heads, dtype, scale, page_size=PAGE_SIZE, D=HEAD_DIM, 
 DECODE_HEADS = (16, 2, 2, 1)
 
 
-def config0(seed: int = 0) -> Workload:
+def tiny_decode(seed: int = 0) -> Workload:
     """Tiny decode: 4 sequences x 1 token, positions U{0..511}, heads 4/1/1/1 (W = 1024),
     16-page pool, page table [4, 8] from permutations of the pool, fp8 caches with scale 1."""
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -150,7 +150,7 @@ def config0(seed: int = 0) -> Workload:
     return _tiny(rng, "tiny-decode-4 (heads 4/1/1/1, W=1024)", hq, hkv, hiq, hik)
 
 
-def config0b(seed: int = 10) -> Workload:
+def tiny_decode_no_index_k(seed: int = 10) -> Workload:
     """Tiny decode without index-K: heads 4/1/1/0 (W = 896)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     return _tiny(rng, "tiny-decode-4 no index-K (heads 4/1/1/0, W=896)", 4, 1, 1, 0)
@@ -173,7 +173,7 @@ def _tiny(rng, name, hq, hkv, hiq, hik):
     return Workload(name, hq, hkv, hiq, hik, D, P, num_pages, x, pos, seq, pt, w, caches)
 
 
-def config1(seed: int = 1, layer: int = 0, meta_only: bool = False) -> Workload:
+def decode_batch64(seed: int = 1, layer: int = 0, meta_only: bool = False) -> Workload:
     """Decode batch 64: 64 sequences x 1 token at positions U{7000..9199}, heads 16/2/2/1,
     page table = permutation(10240) as [64, 160], fp8 caches [10240, H, 64, 128], scales U(0.5, 2).
     `layer` draws a distinct input row, weights and scales per layer over shared metadata."""
@@ -195,7 +195,7 @@ def config1(seed: int = 1, layer: int = 0, meta_only: bool = False) -> Workload:
                     num_pages, x, pos, seq, pt, w, caches)
 
 
-def config2(seed: int = 2) -> Workload:
+def decode_batch256_padded(seed: int = 2) -> Workload:
     """Decode batch 256 with padding: 26 tokens (10%) padded (seq = -1), 5 tokens (2%) whose page-table
     entry points past the pool; x is columns [0, 2944) of a [256, 3072] buffer; caches are the
     [:, :, :64, :] view of storage [40960, H, 65, 128] (padded token dimension)."""
@@ -221,7 +221,7 @@ def config2(seed: int = 2) -> Workload:
                     n_invalid=len(padded) + len(oob))
 
 
-def config3(seed: int = 3, variant: int = 0) -> Workload:
+def prefill_65536(seed: int = 3, variant: int = 0) -> Workload:
     """Prefill chunk: 8 sequences x 8192 tokens (65,536 rows) at positions 0..8191, heads 16/2/2/1,
     x ~ N(0, 1.5^2), page table [8, 128] = 1,024 distinct pages of a permuted 12,000-page pool,
     fp8 caches, scales U(0.5, 2).  `variant` redraws the values (not the shapes)."""
@@ -244,7 +244,7 @@ def config3(seed: int = 3, variant: int = 0) -> Workload:
                     num_pages, x, pos, seq, pt, w, caches)
 
 
-def config4(cache_dtype: int = BF16, seed: int = 4) -> Workload:
+def mixed_batch_64bit(cache_dtype: int = BF16, seed: int = 4) -> Workload:
     """Mixed batch with 64-bit offsets: 4 prefill chunks of 2048 tokens (chunk start U{1..30720})
     followed by 192 decode tokens (positions U{1..32767}); T = 8384; page table [196, 512];
     270,000-page pool so that index-K holds 2.21e9 > 2^31 elements; at least a quarter of the written

@@ -77,7 +77,7 @@ def compare(name, got, ref):
 
 @pytest.mark.parametrize("dtype", [W.FP8_E4M3, W.BF16], ids=["fp8", "bf16"])
 def test_index_standalone_decode64(dtype):
-    wl = W.config1()
+    wl = W.decode_batch64()
     if dtype == W.BF16:
         wl.caches[2].dtype = W.BF16
     fill = W.index_cache_fill(wl)
@@ -91,7 +91,7 @@ def test_index_standalone_decode64(dtype):
     compare("standalone", got, oracle_index(wl, iq, fill, nb))
 
 
-@pytest.mark.parametrize("make", [lambda: W.config1(), lambda: W.config2(), lambda: W.verify_window(draft_len=3)],
+@pytest.mark.parametrize("make", [lambda: W.decode_batch64(), lambda: W.decode_batch256_padded(), lambda: W.verify_window(draft_len=3)],
                          ids=["decode64", "decode256-padded", "verify-window"])
 def test_producer_then_indexer(make):
     """The chain of one sparse layer's front half: produce (writes this step's index-K), then score and

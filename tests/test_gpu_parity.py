@@ -114,32 +114,32 @@ def check(wl, d, full=None):
     say(f"  caches: gathered rows byte-identical, untouched count exact ({len(valid)} tokens written)")
 
 
-@pytest.mark.parametrize("make", [W.config0, W.config0b], ids=["tiny-w1024", "tiny-w896-no-index-k"])
+@pytest.mark.parametrize("make", [W.tiny_decode, W.tiny_decode_no_index_k], ids=["tiny-w1024", "tiny-w896-no-index-k"])
 def test_tiny_decode(make):
     wl = make()
     check(wl, run(wl), full=True)
 
 
 def test_decode_batch_64():
-    wl = W.config1()
+    wl = W.decode_batch64()
     check(wl, run(wl))
 
 
 def test_decode_batch_256_padded_strided():
-    wl = W.config2()
+    wl = W.decode_batch256_padded()
     d = run(wl)
     assert int((d.slots < 0).sum()) == 31
     check(wl, d)
 
 
 def test_prefill_65536():
-    wl = W.config3()
+    wl = W.prefill_65536()
     check(wl, run(wl))
 
 
 @pytest.mark.parametrize("dtype", [W.BF16, W.FP8_E4M3], ids=["bf16", "fp8"])
 def test_mixed_64bit_offsets(dtype):
-    wl = W.config4(dtype)
+    wl = W.mixed_batch_64bit(dtype)
     assert wl.num_pages * wl.caches[2].strides[0] > 2 ** 31
     d = run(wl)
     check(wl, d)
@@ -182,8 +182,8 @@ def test_special_values():
 
 # ------------------------------------------------------------------ step-level entry points
 
-def test_rope_table_exhaustive_configs_domain():
-    """Every position in [0, 131072) at theta = 1e4 (all configs' positions) against the oracle,
+def test_rope_table_exhaustive_workload_positions():
+    """Every position in [0, 131072) at theta = 1e4 (every workload's positions) against the oracle,
     bit for bit."""
     import oracle
     pos = np.arange(131072, dtype=np.int32)
@@ -285,7 +285,7 @@ def test_rms_scale_random_and_edges():
 def test_graph_replay_matches_eager():
     """Three layer calls captured in one HIP graph: every replay (with eager work and
     synchronisation between replays) writes exactly what the eager calls wrote."""
-    layers = [W.config1(layer=i) for i in range(3)]
+    layers = [W.decode_batch64(layer=i) for i in range(3)]
     devs = [W.to_device(wl) for wl in layers]
 
     def call(wl, d):

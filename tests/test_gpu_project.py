@@ -119,9 +119,9 @@ def fused(wl, h, w, d=None, ws=None, stream=None):
 
 
 CASES = {
-    "tiny-w1024": lambda: W.config0(),
-    "decode64": lambda: W.config1(),
-    "decode256-padded-strided": lambda: W.config2(),
+    "tiny-w1024": lambda: W.tiny_decode(),
+    "decode64": lambda: W.decode_batch64(),
+    "decode256-padded-strided": lambda: W.decode_batch256_padded(),
     "verify-window": lambda: W.verify_window(draft_len=3),
     "ragged-3000-tiled": lambda: W.ragged(3000, seed=31, pad_frac=0.1),
     "ragged-700-bf16": lambda: W.ragged(700, seed=32, cache_dtypes=(1, 1, 1), pad_frac=0.1),
@@ -201,7 +201,7 @@ def test_project_produce_prefill_65536_sampled():
     h ~ N(0, 1), w ~ N(0, 1/hidden)): on the device the fused outputs equal msa_project followed by
     msa_produce everywhere; against the oracle's projection and producer on sampled tokens (tile
     edges, chunk edges, the last token, random ones) at the normal-input bars."""
-    wl = W.config3()
+    wl = W.prefill_65536()
     h, w = W.with_projection(wl, seed=1)
     T, K = h.shape
     say(f"[gpu] msa_project_produce prefill T={T} W={wl.W} K={K}")
@@ -249,7 +249,7 @@ def test_project_produce_prefill_65536_sampled():
 def test_workspace_contents_do_not_matter():
     """Two decode calls on one workspace, the second after the outputs are cleared and the workspace
     is filled with garbage: both write the same bytes."""
-    wl = W.config1()
+    wl = W.decode_batch64()
     h, w = W.with_projection(wl, seed=9)
     ws = workspace(wl.T, h.shape[1], wl.W // 128)
     d = fused(wl, h, w, ws=ws)
@@ -268,7 +268,7 @@ def test_workspace_contents_do_not_matter():
 def test_graph_replay_decode_layers():
     """Three decode layers' msa_project_produce calls captured in one HIP graph (one workspace):
     every replay, with eager work between replays, writes what the eager calls wrote."""
-    layers = [W.config1(layer=i) for i in range(3)]
+    layers = [W.decode_batch64(layer=i) for i in range(3)]
     hw = [W.with_projection(wl, seed=20 + i) for i, wl in enumerate(layers)]
     devs = [W.to_device(wl) for wl in layers]
     T, K = hw[0][0].shape

@@ -48,19 +48,19 @@ def run(wl, d=None):
     return d
 
 
-@pytest.mark.parametrize("make", [W.config0, W.config0b], ids=["tiny-w1024", "tiny-w896-no-index-k"])
+@pytest.mark.parametrize("make", [W.tiny_decode, W.tiny_decode_no_index_k], ids=["tiny-w1024", "tiny-w896-no-index-k"])
 def test_tiny_decode(make):
     wl = make()
     check(wl, run(wl), full=True)
 
 
 def test_decode_batch_64():
-    wl = W.config1()
+    wl = W.decode_batch64()
     check(wl, run(wl))
 
 
 def test_decode_batch_256_padded_strided():
-    wl = W.config2()
+    wl = W.decode_batch256_padded()
     d = run(wl)
     assert int((d.slots < 0).sum()) == 31
     check(wl, d)
@@ -68,7 +68,7 @@ def test_decode_batch_256_padded_strided():
 
 @pytest.mark.parametrize("dtype", [W.BF16, W.FP8_E4M3], ids=["bf16", "fp8"])
 def test_mixed_64bit_offsets(dtype):
-    wl = W.config4(dtype)
+    wl = W.mixed_batch_64bit(dtype)
     assert wl.num_pages * wl.caches[2].strides[0] > 2 ** 31
     check(wl, run(wl))
     torch.cuda.empty_cache()
@@ -149,7 +149,7 @@ def test_graph_replay_matches_eager_and_fused():
     """Three layers of (slots once, then 14 launches per layer) captured in one HIP graph: every
     replay writes what the eager calls wrote, and that is byte for byte what the fused producer
     writes from the same inputs."""
-    layers = [W.config1(layer=i) for i in range(3)]
+    layers = [W.decode_batch64(layer=i) for i in range(3)]
     devs = [W.to_device(wl) for wl in layers]
     wss = [workspace(wl) for wl in layers]
 

@@ -145,7 +145,7 @@ def _slot_bruteforce(wl):
     return np.array(out, np.int64)
 
 
-@pytest.mark.parametrize("make", [W.config0, W.config0b, lambda: W.ragged(37, seed=3)])
+@pytest.mark.parametrize("make", [W.tiny_decode, W.tiny_decode_no_index_k, lambda: W.ragged(37, seed=3)])
 def test_slots_closed_form(oracle_lib, make):
     """Invariant: slot = page_table[seq][pos // P] * P + pos % P for every valid token, -1 otherwise."""
     wl = make()
@@ -181,7 +181,7 @@ def test_slots_exhaustive_small_table(oracle_lib):
 
 def test_slot_set_bruteforce_tiny(oracle_lib):
     """Config 0: the set of slots written equals the enumerated expectation, and is all-distinct."""
-    wl = W.config0()
+    wl = W.tiny_decode()
     r, st = H.oracle_caches(wl)
     exp = _slot_bruteforce(wl)
     np.testing.assert_array_equal(r["slots"], exp)
@@ -224,7 +224,7 @@ def _check_against_torch(wl, got_q, got_iq, rows):
 
 
 @pytest.mark.parametrize("make", [
-    W.config0, W.config0b,
+    W.tiny_decode, W.tiny_decode_no_index_k,
     lambda: W.ragged(23, seed=11, cache_dtypes=(W.BF16, W.BF16, W.BF16), row_pad=64),
     lambda: W.ragged(9, seed=12, heads=(3, 1, 2, 2), cache_dtypes=(W.FP8_E4M3, W.BF16, W.FP8_E4M3), sigma=3.0),
 ])
@@ -241,7 +241,7 @@ def test_one_hot_worked_example(oracle_lib):
     r = fl32(1/sqrt(1/128 + eps)); RoPE then puts r*cos(pos*f_j) at j and r*sin(pos*f_j) at j+64.
     This fixes the rotation's orientation and its (i, i+64) pairing."""
     D, pos, j = 128, 1234, 5
-    wl = W.config0()
+    wl = W.tiny_decode()
     wl.x[:] = 0
     wl.x[0, j] = 0x3F80                       # Q head 0 of token 0 = e_j (bf16 1.0)
     wl.weights = [np.full(D, 0x3F80, np.uint16) if w is not None else None for w in wl.weights]
@@ -322,7 +322,7 @@ def _with_positions(wl, p):
 
 def test_v_bytes_closed_form(oracle_lib):
     """Invariant: an fp8 V cache byte is e4m3(bf16 input * fl32(1/scale)), with no norm or RoPE."""
-    wl = W.config2()
+    wl = W.decode_batch256_padded()
     rows = H.oracle_rows(wl)
     D = 128
     v_cols = slice((wl.hq + wl.hkv) * D, (wl.hq + 2 * wl.hkv) * D)
@@ -333,7 +333,7 @@ def test_v_bytes_closed_form(oracle_lib):
     np.testing.assert_array_equal(rows["v"], ref)
 
 
-@pytest.mark.parametrize("make", [W.config0, W.config0b, W.config2, lambda: W.ragged(50, seed=8, pad_frac=0.3)])
+@pytest.mark.parametrize("make", [W.tiny_decode, W.tiny_decode_no_index_k, W.decode_batch256_padded, lambda: W.ragged(50, seed=8, pad_frac=0.3)])
 def test_sentinel_and_written_count(oracle_lib, make):
     """Invariants: slots never written keep their sentinel, and the number of changed cache
     elements is exactly (#valid tokens) * heads * D per cache (padding of the view included)."""
@@ -349,7 +349,7 @@ def test_sentinel_and_written_count(oracle_lib, make):
 
 def test_padded_tokens_still_emit_q(oracle_lib):
     """Q and index-Q are produced for every row, padded or not (only cache writes are skipped)."""
-    wl = W.config2()
+    wl = W.decode_batch256_padded()
     rows = H.oracle_rows(wl)
     pad = np.flatnonzero(wl.seq_idx < 0)
     assert pad.size == 26
@@ -358,7 +358,7 @@ def test_padded_tokens_still_emit_q(oracle_lib):
 
 
 def test_duplicate_slots_rejected(oracle_lib):
-    wl = W.config0()
+    wl = W.tiny_decode()
     wl.seq_idx[1] = wl.seq_idx[0]
     wl.positions[1] = wl.positions[0]
     with pytest.raises(oracle.OracleError):
