@@ -54,7 +54,8 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d)
 }
 
 // Dequantisation scale -> quantisation multiplier, binary32 division rounded once.
-__device__ __forceinline__ float inv_scale_of(const float* scale) { return 1.0f / *scale; }
+__device__ __forceinline__ float inv_scale(float scale) { return 1.0f / scale; }
+__device__ __forceinline__ float inv_scale_of(const float* scale) { return inv_scale(*scale); }
 
 // RMSNorm scale from a binary64 sum of squares: (float)(1 / sqrt(ss / 128 + eps)).
 __device__ __forceinline__ float rms_from_ss(double ss, float eps)

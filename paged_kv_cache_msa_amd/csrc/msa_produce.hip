@@ -65,6 +65,27 @@ struct FreqArgs {
     double inv_freq[kHalf];
 };
 
+// One float through a buffer load of a 4-byte range: always a vector memory instruction, even at a
+// wave-uniform address.  Vector loads retire in issue order, so a later wait for an earlier load
+// does not wait for this one, whereas a scalar load would join the next wait for the (scalar) token
+// metadata.  The range check returns 0 outside the 4 bytes and cannot fault.
+__device__ __forceinline__ float vector_load_f32(const float* p)
+{
+    // 0x00020000: the gfx9-family word 3 of a raw (untyped, dword) buffer resource.
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p), 0, 4, 0x00020000);
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, 0, 0, 0));
+}
+
+// Stream of head slot h (h < heads_total) in the packed row order Q, K, V, index-Q, index-K.
+__device__ __forceinline__ int stream_of(int h, int h_k, int h_v, int h_iq, int h_ik)
+{
+    return h < h_k ? kQ : h < h_v ? kK : h < h_iq ? kV : h < h_ik ? kIQ : kIK;
+}
+
+// One of three wave-uniform values, chosen per lane.
+template <typename V>
+__device__ __forceinline__ V sel3(int i, V v0, V v1, V v2) { return i == 0 ? v0 : i == 1 ? v1 : v2; }
+
 // One producer launch.  PPW = passes (groups of 8 heads) per wave.  HQ..HIK fix the head
 // geometry at compile time (the stream of every head slot then folds to constants); all four
 // negative selects the generic build that reads the geometry from the arguments.
@@ -108,8 +129,32 @@ __global__ __launch_bounds__(kBlock) void produce_kernel(const ProduceArgs a)
     const int hs = lane / kLanesPerHead;   // head slot within a pass
     const int sub = lane % kLanesPerHead;  // element group within the head
 
-    // Row loads of every pass of this wave, issued first.  Slots past the last head (and waves
-    // past the last token) read the token's first head instead, a valid address, and discard it.
+    // Loads that do not depend on the token metadata go out first, so that their memory round
+    // trips overlap one another instead of following the arithmetic (on the decode critical path):
+    // this lane's RoPE frequency, the fp8 dequantisation scales, a one-pass wave's norm weights,
+    // then the rows.  A V head (no norm) reads its "weights" from the input row instead, a valid
+    // address, and discards them.
+    const double freq = a.inv_freq[lane];
+    // Waves with several passes (large batches, bound by bandwidth) read the scales at the cast
+    // instead, which keeps three registers free.
+    float scale_v[3] = {1.0f, 1.0f, 1.0f};
+    if (PPW == 1) {
+#pragma unroll
+        for (int c = 0; c < 3; ++c)   // no scale (bf16 cache, or no heads): read the row instead, unused
+            scale_v[c] = vector_load_f32(a.cache[c].scale ? a.cache[c].scale : reinterpret_cast<const float*>(a.x));
+    }
+    uint4 wa = make_uint4(0, 0, 0, 0), wb = make_uint4(0, 0, 0, 0);
+    if (!kStageW) {
+        const int h = pass0 * kHeadsPerPass + hs;
+        const int st = stream_of(h < heads_total ? h : heads_total - 1, h_k, h_v, h_iq, h_ik);
+        const uint16_t* w = st == kQ ? a.w[0] : st == kK ? a.w[1] : st == kIQ ? a.w[2] : st == kIK ? a.w[3] : nullptr;
+        if (!w) w = a.x;
+        wa = *reinterpret_cast<const uint4*>(w + sub * 8);
+        wb = *reinterpret_cast<const uint4*>(w + kHalf + sub * 8);
+    }
+
+    // Row loads of every pass of this wave.  Slots past the last head (and waves past the last
+    // token) read the token's first head instead, a valid address, and discard it.
     const int32_t t_ld = live ? t : 0;
     const uint16_t* row = a.x + (int64_t)t_ld * a.x_stride + sub * 8;
     uint4 xa[PPW], xb[PPW];
@@ -155,7 +200,7 @@ __global__ __launch_bounds__(kBlock) void produce_kernel(const ProduceArgs a)
         }
         // RoPE coefficients of this token: lane i computes frequency i.
         float c, s;
-        rope_coeff(pos, a.inv_freq[lane], &c, &s);
+        rope_coeff(pos, freq, &c, &s);
         cs_lds[wave][lane] = c;
         cs_lds[wave][kHalf + lane] = s;
     }
@@ -165,7 +210,21 @@ __global__ __launch_bounds__(kBlock) void produce_kernel(const ProduceArgs a)
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     const bool valid = page >= 0;
-    if (chunk == 0 && lane == 0 && a.slots_out) a.slots_out[t] = valid ? page * a.page_size + off : -1;
+    // One-pass waves: this token's row in each cache (head 0, element 0) as a byte address, and the
+    // head stride in bytes, wave-uniform and once per wave; lanes then pick their cache by value
+    // (indexing the descriptors by a per-lane cache number would load them from the argument
+    // segment with vector loads, one more memory round trip before the stores).
+    uint8_t* row_base[3] = {nullptr, nullptr, nullptr};
+    int64_t head_bytes[3] = {0, 0, 0};
+    bool c_bf16[3] = {false, false, false};
+#pragma unroll
+    for (int c = 0; c < (PPW == 1 ? 3 : 0); ++c) {
+        const CacheDev& cd = a.cache[c];
+        c_bf16[c] = cd.is_bf16 != 0;
+        const int64_t esz = c_bf16[c] ? 2 : 1;
+        row_base[c] = cd.data + (page * cd.sp + (int64_t)off * cd.st) * esz;
+        head_bytes[c] = cd.sh * esz;
+    }
 
     float cf[8], sf[8];
     {
@@ -213,7 +272,7 @@ __global__ __launch_bounds__(kBlock) void produce_kernel(const ProduceArgs a)
         // Slots past the last head compute as the last head (its stream has heads, so its weight
         // pointer is valid) and store nothing.
         const int hc = h < heads_total ? h : heads_total - 1;
-        const int st = hc < h_k ? kQ : hc < h_v ? kK : hc < h_iq ? kV : hc < h_ik ? kIQ : kIK;
+        const int st = stream_of(hc, h_k, h_v, h_iq, h_ik);
 
         // Keep each pass's temporaries from being hoisted into the previous pass (register footprint).
         __builtin_amdgcn_sched_barrier(0);
@@ -234,9 +293,8 @@ __global__ __launch_bounds__(kBlock) void produce_kernel(const ProduceArgs a)
                 wv[0] = w0.x; wv[1] = w0.y; wv[2] = w0.z; wv[3] = w0.w; wv[4] = w1.x; wv[5] = w1.y; wv[6] = w1.z; wv[7] = w1.w;
                 wv[8] = w2.x; wv[9] = w2.y; wv[10] = w2.z; wv[11] = w2.w; wv[12] = w3.x; wv[13] = w3.y; wv[14] = w3.z; wv[15] = w3.w;
             } else {
-                const uint16_t* w = a.w[ws] + sub * 8;
-                unpack8(*reinterpret_cast<const uint4*>(w), wv);
-                unpack8(*reinterpret_cast<const uint4*>(w + kHalf), wv + 8);
+                unpack8(wa, wv);         // one pass per wave: loaded at the top
+                unpack8(wb, wv + 8);
             }
             float y[16];
 #pragma unroll
@@ -258,21 +316,35 @@ __global__ __launch_bounds__(kBlock) void produce_kernel(const ProduceArgs a)
         } else if (valid) {
             const int ci = st == kK ? 0 : st == kV ? 1 : 2;
             const int hl = st == kK ? h - h_k : st == kV ? h - h_v : h - h_ik;
-            const CacheDev& cd = a.cache[ci];
-            const int64_t e = page * cd.sp + (int64_t)off * cd.st + (int64_t)hl * cd.sh + sub * 8;
-            if (cd.is_bf16) {
-                uint16_t* dst = reinterpret_cast<uint16_t*>(cd.data) + e;
+            uint8_t* head_row;   // byte address of (token, head hl, element 0) in the cache
+            bool is_bf16;
+            float m = 1.0f;      // fp8 quantisation multiplier
+            if (PPW == 1) {
+                head_row = sel3(ci, row_base[0], row_base[1], row_base[2])
+                         + (int64_t)hl * sel3(ci, head_bytes[0], head_bytes[1], head_bytes[2]);
+                is_bf16 = sel3(ci, c_bf16[0], c_bf16[1], c_bf16[2]);
+                if (!is_bf16) m = inv_scale(sel3(ci, scale_v[0], scale_v[1], scale_v[2]));
+            } else {
+                const CacheDev& cd = a.cache[ci];
+                is_bf16 = cd.is_bf16 != 0;
+                head_row = cd.data + (page * cd.sp + (int64_t)off * cd.st + (int64_t)hl * cd.sh) * (is_bf16 ? 2 : 1);
+                if (!is_bf16) m = inv_scale_of(cd.scale);
+            }
+            if (is_bf16) {
+                uint16_t* dst = reinterpret_cast<uint16_t*>(head_row) + sub * 8;
                 store16<kStream>(dst, bf16x8(o));
                 store16<kStream>(dst + kHalf, bf16x8(o + 8));
             } else {
                 uint2 lo, hi;
-                e4m3x16(o, inv_scale_of(cd.scale), lo, hi);
-                uint8_t* dst = cd.data + e;
+                e4m3x16(o, m, lo, hi);
+                uint8_t* dst = head_row + sub * 8;
                 store8<kStream>(dst, lo);
                 store8<kStream>(dst + kHalf, hi);
             }
         }
     }
+    // Last: a store issued early would make the waits for the rows also wait for it.
+    if (chunk == 0 && lane == 0 && a.slots_out) a.slots_out[t] = valid ? page * a.page_size + off : -1;
 }
 
 // ------------------------------------------------------------------ step-level kernels
