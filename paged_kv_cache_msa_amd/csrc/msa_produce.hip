@@ -147,8 +147,12 @@ __global__ __launch_bounds__(kBlock) void produce_kernel(const ProduceArgs a)
     if (!kStageW) {
         const int h = pass0 * kHeadsPerPass + hs;
         const int st = stream_of(h < heads_total ? h : heads_total - 1, h_k, h_v, h_iq, h_ik);
-        const uint16_t* w = st == kQ ? a.w[0] : st == kK ? a.w[1] : st == kIQ ? a.w[2] : st == kIK ? a.w[3] : nullptr;
-        if (!w) w = a.x;
+        // all four pointers first, then a per-lane choice by value (no branch per stream)
+        const uint16_t* const w0 = a.w[0] ? a.w[0] : a.x;
+        const uint16_t* const w1 = a.w[1] ? a.w[1] : a.x;
+        const uint16_t* const w2 = a.w[2] ? a.w[2] : a.x;
+        const uint16_t* const w3 = a.w[3] ? a.w[3] : a.x;
+        const uint16_t* const w = st == kQ ? w0 : st == kK ? w1 : st == kIQ ? w2 : st == kIK ? w3 : a.x;
         wa = *reinterpret_cast<const uint4*>(w + sub * 8);
         wb = *reinterpret_cast<const uint4*>(w + kHalf + sub * 8);
     }
@@ -182,34 +186,31 @@ __global__ __launch_bounds__(kBlock) void produce_kernel(const ProduceArgs a)
         }
     }
 
-    // Token metadata, once per wave.
-    int64_t page = -1;
-    int32_t off = 0;
-    if (live) {
-        const int32_t pos = a.pos[t];
-        const int32_t sq = a.seq[t];
-        if (sq >= 0 && sq < a.S && pos >= 0) {
-            const int32_t lp = a.page_shift >= 0 ? pos >> a.page_shift : pos / a.page_size;
-            if (lp < a.max_pages) {
-                const int64_t pg = a.pt[(int64_t)sq * a.pt_stride + lp];
-                if (pg >= 0 && pg < a.num_pages) {
-                    page = pg;
-                    off = pos - lp * a.page_size;
-                }
-            }
-        }
+    // Token metadata, once per wave (wave-uniform).  The page-table entry is read without a
+    // branch (an invalid slot reads the position array instead, a valid address) so that the
+    // RoPE coefficients are computed while the entry is in flight.
+    const int32_t pos = a.pos[t_ld];
+    const int32_t sq = a.seq[t_ld];
+    const bool seq_ok = live && sq >= 0 && sq < a.S && pos >= 0;
+    const int32_t lp = a.page_shift >= 0 ? pos >> a.page_shift : pos / a.page_size;
+    const bool lp_ok = seq_ok && lp < a.max_pages;
+    const int32_t* pte = lp_ok ? a.pt + ((int64_t)sq * a.pt_stride + lp) : a.pos;
+    const int64_t pg = *pte;
+    {
         // RoPE coefficients of this token: lane i computes frequency i.
         float c, s;
         rope_coeff(pos, freq, &c, &s);
         cs_lds[wave][lane] = c;
         cs_lds[wave][kHalf + lane] = s;
     }
+    const bool valid = lp_ok && pg >= 0 && pg < a.num_pages;
+    const int64_t page = valid ? pg : -1;
+    const int32_t off = valid ? pos - lp * a.page_size : 0;
     if (!live) return;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    const bool valid = page >= 0;
     // One-pass waves: this token's row in each cache (head 0, element 0) as a byte address, and the
     // head stride in bytes, wave-uniform and once per wave; lanes then pick their cache by value
     // (indexing the descriptors by a per-lane cache number would load them from the argument
