@@ -68,7 +68,7 @@ inline msa_status check_cache(const msa_cache_view* v, int32_t heads, int32_t pa
     out->sp = s[0];
     out->sh = s[1];
     out->st = s[2];
-    out->scale = v->scale;
+    out->scale = v->dtype == MSA_CACHE_FP8_E4M3 ? v->scale : nullptr;   // a bf16 cache's scale is never read
     out->heads = heads;
     out->is_bf16 = v->dtype == MSA_CACHE_BF16;
     return MSA_OK;

@@ -164,6 +164,21 @@ def test_ragged_and_launch_shapes(T, heads, dtypes, pad):
     check(wl, run(wl))
 
 
+@pytest.mark.parametrize("T", [64, 8000], ids=["one-pass-waves", "three-pass-waves"])
+def test_bf16_cache_scale_pointer_is_ignored(T):
+    """A bf16 cache takes no scale: a stray (here misaligned) scale pointer passed with bf16 caches is
+    never read and changes nothing."""
+    wl = W.ragged(T, seed=11, cache_dtypes=(W.BF16, W.BF16, W.BF16), pad_frac=0.1)
+    d = W.to_device(wl)
+    stray = torch.zeros(16, dtype=torch.uint8, device="cuda")[1:]
+    say(f"[gpu] msa_produce {wl.name} with a stray bf16 scale pointer: T={wl.T}")
+    msa.msa_produce(d.x, d.positions, d.seq_idx, d.page_table, *d.weights, d.q_out, d.iq_out,
+                    d.caches[0], d.caches[1], d.caches[2], k_scale=stray, v_scale=stray, ik_scale=stray,
+                    num_pages=wl.num_pages, rms_eps=wl.eps, rope_theta=wl.theta, slots_out=d.slots)
+    torch.cuda.synchronize()
+    check(wl, d)
+
+
 def test_special_values():
     """NaN, infinities, huge and tiny values, all-zero heads and saturating scales."""
     wl = W.ragged(64, seed=77, cache_dtypes=(0, 0, 1), pad_frac=0.0)
