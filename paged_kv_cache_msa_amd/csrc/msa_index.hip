@@ -183,7 +183,21 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
         const double scale = kBf16 ? 1.0 : (double)*a.ik.scale;
         const int32_t p_end = (int32_t)min((int64_t)p0 + a.block_tokens, (int64_t)pos + 1);
         const int64_t head_off = (int64_t)(a.head0 / a.group) * a.ik.sh;   // NH heads share one index-K head
+        // kStepInPage: the page-table entries of up to 64 steps are fetched at once, step j of the
+        // chunk by lane j, and each step reads its entry back with a lane read: one memory round
+        // trip per 64 steps (512 keys) instead of a dependent lookup per step.
+        int32_t step_pg = -1;      // lane j: page of step chunk0 + j, or -1
+        int32_t chunk0 = 0;        // first step (counted from p0) of the fetched chunk
+        bool fetched = false;
         for (int32_t pb = p0; pb < p_end; pb += BATCH * kKeysPerStep) {
+            const int32_t step0 = (pb - p0) / kKeysPerStep;
+            if (kStepInPage && (!fetched || step0 + BATCH > chunk0 + kWave)) {   // wave-uniform
+                chunk0 = step0;
+                fetched = true;
+                const int64_t ps_l = (int64_t)pb + (int64_t)lane * kKeysPerStep;
+                int32_t unused;
+                step_pg = ps_l < p_end ? (int32_t)page_of(a, sq, (int32_t)ps_l, &unused) : -1;
+            }
             int64_t e[BATCH];
             uint32_t live = 0;                     // bit i: key of step i exists and has a page
 #pragma unroll
@@ -194,10 +208,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
                 if (kStepInPage) {
                     // the step's first position decides the page for all 8 keys (wave-uniform)
                     const int32_t ps = pb + i * kKeysPerStep;
-                    int32_t off0 = 0;
-                    const int64_t pgs = ps < p_end ? page_of(a, sq, ps, &off0) : -1;
-                    pg = p < p_end ? pgs : -1;
-                    off = off0 + ks;
+                    const int32_t pe = __builtin_amdgcn_readlane(step_pg, step0 + i - chunk0);
+                    const int32_t lps = a.page_shift >= 0 ? ps >> a.page_shift : ps / a.page_size;
+                    pg = p < p_end ? (int64_t)pe : -1;   // pe is -1 for a step past p_end
+                    off = ps - lps * a.page_size + ks;
                 } else {
                     pg = p < p_end ? page_of(a, sq, p, &off) : -1;
                 }
