@@ -150,23 +150,34 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
     constexpr int BATCH = kBf16 ? 2 : 4;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const uint32_t item = blockIdx.x * kWavesPerBlock + wave;
-    if (item >= (uint32_t)a.T * (uint32_t)a.max_blocks) return;   // wave-uniform
-    const int32_t t = (int32_t)(item / (uint32_t)a.max_blocks);
-    const int32_t b = (int32_t)(item - (uint32_t)t * (uint32_t)a.max_blocks);
+    // Two waves per (token, block), each scoring half of the block's keys; the pair's maxima meet in
+    // LDS.  Half-block waves keep the work after the first round of resident waves short.
+    // Block-major order: waves are dispatched in item order, so the high blocks, which only the
+    // tokens at the longest positions can see (the others exit at once), come last.
+    const uint32_t item = blockIdx.x * (kWavesPerBlock / 2) + (uint32_t)(wave >> 1);
+    const int half = wave & 1;
+    const bool item_ok = item < (uint32_t)a.T * (uint32_t)a.max_blocks;   // wave-uniform
+    const int32_t b = item_ok ? (int32_t)(item / (uint32_t)a.T) : 0;
+    const int32_t t = item_ok ? (int32_t)(item - (uint32_t)b * (uint32_t)a.T) : 0;
     const int ks = lane / kLanesPerKey;    // key slot of a step
     const int sub = lane % kLanesPerKey;   // element group within the key
 
     const int32_t pos = a.pos[t];
     const int32_t sq = a.seq[t];
     int32_t own_off;
-    const bool token_ok = page_of(a, sq, pos, &own_off) >= 0;
-    const int32_t p0 = b * a.block_tokens;
+    const bool token_ok = item_ok && page_of(a, sq, pos, &own_off) >= 0;
+    // The first half takes hb positions (a multiple of 8, so that steps of 8 keys stay within a page
+    // when the block does), the second half the rest.
+    const int64_t hb = ((int64_t)a.block_tokens + 15) / 16 * kKeysPerStep;
+    const int64_t blk0 = (int64_t)b * a.block_tokens;
+    const int64_t p0_64 = blk0 + half * hb;
+    const int64_t p_lim = half ? blk0 + a.block_tokens : min(blk0 + hb, blk0 + (int64_t)a.block_tokens);
+    const int32_t p0 = (int32_t)min(p0_64, (int64_t)INT32_MAX);   // exact whenever the half is scored
     double best[NH];
 #pragma unroll
     for (int h = 0; h < NH; ++h) best[h] = -INFINITY;
 
-    if (token_ok && p0 <= pos) {
+    if (token_ok && p0_64 <= pos && p0_64 < p_lim) {
         // This lane's 16 elements of every head's query, as binary64.
         double q[NH][kElemsPerLane];
 #pragma unroll
@@ -181,7 +192,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
             }
         }
         const double scale = kBf16 ? 1.0 : (double)*a.ik.scale;
-        const int32_t p_end = (int32_t)min((int64_t)p0 + a.block_tokens, (int64_t)pos + 1);
+        const int32_t p_end = (int32_t)min(p_lim, (int64_t)pos + 1);
         const int64_t head_off = (int64_t)(a.head0 / a.group) * a.ik.sh;   // NH heads share one index-K head
         // kStepInPage: the page-table entries of up to 64 steps are fetched at once, step j of the
         // chunk by lane j, and each step reads its entry back with a lane read: one memory round
@@ -245,9 +256,16 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
         best[h] = max_no_nan(best[h], shfl_xor_f64(best[h], 16));
         best[h] = max_no_nan(best[h], shfl_xor_f64(best[h], 32));
     }
+    __shared__ double half_best[kWavesPerBlock][NH];
     if (lane == 0) {
 #pragma unroll
-        for (int h = 0; h < NH; ++h) a.out[((int64_t)(a.head0 + h) * a.T + t) * a.max_blocks + b] = best[h];
+        for (int h = 0; h < NH; ++h) half_best[wave][h] = best[h];
+    }
+    __syncthreads();
+    if (lane == 0 && half == 0 && item_ok) {
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+            a.out[((int64_t)(a.head0 + h) * a.T + t) * a.max_blocks + b] = max_no_nan(best[h], half_best[wave + 1][h]);
     }
 }
 
@@ -398,7 +416,7 @@ msa_status msa_index_scores(const uint16_t* iq, int32_t num_tokens, int32_t head
     a.max_blocks = max_blocks;
     a.ik = ik;
     a.out = block_scores;
-    const dim3 grid((unsigned)((items + kWavesPerBlock - 1) / kWavesPerBlock));
+    const dim3 grid((unsigned)((items + 1) / 2));   // two (token, block) items per work-group, two waves each
     hipStream_t s = static_cast<hipStream_t>(stream);
     // Launches over pairs of index-Q heads that read the same index-K head (two heads' queries fit
     // the registers at once).
