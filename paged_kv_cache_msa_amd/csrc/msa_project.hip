@@ -90,6 +90,7 @@ struct EpiIn {
     float c[2][16];
     float s[2][16];
     int64_t slot;
+    float scale;               // fp8 cache rows: the dequantisation scale (1 otherwise)
 };
 
 __device__ __forceinline__ int stream_of(const Epi& e, int head)
@@ -104,7 +105,12 @@ __device__ __forceinline__ void epilogue_load(const Epi& e, int head, int32_t t,
     const int hh = (threadIdx.x & 63) >> 5;
     const int st = stream_of(e, head);
     const bool tok = t < e.T;
-    in.slot = tok && (st == kK || st == kV || st == kIK) ? e.slots[t] : -1;
+    const bool cache_row = st == kK || st == kV || st == kIK;
+    in.slot = tok && cache_row ? e.slots[t] : -1;
+    // Read here, with the other inputs, rather than at the cast: after the arithmetic it would be one
+    // more memory round trip before the stores.
+    const CacheDev& cd = e.cache[st == kK ? 0 : st == kV ? 1 : 2];
+    in.scale = cache_row && !cd.is_bf16 ? *cd.scale : 1.0f;
     if (st == kV) return;
     const uint16_t* wp = e.w[st == kQ ? 0 : st == kK ? 1 : st == kIQ ? 2 : 3] + 4 * hh;
 #pragma unroll
@@ -236,7 +242,7 @@ __device__ __forceinline__ RowOut epilogue_math(const Epi& e, int head, int32_t 
     const int hl = st == kK ? head - h_k : st == kV ? head - h_v : head - h_ik;
     const int64_t elem = page * cd.sp + off * cd.st + (int64_t)hl * cd.sh;
     o.dst = cd.data + (o.fp8 ? elem : 2 * elem);
-    if (o.fp8) o.m = inv_scale_of(cd.scale);
+    if (o.fp8) o.m = kInline ? inv_scale_of(cd.scale) : inv_scale(in.scale);
     return o;
 }
 
