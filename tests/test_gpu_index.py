@@ -134,10 +134,11 @@ def test_index_head_groups(hiq, hik):
     compare(f"groups {hiq}/{hik}", got, oracle_index(wl, iq, fill, nb))
 
 
-@pytest.mark.parametrize("block_tokens", [100, 36, 256])
+@pytest.mark.parametrize("block_tokens", [100, 36, 256, 8, 24, 136, 2048])
 def test_index_other_block_sizes(block_tokens):
     """Block sizes that are not multiples of the 8-key step (steps straddle pages: per-key page
-    lookups) and a larger one."""
+    lookups), larger ones, and multiples of 8 whose two wave parts are uneven or (8) leave the
+    second part empty; 2048 spans more than 64 steps per part (page entries fetched in chunks)."""
     wl = W.ragged(48, seed=block_tokens, pad_frac=0.1)
     fill = W.index_cache_fill(wl, seed=block_tokens)
     iq = W.index_queries(wl.T, wl.hiq, seed=block_tokens)
