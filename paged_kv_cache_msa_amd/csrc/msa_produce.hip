@@ -223,6 +223,8 @@ __global__ __launch_bounds__(kBlock) void produce_kernel(const ProduceArgs a)
         const CacheDev& cd = a.cache[c];
         c_bf16[c] = cd.is_bf16 != 0;
         const int64_t esz = c_bf16[c] ? 2 : 1;
+        // Only used when the slot is valid and the cache has heads; formed unconditionally (a guard
+        // here made the compiler wait for the page-table entry early: 5% slower per decode call).
         row_base[c] = cd.data + (page * cd.sp + (int64_t)off * cd.st) * esz;
         head_bytes[c] = cd.sh * esz;
     }
