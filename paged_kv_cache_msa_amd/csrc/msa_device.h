@@ -127,12 +127,19 @@ __device__ __forceinline__ void store8(void* p, uint2 v)
 __device__ __forceinline__ void e4m3x16(const float* o, float m, uint2& lo, uint2& hi)
 {
     float z[16];
-    bool special = false;
+    uint32_t a[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         z[j] = o[j] * m;
-        special |= !(fabsf(z[j]) <= 448.0f);
+        a[j] = __float_as_uint(z[j]) & 0x7fffffffu;   // |z| as bits: ordered like |z|, NaN above infinity
     }
+    // Largest magnitude by a balanced tree (4 dependent steps instead of a 16-long chain of tests):
+    // special iff some |z| > 448, an infinity or a NaN.
+#pragma unroll
+    for (int w = 8; w >= 1; w /= 2)
+#pragma unroll
+        for (int j = 0; j < w; ++j) a[j] = a[j] > a[j + w] ? a[j] : a[j + w];
+    const bool special = a[0] > 0x43e00000u;           // bits of 448.0f
     uint32_t w[4];
     if (!special) {
 #pragma unroll
