@@ -11,7 +11,8 @@ The metric has two parts, measured on two workloads:
     heads, fp8 caches of 10,240 pages per layer; 60 layer calls (each with its own input row, norm
     weights, scales and caches) captured once in a HIP graph and replayed.  Reported as
     `us_per_layer_call` and `us_per_decode_step`, with their own roofline under `decode`.
-Also reported: the indexer at decode batch 64 (`indexer`); the same decode step and prefill chunk
+Also reported: speculative-decoding verify rows, 64 sequences x (1 + 3) tokens through the same
+60-layer graph (`verify`); the indexer at decode batch 64 (`indexer`); the same decode step and prefill chunk
 through the unfused path (`unfused`: 14 launches per layer instead of one, identical bytes); and
 the packed projection of hidden states (hidden 3072) alone and with the producer as its epilogue,
 against torch.mm (hipBLASLt) followed by the producer (`projection`).
@@ -107,6 +108,58 @@ def bench_decode(msa, W, torch, layers, steps, warmup):
     bytes_per_call = wls[0].algorithmic_bytes()
     return dict(ms_total=ms, ms_per_step=ms / steps, bytes_per_call=bytes_per_call,
                 bytes_per_step=bytes_per_call * layers, launches=steps * layers, wls=wls, devs=devs)
+
+
+def bench_verify(msa, W, torch, np, wls, devs, steps, warmup, draft_len=3):
+    """Speculative-decoding verify rows through the same producer: 64 sequences x (1 + draft_len)
+    consecutive tokens (windows that cross page boundaries), one call per layer for the decode step's
+    layers, all captured in one HIP graph.  The caches, norm weights and scales of the decode layers
+    are reused (same pool geometry); each layer gets its own input rows and outputs."""
+    import dataclasses
+    vw = W.verify_window(draft_len=draft_len)
+    T = vw.T
+    pos = torch.from_numpy(vw.positions).cuda()
+    seq = torch.from_numpy(vw.seq_idx).cuda()
+    pt = torch.from_numpy(np.ascontiguousarray(vw.page_table)).cuda()
+    slots = torch.empty(T, dtype=torch.int64, device="cuda")
+    rng = np.random.default_rng(17)
+    vdevs = []
+    for wl, d in zip(wls, devs):
+        x = torch.from_numpy(W.to_bf16_bits(rng.standard_normal((T, wl.W), dtype=np.float32)).view(np.int16)).cuda()
+        q = torch.empty((T, wl.hq, wl.head_dim), dtype=torch.int16, device="cuda")
+        iq = torch.empty((T, wl.hiq, wl.head_dim), dtype=torch.int16, device="cuda")
+        vdevs.append(dataclasses.replace(d, x=x, positions=pos, seq_idx=seq, page_table=pt, q_out=q, iq_out=iq,
+                                         slots=slots))
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        for wl, d in zip(wls, vdevs):
+            call(msa, wl, d)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            for wl, d in zip(wls, vdevs):
+                call(msa, wl, d)
+    torch.cuda.synchronize()
+    log(f"[bench] verify-window graph captured ({len(wls)} launches of {T} tokens)")
+    with torch.cuda.stream(s):
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(steps):
+            g.replay()
+        e1.record(s)
+        torch.cuda.synchronize()
+    us_step = e0.elapsed_time(e1) * 1000 / steps
+    bytes_per_call = vw.algorithmic_bytes()      # the same heads and fp8 caches as the decode layers
+    us_call = us_step / len(wls)
+    return {"workload": f"{vw.name}; the decode layers' caches", "tokens": T, "draft_len": draft_len,
+            "layers": len(wls), "steps": steps, "warmup": warmup, "us_per_layer_call": us_call,
+            "us_per_step": us_step, "algorithmic_bytes_per_layer_call": bytes_per_call,
+            "algorithmic_gbs": bytes_per_call / (us_call * 1e-6) / 1e9}
 
 
 def unfused_call(msa, wl, d, slots, ws, stream=None):
@@ -449,6 +502,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-indexer", action="store_true", help="skip the indexer measurement")
     ap.add_argument("--no-unfused", action="store_true", help="skip the unfused-path comparison")
+    ap.add_argument("--no-verify", action="store_true", help="skip the verify-window decode measurement")
     ap.add_argument("--no-projection", action="store_true", help="skip the projection (GEMM + producer) measurement")
     ap.add_argument("--cpu-detail", action="store_true",
                     help="only time the CPU oracle (one thread and every host thread, decode batch 64 and a "
@@ -491,6 +545,8 @@ def main():
     us_call = us_step / args.layers
     launch_us = dec["ms_total"] * 1000 / dec["launches"]
     launch_gbs = dec["bytes_per_call"] / (launch_us * 1e-6) / 1e9
+    ver = None if args.no_verify else bench_verify(msa, W, torch, __import__("numpy"), dec["wls"], dec["devs"],
+                                                   args.decode_steps, args.decode_warmup)
     unf = None
     if not args.no_unfused:
         unf = bench_decode_unfused(msa, torch, dec["wls"], dec["devs"], args.decode_steps, args.decode_warmup)
@@ -555,6 +611,7 @@ def main():
                         "launches_per_call": pre.get("unfused_launches_per_call"),
                         "fused_us_per_call": pre["us_per_call"]},
         },
+        "verify": ver,
         "projection": proj,
         "indexer": idx,
         "cpu_baseline": cpu,
