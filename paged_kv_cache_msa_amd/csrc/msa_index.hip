@@ -289,7 +289,7 @@ constexpr int kRankRowBlocks = 512;
 __global__ __launch_bounds__(kBlock) void index_topk_rank_kernel(const double* scores, int32_t rows, int32_t nb,
                                                                  int32_t top_k, int32_t* ids, int32_t* counts)
 {
-    __shared__ double row_lds[kRankRowBlocks];
+    __shared__ __attribute__((aligned(16))) double row_lds[kRankRowBlocks];
     __shared__ int32_t n_lds[kWavesPerBlock];
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -298,14 +298,13 @@ __global__ __launch_bounds__(kBlock) void index_topk_rank_kernel(const double* s
     if (r >= rows) return;   // uniform over the work-group
     const double* row = scores + (int64_t)r * nb;
     int n_local = 0;
-    for (int32_t i = tid; i < nb; i += kBlock) {
-        const double v = row[i];
+    for (int32_t i0 = 0; i0 < nb; i0 += kBlock) {
+        const int32_t i = i0 + tid;
+        const double v = i < nb ? row[i] : -INFINITY;
         const bool cand = v > -INFINITY;              // -inf and NaN are never picked
-        row_lds[i] = cand ? v : -INFINITY;
-        n_local += cand;
+        if (i < nb) row_lds[i] = cand ? v : -INFINITY;
+        n_local += __popcll(__ballot(cand));          // the wave's candidates, counted once per wave
     }
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) n_local += __shfl_xor(n_local, m);
     if (lane == 0) n_lds[wave] = n_local;
     __syncthreads();
     int32_t n = 0;
@@ -318,10 +317,16 @@ __global__ __launch_bounds__(kBlock) void index_topk_rank_kernel(const double* s
         const double si = row_lds[i];
         if (!(si > -INFINITY)) continue;
         int32_t rank = 0;
-#pragma unroll 8
-        for (int32_t j = 0; j < nb; ++j) {
+        int32_t j = 0;
+#pragma unroll 4
+        for (; j + 1 < nb; j += 2) {                  // two entries per 16-byte LDS read
+            const double2 sj = *reinterpret_cast<const double2*>(&row_lds[j]);
+            rank += (sj.x > si || (sj.x == si && j < i)) ? 1 : 0;   // -inf entries never count
+            rank += (sj.y > si || (sj.y == si && j + 1 < i)) ? 1 : 0;
+        }
+        if (j < nb) {
             const double sj = row_lds[j];
-            rank += (sj > si || (sj == si && j < i)) ? 1 : 0;   // -inf entries never count
+            rank += (sj > si || (sj == si && j < i)) ? 1 : 0;
         }
         if (rank < top_k) out[rank] = i;
     }
