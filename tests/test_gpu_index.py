@@ -172,3 +172,60 @@ def test_topk_rows_with_ties_and_gaps(nb):
         rids, rc = oracle.index_topk(bs[None], k)
         np.testing.assert_array_equal(ids.cpu().numpy(), rids[0])
         np.testing.assert_array_equal(cnt.cpu().numpy(), rc[0])
+
+
+def test_index_graph_replay_matches_eager():
+    """Scores and top-k of three layers' index-K caches captured in one HIP graph: every replay, with
+    eager work and synchronisations between replays, reproduces the eager result bit for bit (and the
+    eager result is the oracle's)."""
+    wls = [W.decode_batch64(layer=i) for i in range(3)]
+    wl = wls[0]
+    nb = W.index_blocks(wl)
+    pos = torch.from_numpy(wl.positions).cuda()
+    seq = torch.from_numpy(wl.seq_idx).cuda()
+    pt = torch.from_numpy(np.ascontiguousarray(wl.page_table)).cuda()
+    layers = []
+    for i, lw in enumerate(wls):
+        fill = W.index_cache_fill(lw, seed=50 + i)
+        iq = W.index_queries(lw.T, lw.hiq, seed=60 + i)
+        st, view, scale = ik_device(lw, fill)
+        bs = torch.empty((lw.hiq, lw.T, nb), dtype=torch.float64, device="cuda")
+        ids = torch.empty((lw.hiq, lw.T, TOPK), dtype=torch.int32, device="cuda")
+        cnt = torch.empty((lw.hiq, lw.T), dtype=torch.int32, device="cuda")
+        layers.append(dict(lw=lw, fill=fill, iq=iq, iq_dev=torch.from_numpy(iq.view(np.int16)).cuda(), st=st,
+                           view=view, scale=scale, bs=bs, ids=ids, cnt=cnt))
+
+    def step():
+        for L in layers:
+            msa.msa_index_scores(L["iq_dev"], pos, seq, pt, L["view"], L["bs"], ik_scale=L["scale"],
+                                 num_pages=L["lw"].num_pages)
+            msa.msa_index_topk(L["bs"], L["ids"], L["cnt"])
+
+    say("[gpu] indexer: 3 layers eager, then captured and replayed 3 times")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.synchronize()
+    eager = [(L["bs"].cpu().numpy(), L["ids"].cpu().numpy(), L["cnt"].cpu().numpy()) for L in layers]
+    for L, got in zip(layers, eager):
+        compare("eager", got, oracle_index(L["lw"], L["iq"], L["fill"], nb))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for L in layers:                       # eager work between replays: clobber the outputs
+            L["bs"].fill_(float(rep))
+            L["ids"].fill_(-5)
+            L["cnt"].fill_(-5)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for L, (ebs, eids, ecnt) in zip(layers, eager):
+            gbs = L["bs"].cpu().numpy()
+            assert np.array_equal(gbs.view(np.int64), ebs.view(np.int64)), f"replay {rep}: block scores differ"
+            np.testing.assert_array_equal(L["ids"].cpu().numpy(), eids)
+            np.testing.assert_array_equal(L["cnt"].cpu().numpy(), ecnt)
+    say("  3 replays identical to the eager result")
