@@ -278,12 +278,14 @@ def mixed_batch_64bit(cache_dtype: int = BF16, seed: int = 4) -> Workload:
 
 
 def ragged(T: int, seed: int = 7, heads=DECODE_HEADS, cache_dtypes=(FP8_E4M3, FP8_E4M3, FP8_E4M3),
-           pad_frac: float = 0.1, sigma: float = 1.0, row_pad: int = 0) -> Workload:
+           pad_frac: float = 0.1, sigma: float = 1.0, row_pad: int = 0, page_size: int = PAGE_SIZE) -> Workload:
     """Arbitrary token count (ragged tails of the launch grid): T single-token sequences with
-    positions U{0..4095}, some padded, distinct pages, caches with mixed dtypes if asked."""
+    positions U{0..4095}, some padded, distinct pages, caches with mixed dtypes if asked, pages of
+    `page_size` tokens (any size; 4096 / page_size pages per sequence)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     hq, hkv, hiq, hik = heads
-    D, P, max_pages = HEAD_DIM, PAGE_SIZE, 64
+    D, P = HEAD_DIM, page_size
+    max_pages = -(-4096 // P)
     S = max(T, 1)
     num_pages = S * 2 + 7
     pos = rng.integers(0, 4096, T).astype(np.int32)
@@ -298,8 +300,9 @@ def ragged(T: int, seed: int = 7, heads=DECODE_HEADS, cache_dtypes=(FP8_E4M3, FP
     x = _normal_bf16(rng, (T, W + row_pad), sigma)
     w = _weights(rng, hq, hkv, hiq, hik, D)
     scales = rng.uniform(0.5, 2.0, 3)
-    caches = [_hnd_cache(num_pages, h, dt, s) for h, dt, s in zip((hkv, hkv, hik), cache_dtypes, scales)]
-    return Workload(f"ragged T={T}", hq, hkv, hiq, hik, D, P, num_pages, x, pos, seq, pt, w, caches,
+    caches = [_hnd_cache(num_pages, h, dt, s, page_size=P) for h, dt, s in zip((hkv, hkv, hik), cache_dtypes, scales)]
+    return Workload(f"ragged T={T}" + ("" if P == PAGE_SIZE else f", page size {P}"), hq, hkv, hiq, hik, D, P,
+                    num_pages, x, pos, seq, pt, w, caches,
                     n_invalid=int(np.count_nonzero(seq < 0)))
 
 

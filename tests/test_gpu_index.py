@@ -150,6 +150,21 @@ def test_index_other_block_sizes(block_tokens):
     compare(f"block {block_tokens}", got, oracle_index(wl, iq, fill, nb, block_tokens=block_tokens))
 
 
+@pytest.mark.parametrize("P", [16, 48, 100])
+def test_index_other_page_sizes(P):
+    """Page sizes other than 64 under 128-token blocks: a power of two, a multiple of 8 that takes the
+    division path, and one that is not a multiple of the 8-key step (per-key page lookups)."""
+    wl = W.ragged(48, seed=300 + P, pad_frac=0.1, page_size=P)
+    fill = W.index_cache_fill(wl, seed=P)
+    iq = W.index_queries(wl.T, wl.hiq, seed=P)
+    nb = int(wl.positions.max()) // 128 + 1
+    st, view, scale = ik_device(wl, fill)
+    dev = W.to_device(wl)
+    got = gpu_index(wl, torch.from_numpy(iq.view(np.int16)).cuda(), dev.positions, dev.seq_idx, dev.page_table,
+                    view, scale, nb)
+    compare(f"page size {P}", got, oracle_index(wl, iq, fill, nb))
+
+
 @pytest.mark.parametrize("nb", [100, 512, 513, 4096])
 def test_topk_rows_with_ties_and_gaps(nb):
     """Rows with repeated scores, -inf gaps and NaN entries; row lengths on both sides of the switch

@@ -179,6 +179,14 @@ def test_bf16_cache_scale_pointer_is_ignored(T):
     check(wl, d)
 
 
+@pytest.mark.parametrize("P,T", [(1, 300), (16, 2000), (48, 300), (48, 8000), (100, 300), (256, 8000)])
+def test_other_page_sizes(P, T):
+    """Page sizes other than 64: one token per page, a power of two, sizes that take the division
+    path (48, 100), and a large one; one-pass (T = 300) and multi-pass (T = 8000) launch shapes."""
+    wl = W.ragged(T, seed=P + T, cache_dtypes=(W.FP8_E4M3, W.BF16, W.FP8_E4M3), page_size=P)
+    check(wl, run(wl))
+
+
 def test_special_values():
     """NaN, infinities, huge and tiny values, all-zero heads and saturating scales."""
     wl = W.ragged(64, seed=77, cache_dtypes=(0, 0, 1), pad_frac=0.0)

@@ -87,6 +87,14 @@ def test_ragged_shapes(T, heads, dtypes, pad):
     check(wl, run(wl))
 
 
+@pytest.mark.parametrize("P,T", [(1, 300), (48, 2000), (100, 300)])
+def test_other_page_sizes(P, T):
+    """The per-cache division, remainder and index cast with page sizes other than 64 (one token per
+    page, and sizes that are not powers of two)."""
+    wl = W.ragged(T, seed=P + T + 1, cache_dtypes=(W.FP8_E4M3, W.BF16, W.FP8_E4M3), page_size=P)
+    check(wl, run(wl))
+
+
 def test_special_values():
     """NaN, infinities, huge and tiny values, all-zero heads and saturating scales."""
     wl = W.ragged(64, seed=78, cache_dtypes=(0, 0, 1), pad_frac=0.0)
