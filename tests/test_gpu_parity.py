@@ -187,6 +187,15 @@ def test_other_page_sizes(P, T):
     check(wl, run(wl))
 
 
+@pytest.mark.parametrize("theta,eps", [(1e6, 1e-5), (5e5, 0.0), (10.0, 1e-6)])
+def test_other_rope_theta_and_eps(theta, eps):
+    """RoPE bases and RMSNorm epsilons other than the workloads' 1e4 / 1e-6 (including eps = 0),
+    through the whole producer; positions up to 4095."""
+    wl = W.ragged(700, seed=int(theta) % 1000 + 5, cache_dtypes=(W.FP8_E4M3, W.FP8_E4M3, W.BF16))
+    wl.theta, wl.eps = theta, eps
+    check(wl, run(wl))
+
+
 def test_special_values():
     """NaN, infinities, huge and tiny values, all-zero heads and saturating scales."""
     wl = W.ragged(64, seed=77, cache_dtypes=(0, 0, 1), pad_frac=0.0)
