@@ -165,6 +165,32 @@ def test_index_other_page_sizes(P):
     compare(f"page size {P}", got, oracle_index(wl, iq, fill, nb))
 
 
+@pytest.mark.parametrize("dtype", [W.FP8_E4M3, W.BF16], ids=["fp8", "bf16"])
+def test_index_special_values(dtype):
+    """NaN keys (fp8 codes S.1111.111, bf16 NaN), infinite bf16 keys and a query row holding a NaN: a
+    NaN score never wins a block, +-inf scores rank as the extremes they are."""
+    wl = W.ragged(96, seed=410 + dtype, pad_frac=0.05, cache_dtypes=(W.FP8_E4M3, W.FP8_E4M3, dtype))
+    fill = W.index_cache_fill(wl, seed=411)
+    rng = np.random.default_rng(412)
+    n = fill.size
+    if dtype == W.FP8_E4M3:
+        fill[rng.choice(n, n // 100, replace=False)] = rng.choice(np.array([0x7F, 0xFF], np.uint8), n // 100)
+    else:
+        pick = rng.choice(n, n // 500, replace=False)
+        fill[pick] = rng.choice(np.array([0x7F80, 0xFF80, 0x7FC0, 0xFFC1], np.uint16), pick.size)
+    iq = W.index_queries(wl.T, wl.hiq, seed=413)
+    iq[5, 0, 17] = 0x7FC0                     # one query row of one head holds a NaN
+    iq[9, 1, 3] = 0x7F80                      # another holds +inf
+    nb = int(wl.positions.max()) // 128 + 1
+    st, view, scale = ik_device(wl, fill)
+    dev = W.to_device(wl)
+    got = gpu_index(wl, torch.from_numpy(iq.view(np.int16)).cuda(), dev.positions, dev.seq_idx, dev.page_table,
+                    view, scale, nb)
+    ref = oracle_index(wl, iq, fill, nb)
+    assert dtype == W.FP8_E4M3 or np.isposinf(ref[0]).any()      # the +inf case is exercised
+    compare(f"special values ({'fp8' if dtype == W.FP8_E4M3 else 'bf16'})", got, ref)
+
+
 @pytest.mark.parametrize("nb", [100, 512, 513, 4096])
 def test_topk_rows_with_ties_and_gaps(nb):
     """Rows with repeated scores, -inf gaps and NaN entries; row lengths on both sides of the switch
