@@ -40,29 +40,32 @@ METRIC = "producer HBM GB/s (% of peak) + µs per layer call at decode batch 64"
 KERNEL_SRCS = [os.path.join(ROOT, "paged_kv_cache_msa_amd", "csrc", n)
                for n in ("msa_produce.hip", "msa_device.h", "msa_common.h")]
 COUNTERS = os.path.join(ROOT, "profiles", "produce_kernel_hbm_counters.json")
+# the indexer's kernels and their counter record
+INDEX_SRCS = [os.path.join(ROOT, "paged_kv_cache_msa_amd", "csrc", n) for n in ("msa_index.hip", "msa_common.h")]
+INDEX_COUNTERS = os.path.join(ROOT, "profiles", "index_kernels_hbm_counters.json")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_digest() -> str:
+def kernel_digest(srcs=None) -> str:
     h = hashlib.sha256()
-    for path in KERNEL_SRCS:
+    for path in KERNEL_SRCS if srcs is None else srcs:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def counter_traffic(workload_key: str):
+def counter_traffic(workload_key: str, path=None, srcs=None):
     """Measured HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel
     calibration) if they were taken on the current kernel source; else None."""
     try:
-        with open(COUNTERS) as f:
+        with open(COUNTERS if path is None else path) as f:
             c = json.load(f)
     except (OSError, ValueError):
         return None
-    if c.get("kernel_sha256_16") != kernel_digest():
+    if c.get("kernel_sha256_16") != (kernel_digest() if srcs is None else kernel_digest(srcs)):
         return None
     return c.get("bytes_per_launch", {}).get(workload_key)
 
@@ -305,7 +308,8 @@ def bench_indexer(msa, W, torch, np, reps):
                          f"{nb} blocks of 128 tokens, top 16",
                 us_per_call=us, algorithmic_bytes_per_call=b,
                 roofline=dict(bound="hbm", achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=gbs / HBM_PEAK_GBS,
-                              traffic=None, kernel="index_scores_kernel<2> + index_topk_kernel"))
+                              traffic=counter_traffic("decode_64_indexer_call", INDEX_COUNTERS, INDEX_SRCS),
+                              kernel="index_scores_kernel<2> + index_topk_kernel"))
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0

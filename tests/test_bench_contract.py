@@ -25,10 +25,10 @@ def test_counter_traffic_only_for_the_profiled_source(monkeypatch, tmp_path):
     path = tmp_path / "counters.json"
     path.write_text(json.dumps(rec))
     monkeypatch.setattr(bench, "COUNTERS", str(path))
-    monkeypatch.setattr(bench, "kernel_digest", lambda: "0123456789abcdef")
+    monkeypatch.setattr(bench, "kernel_digest", lambda *a: "0123456789abcdef")
     assert bench.counter_traffic("prefill_65536") == 123.0
     assert bench.counter_traffic("decode_64") is None
-    monkeypatch.setattr(bench, "kernel_digest", lambda: "fedcba9876543210")
+    monkeypatch.setattr(bench, "kernel_digest", lambda *a: "fedcba9876543210")
     assert bench.counter_traffic("prefill_65536") is None
 
 
