@@ -3,14 +3,17 @@
 The metric has two parts, measured on two workloads:
   * producer HBM GB/s (% of peak): the 65,536-token prefill chunk (8 sequences x 8192 tokens, local
     heads Q=16 / KV=2 / index-Q=2 / index-K=1, head_dim 128, fp8 e4m3 HND caches in a 12,000-page
-    pool).  A step is one msa_produce launch over the whole chunk; `--warmup` untimed steps (the
-    engine clock needs tens of milliseconds of load to settle), then `--steps` timed ones, with
-    HIP events on the launch stream, alternating two input sets.  `value`, `ms_per_step` and
-    `roofline` are this kernel's.
+    pool).  A step is one msa_produce launch over the whole chunk.  The prefill runs first, on input
+    staged before any device work: at least `--warmup` untimed steps, continued until `--warm-ms`
+    of device time has run (the engine clock needs tens of milliseconds of load to settle), then
+    `--steps` timed ones, with HIP events on the launch stream, alternating two input sets.
+    `value`, `ms_per_step` and `roofline` are this kernel's.
   * us per layer call at decode batch 64: 64 sequences x 1 token at positions 7000..9199, the same
-    heads, fp8 caches of 10,240 pages per layer; 60 layer calls (each with its own input row, norm
-    weights, scales and caches) captured once in a HIP graph and replayed.  Reported as
-    `us_per_layer_call` and `us_per_decode_step`, with their own roofline under `decode`.
+    heads, fp8 caches of 10,240 pages per layer; one step = every position advanced by one in place,
+    then 60 layer calls (each with its own input row, norm weights, scales and caches), captured
+    once in a HIP graph and replayed, so every replay writes new slots.  Reported as
+    `us_per_layer_call` (step time / 60) and `us_per_decode_step`, with their own roofline under
+    `decode`.
 Also reported: speculative-decoding verify rows, 64 sequences x (1 + 3) tokens through the same
 60-layer graph (`verify`); the indexer at decode batch 64 (`indexer`); the same decode step and prefill chunk
 through the unfused path (`unfused`: 14 launches per layer instead of one, identical bytes); and
@@ -19,7 +22,7 @@ against torch.mm (hipBLASLt) followed by the producer (`projection`).
 Inputs are resident in HBM before every timed region.  `cpu_baseline` is the CPU oracle on a
 bounded sample of the prefill workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers 60] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--warm-ms MS] [--layers 60] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -78,25 +81,38 @@ def call(msa, wl, d, stream=None):
 
 
 def bench_decode(msa, W, torch, layers, steps, warmup):
+    """The decode step: every replay first advances each sequence's position by one in place (one
+    small elementwise node), then runs the `layers` producer launches, which read the new positions
+    from the same device buffers: consecutive steps write new slots and cross page boundaries, as a
+    serving loop that updates its metadata in place and replays the captured step does."""
     log(f"[bench] staging {layers} decode-64 layers")
     wls = [W.decode_batch64(layer=i) for i in range(layers)]
     devs = [W.to_device(wl) for wl in wls]
     # share the metadata buffers across layers (one batch, many layers)
     for d in devs[1:]:
         d.positions, d.seq_idx, d.page_table = devs[0].positions, devs[0].seq_idx, devs[0].page_table
+    # the page table covers 160 pages (10,240 positions) per sequence: room for every replay
+    replays = 1 + warmup + steps
+    assert int(wls[0].positions.max()) + replays < wls[0].max_pages * wls[0].page_size
+    pos = devs[0].positions
     torch.cuda.synchronize()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     g = torch.cuda.CUDAGraph()
+
+    def step():
+        pos.add_(1)
+        for wl, d in zip(wls, devs):
+            call(msa, wl, d)
+
     with torch.cuda.stream(s):
         for wl, d in zip(wls, devs):      # one eager pass before capture
             call(msa, wl, d)
         torch.cuda.synchronize()
         with torch.cuda.graph(g, stream=s):
-            for wl, d in zip(wls, devs):
-                call(msa, wl, d)
+            step()
     torch.cuda.synchronize()
-    log(f"[bench] decode graph captured ({layers} launches); warmup {warmup}, timing {steps} steps")
+    log(f"[bench] decode graph captured (position update + {layers} launches); warmup {warmup}, timing {steps} steps")
     with torch.cuda.stream(s):
         for _ in range(warmup):
             g.replay()
@@ -218,16 +234,30 @@ def bench_decode_unfused(msa, torch, wls, devs, steps, warmup):
                 steps=steps, warmup=warmup)
 
 
-def bench_prefill(msa, W, torch, iters, warmup, unfused_iters=0):
+def stage_prefill(W, torch):
     log("[bench] staging the 65,536-token prefill chunk (two input sets)")
     sets = [W.prefill_65536(variant=v) for v in range(2)]
     devs = [W.to_device(wl) for wl in sets]
     torch.cuda.synchronize()
+    return sets, devs
+
+
+def bench_prefill(msa, W, torch, iters, warmup, warm_ms, staged, unfused_iters=0):
+    """`warmup` launches, then more back to back until at least `warm_ms` of device time has run (the
+    engine clock settles only after tens of milliseconds of load), then `iters` timed launches."""
+    sets, devs = staged
     s = torch.cuda.current_stream()
-    for i in range(warmup):
-        call(msa, sets[i % 2], devs[i % 2])
-    torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    warm_launches, warm_elapsed = 0, 0.0
+    e0.record(s)
+    while warm_launches < warmup or warm_elapsed < warm_ms:
+        for _ in range(50):
+            call(msa, sets[warm_launches % 2], devs[warm_launches % 2])
+            warm_launches += 1
+        e1.record(s)
+        e1.synchronize()
+        warm_elapsed = e0.elapsed_time(e1)
+    log(f"[bench] prefill warm: {warm_launches} launches, {warm_elapsed:.1f} ms")
     e0.record(s)
     for i in range(iters):
         call(msa, sets[i % 2], devs[i % 2])
@@ -237,7 +267,7 @@ def bench_prefill(msa, W, torch, iters, warmup, unfused_iters=0):
     b = sets[0].algorithmic_bytes()
     us = ms * 1000 / iters
     gbs = b / (us * 1e-6) / 1e9
-    out = dict(us_per_call=us, bytes=b, gbs=gbs, launches=iters)
+    out = dict(us_per_call=us, bytes=b, gbs=gbs, launches=iters, warm_launches=warm_launches, warm_ms=warm_elapsed)
     if unfused_iters:
         # the same chunk through the unfused path (slots from the fused calls above)
         ws = torch.empty(msa.msa_produce_unfused_workspace_size(sets[0].T, sets[0].hkv, sets[0].hik),
@@ -440,10 +470,17 @@ def bench_projection(msa, W, torch, np, layers, steps, warmup):
     return out
 
 
+def host_threads():
+    """(threads the CPU oracle runs on, cores this process may use): one GPU's share of the host is 16
+    threads, so at most 16 of the usable cores."""
+    cores = len(os.sched_getaffinity(0))
+    return min(16, cores), cores
+
+
 def cpu_baseline(W, seconds: float):
     """The CPU oracle as it stands, on leading slices of the prefill workload for about `seconds`."""
     import oracle
-    threads = min(16, os.cpu_count() or 1)
+    threads, cores = host_threads()
     wl = W.prefill_65536()
     rows = 4096
     args = (wl.x, wl.x_stride, rows, wl.head_dim, wl.hq, wl.hkv, wl.hiq, wl.hik, wl.positions[:rows],
@@ -460,9 +497,10 @@ def cpu_baseline(W, seconds: float):
             break
     per_call = el / n
     bytes_per_call = wl.algorithmic_bytes() * rows / wl.T
-    return dict(value=bytes_per_call / per_call / 1e9, unit="GB/s", cores=threads, kind="oracle",
+    return dict(value=bytes_per_call / per_call / 1e9, unit="GB/s", cores=threads, host_cores=cores, kind="oracle",
                 sample=f"{n} oracle calls on the first {rows} tokens of the 65,536-token prefill (all heads, fp8 "
-                       f"cache codes in the dense per-token form), {threads} OpenMP threads, {el:.1f} s: "
+                       f"cache codes in the dense per-token form), {threads} OpenMP threads (one GPU's share of "
+                       f"the host; {cores} cores usable by this process), {el:.1f} s: "
                        f"{per_call * 1e3:.1f} ms per {rows} tokens")
 
 
@@ -475,7 +513,7 @@ def cpu_detail(W, seconds: float):
         args = (wl.x, wl.x_stride, rows, wl.head_dim, wl.hq, wl.hkv, wl.hiq, wl.hik, wl.positions[:rows],
                 wl.seq_idx[:rows], wl.page_table, wl.max_pages, wl.num_seqs, wl.max_pages, wl.page_size,
                 wl.num_pages, *wl.weights, wl.eps, wl.theta)
-        for threads in (1, min(16, os.cpu_count() or 1)):
+        for threads in (1, host_threads()[0]):
             kw = dict(dtypes=[c.dtype for c in wl.caches], scales=[c.scale for c in wl.caches], num_threads=threads)
             oracle.produce_rows(*args, **kw)
             n, t0 = 0, time.perf_counter()
@@ -497,8 +535,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200, help="timed prefill launches")
-    ap.add_argument("--warmup", type=int, default=300,
-                    help="untimed prefill launches first; the engine clock takes tens of ms of load to settle")
+    ap.add_argument("--warmup", type=int, default=300, help="untimed prefill launches first (at least)")
+    ap.add_argument("--warm-ms", type=float, default=300.0,
+                    help="untimed prefill launches continue until this much device time has run: the engine "
+                         "clock takes tens of ms of load to settle")
     ap.add_argument("--layers", type=int, default=60)
     ap.add_argument("--decode-steps", type=int, default=200, help="timed 60-layer decode graph replays")
     ap.add_argument("--decode-warmup", type=int, default=100)
@@ -522,8 +562,9 @@ def main():
 
     if args.cpu_detail:
         from paged_kv_cache_msa_amd import workloads as W
-        print(json.dumps({"cpu_oracle": cpu_detail(W, args.cpu_seconds / 4), "host_threads": os.cpu_count()}),
-              flush=True)
+        threads, cores = host_threads()
+        print(json.dumps({"cpu_oracle": cpu_detail(W, args.cpu_seconds / 4), "threads": threads,
+                          "host_cores": cores}), flush=True)
         return
 
     import torch
@@ -544,6 +585,11 @@ def main():
         print(json.dumps({"copy_calibration_bytes_each": src.numel() * 4, "copies": 3}), flush=True)
         return
 
+    # The prefill runs first, on input staged before any device work, so that nothing but its own
+    # warm phase precedes its timed launches.
+    pre = bench_prefill(msa, W, torch, args.steps, args.warmup, args.warm_ms, stage_prefill(W, torch),
+                        0 if args.no_unfused else 50)
+    torch.cuda.empty_cache()
     dec = bench_decode(msa, W, torch, args.layers, args.decode_steps, args.decode_warmup)
     us_step = dec["ms_per_step"] * 1000
     us_call = us_step / args.layers
@@ -562,7 +608,6 @@ def main():
     torch.cuda.empty_cache()
     proj = None if args.no_projection else bench_projection(msa, W, torch, np, args.layers, args.steps, args.warmup)
     torch.cuda.empty_cache()
-    pre = bench_prefill(msa, W, torch, args.steps, args.warmup, 0 if args.no_unfused else 50)
     cpu = None if args.no_cpu_baseline else cpu_baseline(W, args.cpu_seconds)
 
     line = {
@@ -597,9 +642,12 @@ def main():
             "bound": "hbm", "achieved": pre["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": pre["gbs"] / HBM_PEAK_GBS, "traffic": counter_traffic("prefill_65536"),
             "kernel": "produce_kernel<3, 16, 2, 2, 1> (prefill)", "avg_launch_us": pre["us_per_call"],
+            "warm_launches": pre["warm_launches"], "warm_ms": pre["warm_ms"],
         },
         "decode": {
             "steps": args.decode_steps, "warmup": args.decode_warmup, "layers": args.layers,
+            "step": "positions advanced by one in place (one elementwise node), then one producer launch per "
+                    "layer; every replay writes new slots",
             "us_per_layer_call": us_call, "us_per_step": us_step,
             "roofline": {
                 "bound": "hbm", "achieved": launch_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -21,7 +21,7 @@
  * 1/sqrt(head_dim) factor are monotone within one (t, h) and leave the selection unchanged; they are
  * not applied.  A token without a valid cache slot of its own (padded) selects nothing.
  *
- * Conventions are those of msa_produce.h: device pointers unchecked for residency, no allocation,
+ * Conventions are those of msa_produce.h: operands checked for residency on eager calls, no allocation,
  * no synchronisation, all checks on the host before any launch (an error leaves every byte
  * unchanged), MSA_OK means enqueued, graph-capture safe.
  */

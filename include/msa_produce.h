@@ -22,10 +22,15 @@
  *   NaN inputs give NaN outputs of the same sign.
  *
  * Conventions of every entry point:
- *   - Pointers marked "device" must be device-accessible memory of the current HIP device; they
- *     are not checked for that (a host pointer faults on the device).  The library allocates
- *     nothing, keeps no pointer after it returns, performs no host<->device copy and no
- *     synchronisation, so every call may be captured into a HIP graph.
+ *   - Pointers marked "device" must be memory that kernels on the current HIP device can access:
+ *     device memory of that device, managed memory, or pinned host memory mapped at the same
+ *     address.  An eager call (its stream not being captured into a graph) checks this for every
+ *     operand before launching, together with the operand's extent (the bytes the call may touch
+ *     must lie inside the allocation the runtime reports), and returns MSA_ERR_NOT_DEVICE without
+ *     launching when a check fails (msa_check_device_pointers runs the same check alone).  While the
+ *     stream is being captured the check is skipped: the caller keeps captured operands valid for
+ *     every replay.  The library allocates nothing, keeps no pointer after it returns, performs no
+ *     host<->device copy and no synchronisation, so every call may be captured into a HIP graph.
  *   - `stream` is a hipStream_t (NULL = the null stream).  MSA_OK means the work was enqueued;
  *     device-side faults surface at the caller's next synchronisation.
  *   - Every argument check runs on the host before any launch: on any status other than MSA_OK
@@ -53,7 +58,9 @@ typedef enum msa_status {
     MSA_ERR_DTYPE = 6,          /* unknown cache dtype, or an fp8 cache without a scale */
     MSA_ERR_OVERFLOW = 7,       /* a cache element offset does not fit in int64 */
     MSA_ERR_LAUNCH = 8,         /* the HIP runtime refused the launch */
-    MSA_ERR_WORKSPACE = 9       /* a caller-provided workspace is too small or misaligned */
+    MSA_ERR_WORKSPACE = 9,      /* a caller-provided workspace is too small or misaligned */
+    MSA_ERR_NOT_DEVICE = 10     /* an operand is not accessible from the current device, or the bytes
+                                   the call would touch run past the end of its allocation */
 } msa_status;
 
 typedef enum msa_cache_dtype {
@@ -159,8 +166,24 @@ msa_status msa_quantize(const float* values, int64_t n, int32_t dtype, const flo
 msa_status msa_rms_scale(const double* sum_sq, int64_t n, int32_t head_dim, float rms_eps, float* r_out,
                          void* stream);
 
+/*
+ * msa_check_device_pointers — the operand check of eager calls, alone (launches nothing).
+ *
+ * ptrs     host array [n] of pointers; NULL entries pass.
+ * bytes    host array [n]: bytes from ptrs[i] that a kernel may touch (NULL: one byte each).
+ * n        >= 0.
+ * first_bad optional: the index of the first pointer that fails, or -1.
+ * Returns MSA_OK when every pointer is accessible from the current device with its whole extent
+ * inside its allocation, MSA_ERR_NOT_DEVICE otherwise (also when no device is present), and
+ * MSA_ERR_NULL_POINTER / MSA_ERR_SHAPE for a NULL ptrs array with n > 0 / n < 0.
+ */
+msa_status msa_check_device_pointers(const void* const* ptrs, const uint64_t* bytes, int32_t n, int32_t* first_bad);
+
 /* Static English text for a status code. */
 const char* msa_status_string(msa_status status);
+
+/* The same text under the shorter name. */
+const char* msa_status_str(msa_status status);
 
 #ifdef __cplusplus
 }

@@ -28,7 +28,7 @@
  * slices in a fixed order and runs the epilogue; for larger batches (prefill) one 256 x 256 tiled
  * kernel.  All on v_mfma_f32_32x32x16_bf16.
  *
- * Conventions are those of msa_produce.h (device pointers unchecked for residency, no allocation,
+ * Conventions are those of msa_produce.h (operands checked for residency on eager calls, no allocation,
  * no synchronisation, all checks on the host before any launch, MSA_OK means enqueued,
  * graph-capture safe).
  */

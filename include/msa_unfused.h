@@ -27,7 +27,7 @@
  * to its element size, where msa_produce requires strides in multiples of 8 elements and a 16-byte
  * aligned base (MSA_ERR_STRIDE / MSA_ERR_ALIGNMENT there).
  *
- * Conventions are those of msa_produce.h: device pointers unchecked for residency, no allocation
+ * Conventions are those of msa_produce.h: operands checked for residency on eager calls, no allocation
  * (intermediates live in the caller's workspace), no synchronisation, every check on the host
  * before any launch (an error leaves every byte unchanged), MSA_OK means enqueued, graph-capture
  * safe.

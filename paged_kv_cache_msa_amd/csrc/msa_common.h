@@ -29,11 +29,13 @@ inline bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintp
 // Validates a cache view of `heads` heads over `num_pages` pages of `page_size` tokens and fills its
 // device form.  heads == 0: nothing to check, the descriptor may be NULL.  `vec`: the fused
 // producer's layout (16-byte aligned base, strides multiples of 8 elements); otherwise any positive
-// strides and a base aligned to the element size.
+// strides and a base aligned to the element size.  `span`: if given, receives the bytes from the
+// view's base to one past its last element (0 without heads).
 inline msa_status check_cache(const msa_cache_view* v, int32_t heads, int32_t page_size, int64_t num_pages, CacheDev* out,
-                              bool vec = true)
+                              bool vec = true, uint64_t* span = nullptr)
 {
     std::memset(out, 0, sizeof(*out));
+    if (span) *span = 0;
     if (heads == 0) return MSA_OK;
     if (!v || !v->data) return MSA_ERR_NULL_POINTER;
     if (v->num_heads != heads) return MSA_ERR_SHAPE;
@@ -64,6 +66,7 @@ inline msa_status check_cache(const msa_cache_view* v, int32_t heads, int32_t pa
     int64_t bytes;
     if (__builtin_mul_overflow(max_off + 1, (int64_t)(v->dtype == MSA_CACHE_BF16 ? 2 : 1), &bytes))
         return MSA_ERR_OVERFLOW;
+    if (span) *span = num_pages > 0 ? (uint64_t)bytes : 0;
     out->data = static_cast<uint8_t*>(v->data);
     out->sp = s[0];
     out->sh = s[1];
@@ -72,6 +75,103 @@ inline msa_status check_cache(const msa_cache_view* v, int32_t heads, int32_t pa
     out->heads = heads;
     out->is_bf16 = v->dtype == MSA_CACHE_BF16;
     return MSA_OK;
+}
+
+// ------------------------------------------------------------------ residency of the kernels' operands
+
+// One operand of a launch: the bytes [p, p + bytes) its kernels may touch.
+struct Span {
+    const void* p;
+    uint64_t bytes;
+};
+
+// Whether kernels on device `device` may touch [p, p + bytes): the HIP runtime knows the memory, it
+// is device memory of that device, managed memory, or pinned host memory mapped at the same
+// address, and the range lies inside its allocation (where the runtime reports the allocation's
+// extent).  NULL or empty spans pass.  A failed runtime query leaves no error behind for later calls.
+inline bool span_resident(const Span& s, int device)
+{
+    if (!s.p || s.bytes == 0) return true;
+    hipPointerAttribute_t at;
+    if (hipPointerGetAttributes(&at, s.p) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    switch (at.type) {
+        case hipMemoryTypeDevice:
+            if (at.device != device) return false;
+            break;
+        case hipMemoryTypeManaged:
+            break;
+        case hipMemoryTypeHost:
+            if (at.devicePointer != s.p) return false;
+            break;
+        default:
+            return false;
+    }
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    if (hipMemGetAddressRange(&base, &size, const_cast<void*>(s.p)) != hipSuccess) {
+        (void)hipGetLastError();
+        return true;      // extent not reported (the kind of memory is already known to be accessible)
+    }
+    const uintptr_t b = reinterpret_cast<uintptr_t>(base), q = reinterpret_cast<uintptr_t>(s.p);
+    return q >= b && q - b <= size && s.bytes <= size - (q - b);
+}
+
+// The residency check of n spans on the current device; *first_bad = index of the first failing
+// span (or -1).
+inline msa_status spans_resident(const Span* s, int n, int32_t* first_bad)
+{
+    if (first_bad) *first_bad = -1;
+    int device = -1;
+    for (int i = 0; i < n; ++i) {
+        if (!s[i].p || s[i].bytes == 0) continue;
+        bool ok = true;
+        if (device < 0 && hipGetDevice(&device) != hipSuccess) {
+            (void)hipGetLastError();
+            device = -1;
+            ok = false;
+        }
+        if (!ok || !span_resident(s[i], device)) {
+            if (first_bad) *first_bad = i;
+            return MSA_ERR_NOT_DEVICE;
+        }
+    }
+    return MSA_OK;
+}
+
+// What every launching entry point runs after its argument checks and before its first launch:
+// the residency check of its operands, for eager calls.  While `stream` is being captured into a
+// graph nothing runs here (no runtime query beyond the capture status), since the captured
+// pointers are the caller's to keep alive and valid for every replay.
+inline msa_status check_operands(const Span* s, int n, hipStream_t stream)
+{
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
+        (void)hipGetLastError();
+        return MSA_ERR_LAUNCH;
+    }
+    if (cs != hipStreamCaptureStatusNone) return MSA_OK;
+    return spans_resident(s, n, nullptr);
+}
+
+// Bytes of `count` elements of `elem` bytes, saturating (a saturated extent fails the check).
+inline uint64_t nbytes(int64_t count, int64_t elem)
+{
+    if (count <= 0) return 0;
+    int64_t b;
+    return __builtin_mul_overflow(count, elem, &b) ? UINT64_MAX : (uint64_t)b;
+}
+
+// Bytes a row view of `rows` rows of `row_elems` elements at a stride of `stride` elements spans.
+inline uint64_t row_bytes(int64_t rows, int64_t stride, int64_t row_elems, int64_t elem)
+{
+    if (rows <= 0 || row_elems <= 0) return 0;
+    int64_t last;
+    if (__builtin_mul_overflow(rows - 1, stride, &last) || __builtin_add_overflow(last, row_elems, &last))
+        return UINT64_MAX;
+    return nbytes(last, elem);
 }
 
 // inv_freq_i = 1 / theta^(2i/D) in binary64 (one rounding each for the exponent, pow and the

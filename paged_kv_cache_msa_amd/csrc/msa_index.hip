@@ -23,7 +23,11 @@ namespace {
 using msa_internal::aligned;
 using msa_internal::CacheDev;
 using msa_internal::check_cache;
+using msa_internal::check_operands;
 using msa_internal::kHeadDim;
+using msa_internal::nbytes;
+using msa_internal::row_bytes;
+using msa_internal::Span;
 
 constexpr int kWave = 64;
 constexpr int kWavesPerBlock = 4;
@@ -392,7 +396,8 @@ msa_status msa_index_scores(const uint16_t* iq, int32_t num_tokens, int32_t head
     const int32_t hik = ik_cache->num_heads;
     if (hik < 1 || num_iq_heads % hik) return MSA_ERR_SHAPE;
     CacheDev ik;
-    const msa_status st = check_cache(ik_cache, hik, page_size, num_pages, &ik);
+    uint64_t ik_span;
+    const msa_status st = check_cache(ik_cache, hik, page_size, num_pages, &ik, true, &ik_span);
     if (st != MSA_OK) return st;
     if (num_tokens > 0 && max_blocks > 0) {
         if (!iq || !positions || !seq_idx || !block_scores) return MSA_ERR_NULL_POINTER;
@@ -429,6 +434,19 @@ msa_status msa_index_scores(const uint16_t* iq, int32_t num_tokens, int32_t head
     a.out = block_scores;
     const dim3 grid((unsigned)((items + kWavesPerBlock / kParts - 1) / (kWavesPerBlock / kParts)));
     hipStream_t s = static_cast<hipStream_t>(stream);
+    {
+        const Span spans[] = {
+            {iq, nbytes((int64_t)num_tokens * num_iq_heads * kHeadDim, 2)},
+            {positions, nbytes(num_tokens, 4)},
+            {seq_idx, nbytes(num_tokens, 4)},
+            {page_table, num_seqs > 0 ? row_bytes(num_seqs, page_table_stride, max_pages_per_seq, 4) : 0},
+            {ik.data, ik_span},
+            {ik.scale, 4},
+            {block_scores, nbytes((int64_t)num_iq_heads * items, 8)},
+        };
+        const msa_status cs = check_operands(spans, sizeof(spans) / sizeof(spans[0]), s);
+        if (cs != MSA_OK) return cs;
+    }
     // Launches over pairs of index-Q heads that read the same index-K head (two heads' queries fit
     // the registers at once).
     for (int32_t h0 = 0; h0 < num_iq_heads;) {
@@ -463,6 +481,11 @@ msa_status msa_index_topk(const double* block_scores, int32_t rows, int32_t max_
     if (rows == 0) return MSA_OK;
     if (!block_ids || (max_blocks > 0 && !block_scores)) return MSA_ERR_NULL_POINTER;
     if (!aligned(block_scores, 8) || !aligned(block_ids, 4) || !aligned(counts, 4)) return MSA_ERR_ALIGNMENT;
+    const Span spans[] = {{block_scores, nbytes((int64_t)rows * max_blocks, 8)},
+                          {block_ids, nbytes((int64_t)rows * top_k, 4)},
+                          {counts, nbytes(rows, 4)}};
+    const msa_status st = check_operands(spans, 3, static_cast<hipStream_t>(stream));
+    if (st != MSA_OK) return st;
     const bool rank = max_blocks <= kRankRowBlocks;
     const dim3 grid(rank ? (unsigned)rows : (unsigned)(((int64_t)rows + kWavesPerBlock - 1) / kWavesPerBlock));
     void* args[] = {const_cast<double**>(&block_scores), &rows, &max_blocks, &top_k, &block_ids, &counts};

@@ -453,9 +453,13 @@ msa_status msa_produce(const uint16_t* x, int64_t x_row_stride, int32_t num_toke
     ProduceArgs a;
     std::memset(&a, 0, sizeof(a));
     msa_status st;
-    if ((st = check_cache(k_cache, num_kv_heads, page_size, num_pages, &a.cache[0])) != MSA_OK) return st;
-    if ((st = check_cache(v_cache, num_kv_heads, page_size, num_pages, &a.cache[1])) != MSA_OK) return st;
-    if ((st = check_cache(ik_cache, num_ik_heads, page_size, num_pages, &a.cache[2])) != MSA_OK) return st;
+    uint64_t cache_span[3];
+    if ((st = check_cache(k_cache, num_kv_heads, page_size, num_pages, &a.cache[0], true, &cache_span[0])) != MSA_OK)
+        return st;
+    if ((st = check_cache(v_cache, num_kv_heads, page_size, num_pages, &a.cache[1], true, &cache_span[1])) != MSA_OK)
+        return st;
+    if ((st = check_cache(ik_cache, num_ik_heads, page_size, num_pages, &a.cache[2], true, &cache_span[2])) != MSA_OK)
+        return st;
     int64_t slot_max;
     if (__builtin_mul_overflow(num_pages, (int64_t)page_size, &slot_max)) return MSA_ERR_OVERFLOW;
     if (num_tokens == 0) return MSA_OK;
@@ -497,6 +501,22 @@ msa_status msa_produce(const uint16_t* x, int64_t x_row_stride, int32_t num_toke
     if ((int64_t)num_tokens * a.waves_per_token + kWavesPerBlock > 0x7fffffffLL) return MSA_ERR_SHAPE;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
+    {
+        const Span spans[] = {
+            {x, row_bytes(num_tokens, x_row_stride, heads_total * kHeadDim, 2)},
+            {positions, nbytes(num_tokens, 4)},
+            {seq_idx, nbytes(num_tokens, 4)},
+            {page_table, num_seqs > 0 ? row_bytes(num_seqs, page_table_stride, max_pages_per_seq, 4) : 0},
+            {q_norm_weight, 2 * kHeadDim}, {k_norm_weight, 2 * kHeadDim},
+            {iq_norm_weight, 2 * kHeadDim}, {ik_norm_weight, 2 * kHeadDim},
+            {q_out, nbytes((int64_t)num_tokens * num_q_heads * kHeadDim, 2)},
+            {iq_out, nbytes((int64_t)num_tokens * num_iq_heads * kHeadDim, 2)},
+            {a.cache[0].data, cache_span[0]}, {a.cache[1].data, cache_span[1]}, {a.cache[2].data, cache_span[2]},
+            {a.cache[0].scale, 4}, {a.cache[1].scale, 4}, {a.cache[2].scale, 4},
+            {slots_out, nbytes(num_tokens, 8)},
+        };
+        if ((st = check_operands(spans, sizeof(spans) / sizeof(spans[0]), s)) != MSA_OK) return st;
+    }
     hipError_t e;
     // Builds specialised for the head geometry of one tensor-parallel rank (16/2/2/1); any other
     // geometry runs the generic build.
@@ -525,6 +545,9 @@ msa_status msa_rope_table(const int32_t* positions, int64_t n, double rope_theta
     const int64_t total = n * kHalf;
     const dim3 grid((unsigned)((total + 255) / 256));
     if ((total + 255) / 256 > 0x7fffffffLL) return MSA_ERR_SHAPE;
+    const Span spans[] = {{positions, nbytes(n, 4)}, {cos_out, nbytes(total, 4)}, {sin_out, nbytes(total, 4)}};
+    const msa_status st = check_operands(spans, 3, static_cast<hipStream_t>(stream));
+    if (st != MSA_OK) return st;
     void* args[] = {const_cast<int32_t**>(&positions), &n, &cos_out, &sin_out, &f};
     const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&rope_table_kernel), grid, dim3(256), args, 0,
                                          static_cast<hipStream_t>(stream));
@@ -542,6 +565,9 @@ msa_status msa_quantize(const float* values, int64_t n, int32_t dtype, const flo
     if (!aligned(values, 4) || !aligned(scale, 4) || (dtype == MSA_CACHE_BF16 && !aligned(codes_out, 2)))
         return MSA_ERR_ALIGNMENT;
     int32_t is_bf16 = dtype == MSA_CACHE_BF16;
+    const Span spans[] = {{values, nbytes(n, 4)}, {is_bf16 ? nullptr : scale, 4}, {codes_out, nbytes(n, is_bf16 ? 2 : 1)}};
+    const msa_status st = check_operands(spans, 3, static_cast<hipStream_t>(stream));
+    if (st != MSA_OK) return st;
     const int64_t threads = (n + 3) / 4;
     const dim3 grid((unsigned)((threads + 255) / 256));
     void* args[] = {const_cast<float**>(&values), &n, &is_bf16, const_cast<float**>(&scale), &codes_out};
@@ -558,12 +584,33 @@ msa_status msa_rms_scale(const double* sum_sq, int64_t n, int32_t head_dim, floa
     if (n == 0) return MSA_OK;
     if (!sum_sq || !r_out) return MSA_ERR_NULL_POINTER;
     if (!aligned(sum_sq, 8) || !aligned(r_out, 4)) return MSA_ERR_ALIGNMENT;
+    const Span spans[] = {{sum_sq, nbytes(n, 8)}, {r_out, nbytes(n, 4)}};
+    const msa_status st = check_operands(spans, 2, static_cast<hipStream_t>(stream));
+    if (st != MSA_OK) return st;
     const dim3 grid((unsigned)((n + 255) / 256));
     void* args[] = {const_cast<double**>(&sum_sq), &n, &rms_eps, &r_out};
     const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&rms_scale_kernel), grid, dim3(256), args, 0,
                                          static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MSA_OK : MSA_ERR_LAUNCH;
 }
+
+msa_status msa_check_device_pointers(const void* const* ptrs, const uint64_t* bytes, int32_t n, int32_t* first_bad)
+{
+    if (first_bad) *first_bad = -1;
+    if (n < 0) return MSA_ERR_SHAPE;
+    if (n == 0) return MSA_OK;
+    if (!ptrs) return MSA_ERR_NULL_POINTER;
+    int32_t bad = -1;
+    msa_status st = MSA_OK;
+    for (int32_t i = 0; i < n && st == MSA_OK; ++i) {
+        const Span sp{ptrs[i], bytes ? bytes[i] : 1};
+        if ((st = spans_resident(&sp, 1, nullptr)) != MSA_OK) bad = i;
+    }
+    if (first_bad) *first_bad = bad;
+    return st;
+}
+
+const char* msa_status_str(msa_status s) { return msa_status_string(s); }
 
 const char* msa_status_string(msa_status s)
 {
@@ -578,6 +625,7 @@ const char* msa_status_string(msa_status s)
         case MSA_ERR_OVERFLOW: return "element offset overflows int64";
         case MSA_ERR_LAUNCH: return "kernel launch failed";
         case MSA_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
+        case MSA_ERR_NOT_DEVICE: return "an operand is not accessible from the current device or runs past its allocation";
     }
     return "unknown status";
 }

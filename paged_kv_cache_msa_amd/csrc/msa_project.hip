@@ -674,6 +674,12 @@ SplitPlan split_plan(int32_t T, int32_t K, int32_t heads)
     return p;
 }
 
+// Workspace bytes a projection of T tokens uses (the split-K partial sums; none for the tiled path).
+uint64_t workspace_need(int32_t T, int32_t K, int32_t heads)
+{
+    return T <= 0 || T > kSplitMaxTokens ? 0 : split_plan(T, K, heads).bytes;
+}
+
 msa_status check_gemm(const uint16_t* h, int64_t h_row_stride, int32_t T, int32_t K, const uint16_t* w,
                       int64_t w_row_stride, int64_t N)
 {
@@ -766,6 +772,15 @@ msa_status msa_project(const uint16_t* h, int64_t h_row_stride, int32_t num_toke
     e.x_out = x_out;
     e.x_stride = x_row_stride;
     e.T = num_tokens;
+    const uint64_t need = workspace_need(num_tokens, hidden, num_cols / kHeadDim);
+    if (need > 0 && (!workspace || !aligned(workspace, kAlign) || workspace_bytes < need)) return MSA_ERR_WORKSPACE;
+    const Span spans[] = {
+        {h, row_bytes(num_tokens, h_row_stride, hidden, 2)},
+        {w, row_bytes(num_cols, w_row_stride, hidden, 2)},
+        {x_out, row_bytes(num_tokens, x_row_stride, num_cols, 2)},
+        {workspace, need},
+    };
+    if ((st = check_operands(spans, 4, static_cast<hipStream_t>(stream))) != MSA_OK) return st;
     return launch_projection<false>(h, h_row_stride, num_tokens, hidden, w, w_row_stride, num_cols / kHeadDim, e,
                                     workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
@@ -803,9 +818,13 @@ msa_status msa_project_produce(const uint16_t* h, int64_t h_row_stride, int32_t 
         return MSA_ERR_ALIGNMENT;
     Epi e;
     std::memset(&e, 0, sizeof(e));
-    if ((st = check_cache(k_cache, num_kv_heads, page_size, num_pages, &e.cache[0])) != MSA_OK) return st;
-    if ((st = check_cache(v_cache, num_kv_heads, page_size, num_pages, &e.cache[1])) != MSA_OK) return st;
-    if ((st = check_cache(ik_cache, num_ik_heads, page_size, num_pages, &e.cache[2])) != MSA_OK) return st;
+    uint64_t cache_span[3];
+    if ((st = check_cache(k_cache, num_kv_heads, page_size, num_pages, &e.cache[0], true, &cache_span[0])) != MSA_OK)
+        return st;
+    if ((st = check_cache(v_cache, num_kv_heads, page_size, num_pages, &e.cache[1], true, &cache_span[1])) != MSA_OK)
+        return st;
+    if ((st = check_cache(ik_cache, num_ik_heads, page_size, num_pages, &e.cache[2], true, &cache_span[2])) != MSA_OK)
+        return st;
     int64_t tmp;
     if (__builtin_mul_overflow(num_pages, (int64_t)page_size, &tmp)) return MSA_ERR_OVERFLOW;
     if (num_tokens == 0) return MSA_OK;
@@ -826,6 +845,24 @@ msa_status msa_project_produce(const uint16_t* h, int64_t h_row_stride, int32_t 
     e.hik = num_ik_heads;
     e.T = num_tokens;
     e.eps = rms_eps;
+    const uint64_t need = workspace_need(num_tokens, hidden, (int32_t)heads);
+    if (need > 0 && (!workspace || !aligned(workspace, kAlign) || workspace_bytes < need)) return MSA_ERR_WORKSPACE;
+    const Span spans[] = {
+        {h, row_bytes(num_tokens, h_row_stride, hidden, 2)},
+        {w, row_bytes(heads * kHeadDim, w_row_stride, hidden, 2)},
+        {rope_cos, nbytes((int64_t)num_tokens * (kHeadDim / 2), 4)},
+        {rope_sin, nbytes((int64_t)num_tokens * (kHeadDim / 2), 4)},
+        {slots, nbytes(num_tokens, 8)},
+        {q_norm_weight, 2 * kHeadDim}, {k_norm_weight, 2 * kHeadDim},
+        {iq_norm_weight, 2 * kHeadDim}, {ik_norm_weight, 2 * kHeadDim},
+        {q_out, nbytes((int64_t)num_tokens * num_q_heads * kHeadDim, 2)},
+        {iq_out, nbytes((int64_t)num_tokens * num_iq_heads * kHeadDim, 2)},
+        {e.cache[0].data, cache_span[0]}, {e.cache[1].data, cache_span[1]}, {e.cache[2].data, cache_span[2]},
+        {e.cache[0].scale, 4}, {e.cache[1].scale, 4}, {e.cache[2].scale, 4},
+        {workspace, need},
+    };
+    if ((st = check_operands(spans, sizeof(spans) / sizeof(spans[0]), static_cast<hipStream_t>(stream))) != MSA_OK)
+        return st;
     return launch_projection<true>(h, h_row_stride, num_tokens, hidden, w, w_row_stride, (int32_t)heads, e, workspace,
                                    workspace_bytes, static_cast<hipStream_t>(stream));
 }

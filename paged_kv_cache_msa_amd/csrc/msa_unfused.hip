@@ -310,6 +310,11 @@ msa_status msa_slots(const int32_t* positions, const int32_t* seq_idx, int32_t n
     a.S = num_seqs;
     a.max_pages = max_pages_per_seq;
     a.page_size = page_size;
+    const Span spans[] = {{positions, nbytes(num_tokens, 4)}, {seq_idx, nbytes(num_tokens, 4)},
+                          {page_table, num_seqs > 0 ? row_bytes(num_seqs, page_table_stride, max_pages_per_seq, 4) : 0},
+                          {slots_out, nbytes(num_tokens, 8)}};
+    const msa_status st = check_operands(spans, 4, static_cast<hipStream_t>(stream));
+    if (st != MSA_OK) return st;
     void* args[] = {&a};
     const hipError_t e = launch(reinterpret_cast<const void*>(&slots_kernel), num_tokens, args,
                                 static_cast<hipStream_t>(stream));
@@ -360,10 +365,14 @@ msa_status msa_produce_unfused(const uint16_t* x, int64_t x_row_stride, int32_t 
     int64_t tmp;
     if (__builtin_mul_overflow((int64_t)num_tokens, x_row_stride, &tmp)) return MSA_ERR_OVERFLOW;
     CacheDev cache[3];
+    uint64_t cache_span[3];
     msa_status st;
-    if ((st = check_cache(k_cache, num_kv_heads, page_size, num_pages, &cache[0], false)) != MSA_OK) return st;
-    if ((st = check_cache(v_cache, num_kv_heads, page_size, num_pages, &cache[1], false)) != MSA_OK) return st;
-    if ((st = check_cache(ik_cache, num_ik_heads, page_size, num_pages, &cache[2], false)) != MSA_OK) return st;
+    for (int c = 0; c < 3; ++c) {
+        const msa_cache_view* v = c == 0 ? k_cache : c == 1 ? v_cache : ik_cache;
+        if ((st = check_cache(v, c == 2 ? num_ik_heads : num_kv_heads, page_size, num_pages, &cache[c], false,
+                              &cache_span[c])) != MSA_OK)
+            return st;
+    }
     if (__builtin_mul_overflow(num_pages, (int64_t)page_size, &tmp)) return MSA_ERR_OVERFLOW;
     const Workspace ws = layout(num_tokens, num_kv_heads, num_ik_heads);
     if (num_tokens == 0) return MSA_OK;
@@ -371,6 +380,21 @@ msa_status msa_produce_unfused(const uint16_t* x, int64_t x_row_stride, int32_t 
     if ((int64_t)num_tokens * heads_total > ((int64_t)1 << 31)) return MSA_ERR_SHAPE;   // grid sizes
 
     hipStream_t s = static_cast<hipStream_t>(stream);
+    {
+        const Span spans[] = {
+            {x, row_bytes(num_tokens, x_row_stride, heads_total * kHeadDim, 2)},
+            {positions, nbytes(num_tokens, 4)},
+            {slots, nbytes(num_tokens, 8)},
+            {q_norm_weight, 2 * kHeadDim}, {k_norm_weight, 2 * kHeadDim},
+            {iq_norm_weight, 2 * kHeadDim}, {ik_norm_weight, 2 * kHeadDim},
+            {q_out, nbytes((int64_t)num_tokens * num_q_heads * kHeadDim, 2)},
+            {iq_out, nbytes((int64_t)num_tokens * num_iq_heads * kHeadDim, 2)},
+            {cache[0].data, cache_span[0]}, {cache[1].data, cache_span[1]}, {cache[2].data, cache_span[2]},
+            {cache[0].scale, 4}, {cache[1].scale, 4}, {cache[2].scale, 4},
+            {workspace, ws.total},
+        };
+        if ((st = check_operands(spans, sizeof(spans) / sizeof(spans[0]), s)) != MSA_OK) return st;
+    }
     uint8_t* w = static_cast<uint8_t*>(workspace);
     float* k_f32 = reinterpret_cast<float*>(w + ws.k_f32);
     float* ik_f32 = reinterpret_cast<float*>(w + ws.ik_f32);

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADERS = [os.path.join(ROOT, "include", n) for n in sorted(os.listdir(os.path.join(ROOT, "include")))
            if n.endswith(".h")]
 
-OK, NULLP, UNSUP, SHAPE, STRIDE, ALIGN, DTYPE, OVERFLOW, LAUNCH, WORKSPACE = range(10)
+OK, NULLP, UNSUP, SHAPE, STRIDE, ALIGN, DTYPE, OVERFLOW, LAUNCH, WORKSPACE, NOT_DEVICE = range(11)
 
 
 @pytest.fixture(scope="module")
@@ -35,16 +35,34 @@ def declared_functions():
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert set(names) >= {"msa_produce", "msa_rope_table", "msa_quantize", "msa_rms_scale", "msa_status_string",
-                          "msa_index_scores", "msa_index_topk", "msa_slots", "msa_produce_unfused",
-                          "msa_produce_unfused_workspace_size"}
+                          "msa_status_str", "msa_check_device_pointers", "msa_index_scores", "msa_index_topk",
+                          "msa_slots", "msa_produce_unfused", "msa_produce_unfused_workspace_size"}
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_status_strings(L):
-    for code in range(10):
+    for code in range(11):
         assert msa.string(code) and msa.string(code) != "unknown status"
+        assert L.msa_status_str(code) == L.msa_status_string(code)
     assert msa.string(99) == "unknown status"
+
+
+def test_device_pointer_check_without_a_device(L):
+    """With no GPU every non-NULL pointer fails the residency check (reported with its index); NULL
+    entries and an empty list pass; a negative count or a NULL array is an argument error."""
+    assert msa.msa_check_device_pointers([]) == (OK, -1)
+    assert msa.msa_check_device_pointers([None, None]) == (OK, -1)
+    assert msa.msa_check_device_pointers([None, X, Q]) == (NOT_DEVICE, 1)
+    assert msa.msa_check_device_pointers([X], [0]) == (OK, -1)          # an empty extent touches nothing
+    assert L.msa_check_device_pointers(None, None, -1, None) == SHAPE
+    assert L.msa_check_device_pointers(None, None, 2, None) == NULLP
+
+
+def test_valid_call_without_a_device_launches_nothing(L):
+    """Arguments that pass every host check, T > 0, no GPU: the operand check (the capture query, or
+    the residency of the first operand) fails and the call returns before any launch."""
+    assert call(L, T=64) in (LAUNCH, NOT_DEVICE)
 
 
 # Fake, aligned device addresses: validation returns before anything could dereference them.

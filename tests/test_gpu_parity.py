@@ -17,10 +17,9 @@ import torch
 import paged_kv_cache_msa_amd as msa
 from paged_kv_cache_msa_amd import workloads as W
 from tests import helpers as H
+from tests.parity import THREADS, check, say
 
 pytestmark = pytest.mark.gpu
-
-THREADS = min(16, os.cpu_count() or 1)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -28,10 +27,6 @@ def _gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     msa.lib()
-
-
-def say(*a):
-    print(*a, flush=True, file=sys.stderr)
 
 
 def run(wl):
@@ -43,75 +38,6 @@ def run(wl):
                     slots_out=d.slots)
     torch.cuda.synchronize()
     return d
-
-
-def check_q(name, gpu_bits, ref_bits):
-    g = H.bf16_bits_to_f32(gpu_bits).astype(np.float64)
-    r = H.bf16_bits_to_f32(ref_bits).astype(np.float64)
-    nan_g, nan_r = np.isnan(g), np.isnan(r)
-    assert np.array_equal(nan_g, nan_r), f"{name}: NaN positions differ"
-    fin = ~nan_r
-    with np.errstate(invalid="ignore"):
-        ok = (g[fin] == r[fin]) | (np.abs(g[fin] - r[fin]) <= 2.0 ** -7 * np.abs(r[fin]))
-    bad = np.flatnonzero(~ok)
-    assert bad.size == 0, f"{name}: {bad.size} elements beyond 1 bf16 ulp, first {g[fin][bad[:4]]} vs {r[fin][bad[:4]]}"
-    n_inexact = int(np.count_nonzero(gpu_bits != ref_bits))
-    say(f"  {name}: within 1 bf16 ulp; bit-identical elements {gpu_bits.size - n_inexact}/{gpu_bits.size}")
-
-
-def is_nan_code(c, dtype):
-    c = np.asarray(c)
-    if dtype == W.FP8_E4M3:
-        return (c & 0x7F) == 0x7F
-    return (c & 0x7FFF) > 0x7F80
-
-
-def code_diff(gpu, ref, dtype):
-    """Indices where two cache-code arrays disagree.  Codes must be identical except where the
-    oracle's code is a NaN: which NaN (sign, payload) an IEEE-754 operation returns is not fixed
-    by the standard (x86 and the GPU differ), so there the GPU code only has to be a NaN too."""
-    nan_r = is_nan_code(ref, dtype)
-    ok = np.where(nan_r, is_nan_code(gpu, dtype), gpu == ref)
-    return np.flatnonzero(~ok)
-
-
-def check(wl, d, full=None):
-    """Compare a device result with the oracle.  full=True compares whole cache storages against the
-    oracle's cache form; otherwise rows are gathered at the oracle's slots and the untouched count
-    is checked on the device."""
-    if full is None:
-        full = all(c.storage_elems <= (1 << 26) for c in wl.caches)
-    ref = H.oracle_rows(wl, num_threads=THREADS)
-    slots = d.slots.cpu().numpy()
-    np.testing.assert_array_equal(slots, ref["slots"])
-    check_q("q", d.q_out.cpu().numpy().view(np.uint16), ref["q"])
-    check_q("iq", d.iq_out.cpu().numpy().view(np.uint16), ref["iq"])
-    valid = np.flatnonzero(ref["slots"] >= 0)
-    if full:
-        _, st = H.oracle_caches(wl)
-        for name, spec, s_ref, s_gpu in zip(("k", "v", "ik"), wl.caches, st, d.storages):
-            if spec.heads == 0:
-                continue
-            g = s_gpu.cpu().numpy()
-            g = g.view(np.uint8) if spec.dtype == W.FP8_E4M3 else g.view(np.uint16)
-            diff = code_diff(g, s_ref.reshape(-1), spec.dtype)
-            assert diff.size == 0, f"{name} cache: {diff.size} elements differ, first at {diff[:4]}"
-        say(f"  caches: whole storages byte-identical ({len(valid)} tokens written)")
-        return
-    pg = torch.from_numpy(ref["slots"][valid] // wl.page_size).cuda()
-    off = torch.from_numpy(ref["slots"][valid] % wl.page_size).cuda()
-    for name, spec, view, store in zip(("k", "v", "ik"), wl.caches, d.caches, d.storages):
-        if spec.heads == 0:
-            continue
-        rows = view[pg, :, off, :].cpu().numpy()          # [n_valid, H, D]
-        rows = rows.view(np.uint8) if spec.dtype == W.FP8_E4M3 else rows.view(np.uint16)
-        exp = ref[name][valid]
-        diff = code_diff(rows.reshape(-1), exp.reshape(-1), spec.dtype)
-        assert diff.size == 0, f"{name} cache rows: {len(diff)} elements differ, first {diff[:4]}"
-        sent = W.SENTINEL_BYTE if spec.dtype == W.FP8_E4M3 else W.SENTINEL_BYTE * 0x0101
-        changed = int((store != sent).sum().item())
-        assert changed == len(valid) * spec.heads * wl.head_dim, f"{name}: {changed} elements changed"
-    say(f"  caches: gathered rows byte-identical, untouched count exact ({len(valid)} tokens written)")
 
 
 @pytest.mark.parametrize("make", [W.tiny_decode, W.tiny_decode_no_index_k], ids=["tiny-w1024", "tiny-w896-no-index-k"])
@@ -214,33 +140,52 @@ def test_special_values():
 
 # ------------------------------------------------------------------ step-level entry points
 
-def test_rope_table_exhaustive_workload_positions():
-    """Every position in [0, 131072) at theta = 1e4 (every workload's positions) against the oracle,
-    bit for bit."""
+def _oracle_rope(pos, theta, threads=THREADS):
+    """The oracle's table, in parallel chunks (the C oracle releases the interpreter lock)."""
     import oracle
-    pos = np.arange(131072, dtype=np.int32)
+    from concurrent.futures import ThreadPoolExecutor
+    parts = np.array_split(pos, threads)
+    with ThreadPoolExecutor(threads) as ex:
+        out = list(ex.map(lambda p: oracle.rope_table(p, theta, 128), parts))
+    return np.concatenate([c for c, _ in out]), np.concatenate([s for _, s in out])
+
+
+def _gpu_rope(pos, theta):
     dp = torch.from_numpy(pos).cuda()
     c = torch.empty((pos.size, 64), dtype=torch.float32, device="cuda")
     s = torch.empty_like(c)
-    msa.msa_rope_table(dp, c, s, 1e4)
+    msa.msa_rope_table(dp, c, s, theta)
     torch.cuda.synchronize()
-    rc, rs = oracle.rope_table(pos, 1e4, 128)
-    assert np.array_equal(c.cpu().numpy().view(np.uint32), rc.view(np.uint32))
-    assert np.array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    return c.cpu().numpy(), s.cpu().numpy()
+
+
+@pytest.mark.parametrize("theta,n", [(1e4, 1 << 20), (5e5, 1 << 17), (1e6, 1 << 17)])
+def test_rope_table_exhaustive(theta, n):
+    """Every position in [0, n) against the oracle, bit for bit: at theta = 1e4 over 2^20 positions
+    (a million-token context), and at the other two bases over [0, 131072), which holds every
+    position the workloads use.  This pins the single binary32 rounding of the binary64 cos / sin
+    of the two implementations over those domains."""
+    pos = np.arange(n, dtype=np.int32)
+    say(f"[gpu] msa_rope_table theta={theta}: positions [0, {n})")
+    gc, gs = _gpu_rope(pos, theta)
+    rc, rs = _oracle_rope(pos, theta)
+    bad_c = np.flatnonzero(gc.view(np.uint32) != rc.view(np.uint32))
+    bad_s = np.flatnonzero(gs.view(np.uint32) != rs.view(np.uint32))
+    assert bad_c.size == 0 and bad_s.size == 0, (
+        f"cos differs at {bad_c.size} (first (pos, i) {np.unravel_index(bad_c[:3], gc.shape)}), "
+        f"sin at {bad_s.size} (first {np.unravel_index(bad_s[:3], gs.shape)})")
 
 
 def test_rope_table_other_theta_sampled():
+    """Random positions over the whole int32 range (negative ones included) at three bases: within
+    one binary32 ulp of the oracle (the binary64 sincos of the two implementations may differ in
+    its last bit for huge angles)."""
     import oracle
     rng = np.random.default_rng(3)
     for theta in (1e6, 5e5, 1e4):
         pos = np.concatenate([rng.integers(-2 ** 31, 2 ** 31 - 1, 20000), [0, 1, -1, 2 ** 31 - 1, -2 ** 31]]).astype(np.int32)
-        dp = torch.from_numpy(pos).cuda()
-        c = torch.empty((pos.size, 64), dtype=torch.float32, device="cuda")
-        s = torch.empty_like(c)
-        msa.msa_rope_table(dp, c, s, theta)
-        torch.cuda.synchronize()
+        gc, gs = _gpu_rope(pos, theta)
         rc, rs = oracle.rope_table(pos, theta, 128)
-        gc, gs = c.cpu().numpy(), s.cpu().numpy()
         n_diff = int(np.count_nonzero(gc.view(np.uint32) != rc.view(np.uint32)) +
                      np.count_nonzero(gs.view(np.uint32) != rs.view(np.uint32)))
         assert np.all(np.abs(gc.astype(np.float64) - rc) <= H.ulp32(rc)), theta
@@ -357,6 +302,130 @@ def test_graph_replay_matches_eager():
             for a, b in zip(sts, d.storages):
                 assert torch.equal(a, b), rep
     check(layers[0], devs[0])
+
+
+def _reset(devs):
+    for d in devs:
+        d.q_out.fill_(3)
+        d.iq_out.fill_(3)
+        d.slots.fill_(-7)
+        for st in d.storages:
+            st.fill_(W.SENTINEL_BYTE if st.dtype == torch.uint8 else W.SENTINEL_BYTE * 0x0101)
+
+
+def test_decode_graph_steps_with_metadata_updated_in_place():
+    """The serving loop's decode step: three layer calls captured once, then four steps, each after
+    the host wrote that step's metadata into the same device buffers (every position advanced by one,
+    eight tokens crossing into a new page; a logical page remapped to another physical page; four
+    tokens padded; one page-table entry outside the pool).  Before every replay the caches are refilled
+    with the sentinel and the outputs clobbered, so each replay must write everything itself: every
+    layer of every step equals the oracle on that step's metadata, and every other cache element
+    still holds the sentinel."""
+    import dataclasses
+    layers = [W.decode_batch64(layer=i) for i in range(3)]
+    P = layers[0].page_size
+    pos = layers[0].positions.copy()
+    pos[:8] = (pos[:8] // P) * P + P - 1            # the next step starts a new page for these
+    seq = layers[0].seq_idx.copy()
+    pt = np.ascontiguousarray(layers[0].page_table.copy())
+    layers = [dataclasses.replace(wl, positions=pos.copy()) for wl in layers]
+    devs = [W.to_device(wl) for wl in layers]
+    d0 = devs[0]
+    for d in devs[1:]:
+        d.positions, d.seq_idx, d.page_table = d0.positions, d0.seq_idx, d0.page_table
+
+    def call(wl, d):
+        msa.msa_produce(d.x, d.positions, d.seq_idx, d.page_table, *d.weights, d.q_out, d.iq_out,
+                        d.caches[0], d.caches[1], d.caches[2], k_scale=d.scales[0], v_scale=d.scales[1],
+                        ik_scale=d.scales[2], num_pages=wl.num_pages, slots_out=d.slots)
+
+    for wl, d in zip(layers, devs):
+        call(wl, d)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for wl, d in zip(layers, devs):
+                call(wl, d)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+
+    for step in range(4):
+        if step >= 1:
+            pos += 1
+        if step == 2:
+            for t in range(4):                     # remap the page these tokens just entered
+                lp = pos[t] // P
+                pt[t, lp], pt[t + 32, 0] = pt[t + 32, 0], pt[t, lp]
+            seq[10:14] = -1
+        if step == 3:
+            seq[10:14] = np.arange(10, 14)
+            pt[20, pos[20] // P] = layers[0].num_pages + 5
+        d0.positions.copy_(torch.from_numpy(pos))
+        d0.seq_idx.copy_(torch.from_numpy(seq))
+        d0.page_table.copy_(torch.from_numpy(pt))
+        _reset(devs)
+        torch.cuda.synchronize()
+        say(f"[gpu] decode graph step {step}: replay of 3 layer calls")
+        g.replay()
+        torch.cuda.synchronize()
+        n_valid = int(np.count_nonzero(d0.slots.cpu().numpy() >= 0))
+        if step == 2:
+            assert n_valid == 60
+        if step == 3:
+            assert n_valid == 63
+        for wl, d in zip(layers, devs):
+            check(dataclasses.replace(wl, positions=pos.copy(), seq_idx=seq.copy(), page_table=pt.copy()), d)
+
+
+# ------------------------------------------------------------------ operand residency (eager calls)
+
+def test_check_device_pointers():
+    """The residency check alone (nothing is launched): device memory of this device passes with an
+    extent inside its allocation; pageable host memory, or an extent past the allocation, fails with
+    the index of the pointer; pinned host memory passes."""
+    dev = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    host = torch.empty(1 << 20, dtype=torch.uint8)
+    pinned = torch.empty(1 << 20, dtype=torch.uint8, pin_memory=True)
+    assert msa.msa_check_device_pointers([dev.data_ptr()], [1 << 20]) == (0, -1)
+    assert msa.msa_check_device_pointers([dev.data_ptr() + 4096, None], [4096, 0]) == (0, -1)
+    assert msa.msa_check_device_pointers([dev.data_ptr(), host.data_ptr()], [64, 64]) == (10, 1)
+    assert msa.msa_check_device_pointers([dev.data_ptr()], [1 << 50]) == (10, 0)
+    assert msa.msa_check_device_pointers([pinned.data_ptr()], [1 << 20]) == (0, -1)
+    # host cost of the check, for the record
+    import time
+    ptrs = [dev.data_ptr()] * 16
+    t0 = time.perf_counter()
+    for _ in range(200):
+        msa.msa_check_device_pointers(ptrs, [64] * 16)
+    say(f"  residency check of 16 pointers: {(time.perf_counter() - t0) / 200 * 1e6:.1f} us on the host")
+
+
+def test_eager_call_with_cache_past_its_allocation_is_refused():
+    """A call whose cache view, by the page count it is given, reaches past the end of the cache's
+    allocation returns MSA_ERR_NOT_DEVICE and launches nothing (caches keep the sentinel, Q keeps its
+    contents).  Every page-table entry stays inside the real allocation, so even a launch would only
+    touch memory the call owns."""
+    import ctypes
+    torch.cuda.empty_cache()
+    wl = W.decode_batch64()
+    d = W.to_device(wl)
+    L = msa.lib()
+    views = [msa.cache_view(c, sc) for c, sc in zip(d.caches, d.scales)]
+    st = L.msa_produce(d.x.data_ptr(), d.x.stride(0), wl.T, 128, wl.hq, wl.hkv, wl.hiq, wl.hik,
+                       d.positions.data_ptr(), d.seq_idx.data_ptr(), d.page_table.data_ptr(), d.page_table.stride(0),
+                       wl.num_seqs, wl.max_pages, wl.page_size, 1000 * wl.num_pages,
+                       *[w.data_ptr() for w in d.weights], 1e-6, 1e4, d.q_out.data_ptr(), d.iq_out.data_ptr(),
+                       *[ctypes.byref(v) for v in views], d.slots.data_ptr(),
+                       torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == 10, msa.string(st)
+    assert int((d.q_out != 0).sum()) == 0
+    assert int((d.slots != -7).sum()) == 0
+    for store in d.storages:
+        assert int((store != W.SENTINEL_BYTE).sum()) == 0
 
 
 # ------------------------------------------------------------------ speculative-decoding verify rows

@@ -25,7 +25,7 @@ import oracle
 import paged_kv_cache_msa_amd as msa
 from paged_kv_cache_msa_amd import workloads as W
 from tests import helpers as H
-from tests.test_gpu_parity import check
+from tests.parity import check
 
 pytestmark = pytest.mark.gpu
 THREADS = min(16, os.cpu_count() or 1)

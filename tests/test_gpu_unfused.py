@@ -12,7 +12,7 @@ import torch
 import paged_kv_cache_msa_amd as msa
 from paged_kv_cache_msa_amd import workloads as W
 from tests import helpers as H
-from tests.test_gpu_parity import check, code_diff
+from tests.parity import check, storage_mismatches, written_mask
 
 pytestmark = pytest.mark.gpu
 
@@ -64,6 +64,13 @@ def test_decode_batch_256_padded_strided():
     d = run(wl)
     assert int((d.slots < 0).sum()) == 31
     check(wl, d)
+
+
+def test_prefill_65536():
+    """The full 65,536-token prefill chunk, the size the benchmark times this path at."""
+    wl = W.prefill_65536()
+    check(wl, run(wl))
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("dtype", [W.BF16, W.FP8_E4M3], ids=["bf16", "fp8"])
@@ -148,9 +155,10 @@ def test_layouts_the_fused_kernel_rejects(base_off):
         g = s_gpu.cpu().numpy()
         g = g.view(np.uint8) if spec.dtype == W.FP8_E4M3 else g.view(np.uint16)
         assert np.all(g[:off] == s_ref.reshape(-1)[0]), f"{name}: prefix written"
-        diff = code_diff(g[off:], s_ref.reshape(-1), spec.dtype)
+        mask = written_mask(spec, ref["slots"], wl.page_size)
+        diff = storage_mismatches(g[off:], s_ref.reshape(-1), mask, spec.dtype)
         assert diff.size == 0, f"{name} cache: {diff.size} elements differ, first at {diff[:4]}"
-    say(f"  odd layouts {base_off}: whole storages byte-identical")
+    say(f"  odd layouts {base_off}: whole storages identical, every unwritten element holds the sentinel")
 
 
 def test_graph_replay_matches_eager_and_fused():
