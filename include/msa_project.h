@@ -97,6 +97,38 @@ msa_status msa_project_produce(const uint16_t* h, int64_t h_row_stride, int32_t 
                                const msa_cache_view* ik_cache,
                                void* workspace, uint64_t workspace_bytes, void* stream);
 
+/*
+ * msa_project_produce_noalloc — msa_project_produce without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  It allocates nothing (no hipMalloc, no hipFree, no allocating library routine).
+ *
+ * The split-K partial sums go to a scratch array the library owns: 32 MiB (33,554,432 bytes) of
+ * device memory per GPU, part of the library's code object, held by every GPU the library runs on
+ * until the process ends.  A call whose workspace need (msa_project_workspace_size) exceeds it
+ * returns MSA_ERR_WORKSPACE before touching the device: 23 heads of hidden 3,072 fit up to 256
+ * tokens; batches above 1,024 tokens need no scratch and always fit.  The first call on a device
+ * looks up that device's copy of the array (a runtime query that allocates nothing); if the runtime
+ * refuses such queries during graph capture, make one eager call first.
+ *
+ * Every call on one GPU shares that GPU's array, and the array keeps the last call's partial sums
+ * (each call overwrites everything it reads, so nothing needs clearing).  Calls that overlap in time
+ * on one GPU (different streams without ordering between them, or several host threads) race on it
+ * and give wrong results; calls on one stream, or otherwise ordered, are safe.
+ *
+ * Arguments, results and the other errors: as msa_project_produce, minus workspace and
+ * workspace_bytes.
+ */
+msa_status msa_project_produce_noalloc(const uint16_t* h, int64_t h_row_stride, int32_t num_tokens, int32_t hidden,
+                                       const uint16_t* w, int64_t w_row_stride, int32_t head_dim,
+                                       int32_t num_q_heads, int32_t num_kv_heads, int32_t num_iq_heads,
+                                       int32_t num_ik_heads, const float* rope_cos, const float* rope_sin,
+                                       const int64_t* slots, int32_t page_size, int64_t num_pages,
+                                       const uint16_t* q_norm_weight, const uint16_t* k_norm_weight,
+                                       const uint16_t* iq_norm_weight, const uint16_t* ik_norm_weight,
+                                       float rms_eps, uint16_t* q_out, uint16_t* iq_out,
+                                       const msa_cache_view* k_cache, const msa_cache_view* v_cache,
+                                       const msa_cache_view* ik_cache, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

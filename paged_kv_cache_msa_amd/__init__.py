@@ -23,6 +23,8 @@ Entry points (same names as the C ABI):
                         main and index norm/RoPE producers, then division, remainder, index cast
                         and scatter per cache (14 launches per layer); takes any positive,
                         non-overlapping cache strides.
+  msa_project_produce_noalloc(...)  msa_project_produce with the library's static per-GPU scratch in place
+                        of a workspace (allocates nothing; calls on one GPU must not overlap).
   msa_check_device_pointers(...)  the residency check eager calls run on their operands, alone.
 
 Every wrapper checks its tensors' dtypes, shapes, extents and devices against the counts it hands to
@@ -107,6 +109,9 @@ def lib() -> ctypes.CDLL:
         L.msa_project_produce.argtypes = [p, i64, i32, i32, p, i64, i32, i32, i32, i32, i32, p, p, p, i32, i64,
                                           p, p, p, p, f32, p, p, cv, cv, cv, p, u64, p]
         L.msa_project_produce.restype = ctypes.c_int
+        L.msa_project_produce_noalloc.argtypes = [p, i64, i32, i32, p, i64, i32, i32, i32, i32, i32, p, p, p, i32,
+                                                  i64, p, p, p, p, f32, p, p, cv, cv, cv, p]
+        L.msa_project_produce_noalloc.restype = ctypes.c_int
         L.msa_status_string.argtypes = [ctypes.c_int]
         L.msa_status_string.restype = ctypes.c_char_p
         L.msa_status_str.argtypes = [ctypes.c_int]
@@ -521,6 +526,40 @@ def msa_project_produce(h, w, rope_cos, rope_sin, slots, q_norm_weight, k_norm_w
         _ptr(q_out), _ptr(iq_out), _ref(kv), _ref(vv), _ref(iv), wp, wb, _stream(stream))
     if st != 0:
         raise MsaError(st, "msa_project_produce")
+
+
+def msa_project_produce_noalloc(h, w, rope_cos, rope_sin, slots, q_norm_weight, k_norm_weight, iq_norm_weight,
+                                ik_norm_weight, q_out, iq_out, k_cache, v_cache, ik_cache=None, *, k_scale=None,
+                                v_scale=None, ik_scale=None, num_pages: Optional[int] = None, rms_eps: float = 1e-6,
+                                stream=None) -> None:
+    """msa_project_produce with the library's own 32 MiB per-GPU scratch instead of a workspace: allocates
+    nothing.  Calls on one GPU share the scratch, so calls that overlap in time on one GPU race.  A call
+    that needs more scratch than that raises MsaError (MSA_ERR_WORKSPACE)."""
+    T, K, N = _gemm_operands(h, w)
+    hkv, hik, page_size, pages = _caches(k_cache, v_cache, ik_cache, num_pages, k_scale, v_scale, ik_scale)
+    _tensor("q_out", q_out, dim=3)
+    _tensor("iq_out", iq_out, dim=3)
+    hq, hiq = q_out.shape[1], iq_out.shape[1]
+    _rows_out("q_out", q_out, T, hq)
+    _rows_out("iq_out", iq_out, T, hiq)
+    heads = hq + 2 * hkv + hiq + hik
+    _need(N == heads * 128, f"w has {N} rows, the heads need {heads * 128}")
+    for name, t in (("rope_cos", rope_cos), ("rope_sin", rope_sin)):
+        _tensor(name, t, contiguous=True)
+        _float(name, t, 32)
+        _need(t.numel() >= T * 64, f"{name} holds {t.numel()} elements, needs {T * 64}")
+    _int("slots", slots, 64, T)
+    _weights((q_norm_weight, k_norm_weight, iq_norm_weight, ik_norm_weight), (hq, hkv, hiq, hik))
+    _same_device(h, w, rope_cos, rope_sin, slots, q_norm_weight, k_norm_weight, iq_norm_weight, ik_norm_weight,
+                 q_out, iq_out, k_cache, v_cache, ik_cache)
+    kv, vv, iv = cache_view(k_cache, k_scale), cache_view(v_cache, v_scale), cache_view(ik_cache, ik_scale)
+    st = lib().msa_project_produce_noalloc(
+        _ptr(h), h.stride(0), T, K, _ptr(w), w.stride(0), 128, hq, hkv, hiq, hik,
+        _ptr(rope_cos), _ptr(rope_sin), _ptr(slots), page_size, pages,
+        _ptr(q_norm_weight), _ptr(k_norm_weight), _ptr(iq_norm_weight), _ptr(ik_norm_weight), float(rms_eps),
+        _ptr(q_out), _ptr(iq_out), _ref(kv), _ref(vv), _ref(iv), _stream(stream))
+    if st != 0:
+        raise MsaError(st, "msa_project_produce_noalloc")
 
 
 def msa_check_device_pointers(ptrs, nbytes=None):

@@ -35,6 +35,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "msa_common.h"
 #include "msa_device.h"
@@ -742,60 +743,19 @@ msa_status launch_projection(const uint16_t* h, int64_t h_row_stride, int32_t T,
     return err == hipSuccess ? MSA_OK : MSA_ERR_LAUNCH;
 }
 
-}  // namespace
-
-extern "C" {
-
-msa_status msa_project_workspace_size(int32_t num_tokens, int32_t hidden, int32_t num_heads, uint64_t* bytes)
-{
-    if (!bytes) return MSA_ERR_NULL_POINTER;
-    if (num_tokens < 0 || hidden <= 0 || hidden % kBK || num_heads <= 0 || num_heads > 4096) return MSA_ERR_SHAPE;
-    *bytes = num_tokens == 0 || num_tokens > kSplitMaxTokens ? 0 : split_plan(num_tokens, hidden, num_heads).bytes;
-    return MSA_OK;
-}
-
-msa_status msa_project(const uint16_t* h, int64_t h_row_stride, int32_t num_tokens, int32_t hidden,
-                       const uint16_t* w, int64_t w_row_stride, int32_t num_cols,
-                       uint16_t* x_out, int64_t x_row_stride,
-                       void* workspace, uint64_t workspace_bytes, void* stream)
-{
-    msa_status st = check_gemm(h, h_row_stride, num_tokens, hidden, w, w_row_stride, num_cols);
-    if (st != MSA_OK) return st;
-    if (x_row_stride < num_cols || x_row_stride % 8) return MSA_ERR_STRIDE;
-    if (num_tokens > 0 && !x_out) return MSA_ERR_NULL_POINTER;
-    if (!aligned(x_out, 16)) return MSA_ERR_ALIGNMENT;
-    int64_t tmp;
-    if (__builtin_mul_overflow((int64_t)num_tokens, x_row_stride, &tmp)) return MSA_ERR_OVERFLOW;
-    if (num_tokens == 0) return MSA_OK;
-    Epi e;
-    std::memset(&e, 0, sizeof(e));
-    e.x_out = x_out;
-    e.x_stride = x_row_stride;
-    e.T = num_tokens;
-    const uint64_t need = workspace_need(num_tokens, hidden, num_cols / kHeadDim);
-    if (need > 0 && (!workspace || !aligned(workspace, kAlign) || workspace_bytes < need)) return MSA_ERR_WORKSPACE;
-    const Span spans[] = {
-        {h, row_bytes(num_tokens, h_row_stride, hidden, 2)},
-        {w, row_bytes(num_cols, w_row_stride, hidden, 2)},
-        {x_out, row_bytes(num_tokens, x_row_stride, num_cols, 2)},
-        {workspace, need},
-    };
-    if ((st = check_operands(spans, 4, static_cast<hipStream_t>(stream))) != MSA_OK) return st;
-    return launch_projection<false>(h, h_row_stride, num_tokens, hidden, w, w_row_stride, num_cols / kHeadDim, e,
-                                    workspace, workspace_bytes, static_cast<hipStream_t>(stream));
-}
-
-msa_status msa_project_produce(const uint16_t* h, int64_t h_row_stride, int32_t num_tokens, int32_t hidden,
-                               const uint16_t* w, int64_t w_row_stride, int32_t head_dim,
-                               int32_t num_q_heads, int32_t num_kv_heads, int32_t num_iq_heads,
-                               int32_t num_ik_heads, const float* rope_cos, const float* rope_sin,
-                               const int64_t* slots, int32_t page_size, int64_t num_pages,
-                               const uint16_t* q_norm_weight, const uint16_t* k_norm_weight,
-                               const uint16_t* iq_norm_weight, const uint16_t* ik_norm_weight,
-                               float rms_eps, uint16_t* q_out, uint16_t* iq_out,
-                               const msa_cache_view* k_cache, const msa_cache_view* v_cache,
-                               const msa_cache_view* ik_cache,
-                               void* workspace, uint64_t workspace_bytes, void* stream)
+// msa_project_produce's checks and launches.  `own_scratch`: the workspace is the library's static
+// scratch array (its residency is not queried: the runtime places the code object's arrays itself).
+msa_status project_produce(const uint16_t* h, int64_t h_row_stride, int32_t num_tokens, int32_t hidden,
+                           const uint16_t* w, int64_t w_row_stride, int32_t head_dim,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t num_iq_heads,
+                           int32_t num_ik_heads, const float* rope_cos, const float* rope_sin,
+                           const int64_t* slots, int32_t page_size, int64_t num_pages,
+                           const uint16_t* q_norm_weight, const uint16_t* k_norm_weight,
+                           const uint16_t* iq_norm_weight, const uint16_t* ik_norm_weight,
+                           float rms_eps, uint16_t* q_out, uint16_t* iq_out,
+                           const msa_cache_view* k_cache, const msa_cache_view* v_cache,
+                           const msa_cache_view* ik_cache,
+                           void* workspace, uint64_t workspace_bytes, hipStream_t stream, bool own_scratch)
 {
     if (head_dim != kHeadDim) return MSA_ERR_UNSUPPORTED;
     if (num_tokens < 0 || num_q_heads < 0 || num_kv_heads < 0 || num_iq_heads < 0 || num_ik_heads < 0)
@@ -859,12 +819,135 @@ msa_status msa_project_produce(const uint16_t* h, int64_t h_row_stride, int32_t 
         {iq_out, nbytes((int64_t)num_tokens * num_iq_heads * kHeadDim, 2)},
         {e.cache[0].data, cache_span[0]}, {e.cache[1].data, cache_span[1]}, {e.cache[2].data, cache_span[2]},
         {e.cache[0].scale, 4}, {e.cache[1].scale, 4}, {e.cache[2].scale, 4},
+        {own_scratch ? nullptr : workspace, need},
+    };
+    if ((st = check_operands(spans, sizeof(spans) / sizeof(spans[0]), stream)) != MSA_OK) return st;
+    return launch_projection<true>(h, h_row_stride, num_tokens, hidden, w, w_row_stride, (int32_t)heads, e, workspace,
+                                   workspace_bytes, stream);
+}
+
+
+// ------------------------------------------------------------------ the library's own scratch
+
+// Split-K partial sums of msa_project_produce_noalloc: one array per device, resident from the
+// code object's load until the process ends.  32 MiB holds the partial sums of 23 heads x 3,072
+// hidden columns for up to 256 tokens (64 tokens: 5.9 MB).  Host code never names `scratch` where
+// it needs the memory: the name is a host-side stand-in, and each device's address comes from the
+// runtime (scratch_address).
+constexpr uint64_t kScratchBytes = 32ull << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_dev_ptr[kMaxDevices];
+
+// The current device's copy of `scratch`, looked up once per device (with that device current) and
+// kept.
+msa_status scratch_address(void** out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return MSA_ERR_LAUNCH;
+    }
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_dev_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return MSA_ERR_LAUNCH;
+        }
+        scratch_dev_ptr[dev] = p;
+    }
+    *out = scratch_dev_ptr[dev];
+    return MSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+msa_status msa_project_workspace_size(int32_t num_tokens, int32_t hidden, int32_t num_heads, uint64_t* bytes)
+{
+    if (!bytes) return MSA_ERR_NULL_POINTER;
+    if (num_tokens < 0 || hidden <= 0 || hidden % kBK || num_heads <= 0 || num_heads > 4096) return MSA_ERR_SHAPE;
+    *bytes = num_tokens == 0 || num_tokens > kSplitMaxTokens ? 0 : split_plan(num_tokens, hidden, num_heads).bytes;
+    return MSA_OK;
+}
+
+msa_status msa_project(const uint16_t* h, int64_t h_row_stride, int32_t num_tokens, int32_t hidden,
+                       const uint16_t* w, int64_t w_row_stride, int32_t num_cols,
+                       uint16_t* x_out, int64_t x_row_stride,
+                       void* workspace, uint64_t workspace_bytes, void* stream)
+{
+    msa_status st = check_gemm(h, h_row_stride, num_tokens, hidden, w, w_row_stride, num_cols);
+    if (st != MSA_OK) return st;
+    if (x_row_stride < num_cols || x_row_stride % 8) return MSA_ERR_STRIDE;
+    if (num_tokens > 0 && !x_out) return MSA_ERR_NULL_POINTER;
+    if (!aligned(x_out, 16)) return MSA_ERR_ALIGNMENT;
+    int64_t tmp;
+    if (__builtin_mul_overflow((int64_t)num_tokens, x_row_stride, &tmp)) return MSA_ERR_OVERFLOW;
+    if (num_tokens == 0) return MSA_OK;
+    Epi e;
+    std::memset(&e, 0, sizeof(e));
+    e.x_out = x_out;
+    e.x_stride = x_row_stride;
+    e.T = num_tokens;
+    const uint64_t need = workspace_need(num_tokens, hidden, num_cols / kHeadDim);
+    if (need > 0 && (!workspace || !aligned(workspace, kAlign) || workspace_bytes < need)) return MSA_ERR_WORKSPACE;
+    const Span spans[] = {
+        {h, row_bytes(num_tokens, h_row_stride, hidden, 2)},
+        {w, row_bytes(num_cols, w_row_stride, hidden, 2)},
+        {x_out, row_bytes(num_tokens, x_row_stride, num_cols, 2)},
         {workspace, need},
     };
-    if ((st = check_operands(spans, sizeof(spans) / sizeof(spans[0]), static_cast<hipStream_t>(stream))) != MSA_OK)
-        return st;
-    return launch_projection<true>(h, h_row_stride, num_tokens, hidden, w, w_row_stride, (int32_t)heads, e, workspace,
-                                   workspace_bytes, static_cast<hipStream_t>(stream));
+    if ((st = check_operands(spans, 4, static_cast<hipStream_t>(stream))) != MSA_OK) return st;
+    return launch_projection<false>(h, h_row_stride, num_tokens, hidden, w, w_row_stride, num_cols / kHeadDim, e,
+                                    workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+msa_status msa_project_produce(const uint16_t* h, int64_t h_row_stride, int32_t num_tokens, int32_t hidden,
+                               const uint16_t* w, int64_t w_row_stride, int32_t head_dim,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t num_iq_heads,
+                               int32_t num_ik_heads, const float* rope_cos, const float* rope_sin,
+                               const int64_t* slots, int32_t page_size, int64_t num_pages,
+                               const uint16_t* q_norm_weight, const uint16_t* k_norm_weight,
+                               const uint16_t* iq_norm_weight, const uint16_t* ik_norm_weight,
+                               float rms_eps, uint16_t* q_out, uint16_t* iq_out,
+                               const msa_cache_view* k_cache, const msa_cache_view* v_cache,
+                               const msa_cache_view* ik_cache,
+                               void* workspace, uint64_t workspace_bytes, void* stream)
+{
+    return project_produce(h, h_row_stride, num_tokens, hidden, w, w_row_stride, head_dim, num_q_heads, num_kv_heads,
+                           num_iq_heads, num_ik_heads, rope_cos, rope_sin, slots, page_size, num_pages, q_norm_weight,
+                           k_norm_weight, iq_norm_weight, ik_norm_weight, rms_eps, q_out, iq_out, k_cache, v_cache,
+                           ik_cache, workspace, workspace_bytes, static_cast<hipStream_t>(stream), false);
+}
+
+msa_status msa_project_produce_noalloc(const uint16_t* h, int64_t h_row_stride, int32_t num_tokens, int32_t hidden,
+                                       const uint16_t* w, int64_t w_row_stride, int32_t head_dim,
+                                       int32_t num_q_heads, int32_t num_kv_heads, int32_t num_iq_heads,
+                                       int32_t num_ik_heads, const float* rope_cos, const float* rope_sin,
+                                       const int64_t* slots, int32_t page_size, int64_t num_pages,
+                                       const uint16_t* q_norm_weight, const uint16_t* k_norm_weight,
+                                       const uint16_t* iq_norm_weight, const uint16_t* ik_norm_weight,
+                                       float rms_eps, uint16_t* q_out, uint16_t* iq_out,
+                                       const msa_cache_view* k_cache, const msa_cache_view* v_cache,
+                                       const msa_cache_view* ik_cache, void* stream)
+{
+    // Sizes first (nothing touches the device for a call that cannot fit).
+    const int64_t heads = (int64_t)num_q_heads + 2 * (int64_t)num_kv_heads + num_iq_heads + num_ik_heads;
+    if (num_tokens < 0 || heads < 1 || heads > 4096 || hidden <= 0 || hidden % kBK) return MSA_ERR_SHAPE;
+    if (workspace_need(num_tokens, hidden, (int32_t)heads) > kScratchBytes) return MSA_ERR_WORKSPACE;
+    void* scratch_dev = nullptr;
+    if (num_tokens > 0) {
+        const msa_status st = scratch_address(&scratch_dev);
+        if (st != MSA_OK) return st;
+    }
+    return project_produce(h, h_row_stride, num_tokens, hidden, w, w_row_stride, head_dim, num_q_heads, num_kv_heads,
+                           num_iq_heads, num_ik_heads, rope_cos, rope_sin, slots, page_size, num_pages, q_norm_weight,
+                           k_norm_weight, iq_norm_weight, ik_norm_weight, rms_eps, q_out, iq_out, k_cache, v_cache,
+                           ik_cache, scratch_dev, kScratchBytes, static_cast<hipStream_t>(stream), true);
 }
 
 }  // extern "C"
