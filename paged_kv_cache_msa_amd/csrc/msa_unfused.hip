@@ -3,9 +3,10 @@
 // launch-count comparison.  Structure: page "Fuse MiniMax-M3 MSA per-layer KV-cache writes into
 // one kernel" ("The problem": division, remainder, index cast and an indexed scatter for each of
 // K, V and index-K; summary: layouts the fused kernel cannot take use the per-cache writes);
-// page "Wire in custom decode kernels for MinimaxM3" (commit notes of the ported fusion: three
-// advanced-indexing writes, each with its own division / remainder / cast); page "Fuse
-// MiniMax-M3 QKV and index projection" (BEFORE figure: separate main and index producers).
+// page "Wire in custom decode kernels for MinimaxM3" (commit notes of the ported fusion: before it,
+// every cache tensor recomputed its slot's page and offset and converted the index on its own
+// before its indexed store); page "Fuse MiniMax-M3 QKV and index projection" (BEFORE figure:
+// separate main and index producers).
 //
 // Every rounding comes from the device arithmetic the fused kernel uses, in the same order, so
 // both paths write the same bytes: the producers hold each head as 8 lanes x (8 + 8) elements
