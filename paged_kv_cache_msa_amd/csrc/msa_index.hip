@@ -4,11 +4,14 @@
 // page "Fuse MiniMax-M3 QKV and index projection", BEFORE/AFTER figures (score visible index-K,
 // max-pool by block, select top-k block IDs).  The reading is documented in include/msa_index.h.
 //
-// Scoring is a stream over the visible keys (about 128 B of fp8 per key and 2 multiply-adds per
-// byte per index-Q head): HBM-bound, so it runs on the vector ALUs, not on MFMA.  Two wavefronts
-// take one (token, block), each a contiguous half of its keys: 8 lanes per key (16 elements each),
-// 8 keys per step, 8 steps per wave for a 128-token block.  Products of bf16 and e4m3/bf16 values are exact in binary64 and so are their
-// sums, so the block scores do not depend on the summation order.
+// Scoring streams the visible keys (128 B of fp8 per key).  Each key meets only the few index-Q
+// heads of its own token (decode tokens share no keys), so there is no reuse for the matrix cores
+// to exploit, and the scores are exact binary64 dot products: it runs on the vector ALUs, where the
+// binary64 conversions and multiply-adds (about 3.5 vector instructions per key byte with two
+// heads) cost about as much time as the key bytes take to arrive, so the kernels are built to keep
+// both busy at once.  8 lanes per key (16 elements each), 8 keys per step.  Products of bf16 and
+// e4m3/bf16 values are exact in binary64 and so are their sums, so the block scores do not depend
+// on the summation order.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -39,6 +42,7 @@ constexpr int kMaxHeadsPerLaunch = 2;
 constexpr int kParts = 2;                  // waves per (token, block), each scoring a contiguous part
 constexpr int kMaxTopK = 64;
 constexpr int kMaxRowBlocks = 4096;
+constexpr int kRankRowBlocks = 512;     // rows of up to this many blocks are ranked in LDS
 
 struct ScoreArgs {
     const uint16_t* iq;
@@ -146,13 +150,14 @@ __device__ __forceinline__ void decode_key(const KeyRaw<kBf16>& r, double* k)
 // key, then the arithmetic, so a wave waits on two memory round trips per batch, not two per step.
 // kStepInPage: page_size and block_tokens are multiples of 8, so the 8 keys of a step always share
 // one page: the page lookup and the 64-bit page base are then wave-uniform (scalar) per step.
-// Four waves per SIMD (at most 128 registers, no spills): batches of 4 steps (2 with bf16 keys,
-// whose raw rows are twice as wide) are the deepest that fit; measured 3% faster than 3 waves with
-// batches of 8.
+// Four waves per SIMD (at most 128 registers, no spills): batches of 3 steps with two fp8 heads, 4
+// with one, 2 with bf16 keys (whose raw rows are twice as wide) are the deepest that fit.  This
+// kernel serves the layouts the batch-in-page kernel below does not take (page sizes or selection
+// blocks that are not multiples of 64 tokens).
 template <int NH, bool kBf16, bool kStepInPage>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void index_scores_kernel(const ScoreArgs a)
 {
-    constexpr int BATCH = kBf16 ? 2 : 4;
+    constexpr int BATCH = kBf16 ? 2 : NH == 2 ? 3 : 4;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     // kParts waves per (token, block), each scoring a contiguous part of the block's keys; their
@@ -279,6 +284,189 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
     }
 }
 
+// ------------------------------------------------------------------ batch-in-page score kernel
+
+// The common layout (pages of a multiple of 64 tokens, selection blocks of a multiple of 64 tokens
+// and at most 64 batches): one wave per (token, block), scoring the block in batches of 8
+// (step, head) items per lane: NH heads x 8 / NH steps of 8 keys, i.e. 32 or 64 consecutive
+// positions, which never cross a page, so one page-table entry and one scalar row base serve a
+// batch.  Two batches' loads are in flight at a time.
+//
+// The 8 lanes of a key each hold a partial dot product of every item.  Instead of summing each item
+// over the 8 lanes (three exchange-and-add steps per item), the items are summed with a
+// reduce-scatter: three steps that halve the number of values a lane carries (4 + 2 + 1 exchanges
+// and additions for 8 items instead of 24), after which lane L of the group holds the full dot
+// product of one item.  For that, lane L keeps item s ^ g(L) in register slot s, where g is the
+// XOR-linear map with g(1) = 1, g(2) = 2, g(4) = 7: the partners of the three steps are lanes L ^ 1,
+// L ^ 2 and L ^ 7 (the last being the DPP half-row mirror), and each step adds one of the lane's
+// slots to the partner's other slot, which holds the same item, with no selects.  The per-lane slot
+// order costs nothing: lane L loads the key of step i ^ (g(L) >> 1) (NH = 2; i ^ g(L) for NH = 1)
+// into batch slot i, and the query of head h ^ (g(L) & 1) into query slot h.  Each item is still an
+// exact binary64 dot product, so the block scores are those of the other kernel, bit for bit.
+__device__ __forceinline__ int slot_map(int sub) { return (sub & 3) ^ ((sub & 4) ? 7 : 0); }
+
+template <bool kBf16, int BATCH>
+struct Batch {
+    KeyRaw<kBf16> raw[BATCH];
+    int32_t pg;
+};
+
+// Three waves per SIMD: the queries (binary64) and two batches of raw keys fit 168 registers
+// without spilling; measured 15% faster than the per-key-reduction kernel at four waves per SIMD.
+template <int NH, bool kBf16>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void index_scores_rs_kernel(const ScoreArgs a)
+{
+    constexpr int BATCH = 8 / NH;                          // steps per batch
+    constexpr int kBatchPos = BATCH * kKeysPerStep;        // 32 or 64 positions
+    // One bf16 head's batch holds 64 raw registers: two of them would not fit.
+    constexpr bool kPairs = !(kBf16 && NH == 1);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    // Block-major item order, as in the other kernel.
+    const uint32_t item = blockIdx.x * kWavesPerBlock + (uint32_t)wave;
+    if (item >= (uint32_t)a.T * (uint32_t)a.max_blocks) return;          // wave-uniform
+    const int32_t b = (int32_t)(item / (uint32_t)a.T);
+    const int32_t t = (int32_t)(item - (uint32_t)b * (uint32_t)a.T);
+    const int ks = lane / kLanesPerKey;
+    const int sub = lane % kLanesPerKey;
+    const int g = slot_map(sub);
+    const int g_head = NH == 2 ? (g & 1) : 0;
+    const int g_step = NH == 2 ? (g >> 1) : g;
+
+    // The query rows go out first (their address needs only t), then the token metadata.
+    uint4 qraw[NH][2];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        const uint16_t* qp = a.iq + ((int64_t)t * a.hiq + a.head0 + (h ^ g_head)) * kHeadDim + sub * kElemsPerLane;
+        qraw[h][0] = reinterpret_cast<const uint4*>(qp)[0];
+        qraw[h][1] = reinterpret_cast<const uint4*>(qp)[1];
+    }
+    const int32_t pos = a.pos[t];
+    const int32_t sq = a.seq[t];
+    const int64_t p0_64 = (int64_t)b * a.block_tokens;
+    const int32_t p0 = (int32_t)min(p0_64, (int64_t)INT32_MAX);   // exact whenever the block is scored
+    const int32_t p_end = (int32_t)min(p0_64 + a.block_tokens, (int64_t)pos + 1);
+    // Own slot and the page-table entries of the block's batches (lane j: batch j), requested together.
+    int32_t own_off, unused;
+    const int64_t own_pg = page_of(a, sq, pos, &own_off);
+    int32_t batch_pg = -1;
+    {
+        const int64_t ps = p0_64 + (int64_t)lane * kBatchPos;
+        if (ps < p_end) batch_pg = (int32_t)page_of(a, sq, (int32_t)ps, &unused);
+    }
+    double best = -INFINITY;      // lane L: head g(L) & 1 (NH = 2)
+
+    if (own_pg >= 0 && p0_64 <= pos) {
+        const double scale = kBf16 ? 1.0 : (double)*a.ik.scale;
+        const int64_t head_off = (int64_t)(a.head0 / a.group) * a.ik.sh;
+        const int64_t st = a.ik.st;
+        const int32_t n_batches = (p_end - p0 + kBatchPos - 1) / kBatchPos;
+        // Loads of batch j.  Past the last batch, and for a batch without a page, the pool's first
+        // row is read (a valid address) and discarded.
+        auto fetch = [&](int32_t j) {
+            Batch<kBf16, BATCH> bt;
+            const int32_t pb = p0 + j * kBatchPos;
+            bt.pg = j < n_batches ? __builtin_amdgcn_readlane(batch_pg, j & (kWave - 1)) : -1;
+            const int32_t lp = a.page_shift >= 0 ? pb >> a.page_shift : pb / a.page_size;
+            const int32_t off0 = pb - lp * a.page_size;
+            const int64_t base = bt.pg >= 0 ? (int64_t)bt.pg * a.ik.sp + head_off + (int64_t)off0 * st : 0;
+#pragma unroll
+            for (int i = 0; i < BATCH; ++i) {
+                const int key = (i ^ g_step) * kKeysPerStep + ks;       // within the batch
+                bt.raw[i] = load_key<kBf16>(a.ik, (bt.pg >= 0 ? base + (int64_t)key * st : 0) + sub * kElemsPerLane);
+            }
+            return bt;
+        };
+        double qs[NH][kElemsPerLane];
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            const uint32_t w[8] = {qraw[h][0].x, qraw[h][0].y, qraw[h][0].z, qraw[h][0].w,
+                                   qraw[h][1].x, qraw[h][1].y, qraw[h][1].z, qraw[h][1].w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                qs[h][2 * i] = (double)__uint_as_float(w[i] << 16);
+                qs[h][2 * i + 1] = (double)__uint_as_float(w[i] & 0xffff0000u);
+            }
+        }
+        // Sums batch j (its loads in bt) into this lane's running maximum.
+        auto consume = [&](const Batch<kBf16, BATCH>& bt, int32_t j) {
+            double acc[BATCH][NH];
+#pragma unroll
+            for (int i = 0; i < BATCH; ++i)
+#pragma unroll
+                for (int h = 0; h < NH; ++h) acc[i][h] = 0.0;
+#pragma unroll
+            for (int i = 0; i < BATCH; ++i) {
+                // four elements at a time (keeps the decoded values few)
+#pragma unroll
+                for (int e4 = 0; e4 < kElemsPerLane / 4; ++e4) {
+                    double k[4];
+                    if (kBf16) {
+                        const uint32_t w0 = bt.raw[i].w[2 * e4], w1 = bt.raw[i].w[2 * e4 + 1];
+                        k[0] = (double)__uint_as_float(w0 << 16);
+                        k[1] = (double)__uint_as_float(w0 & 0xffff0000u);
+                        k[2] = (double)__uint_as_float(w1 << 16);
+                        k[3] = (double)__uint_as_float(w1 & 0xffff0000u);
+                    } else {
+                        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)bt.raw[i].w[e4], false);
+                        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)bt.raw[i].w[e4], true);
+                        k[0] = (double)lo[0];
+                        k[1] = (double)lo[1];
+                        k[2] = (double)hi[0];
+                        k[3] = (double)hi[1];
+                    }
+#pragma unroll
+                    for (int h = 0; h < NH; ++h)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[i][h] = __builtin_fma(qs[h][4 * e4 + e], k[e], acc[i][h]);
+                }
+            }
+            // Slot s = NH * i + h.  Reduce-scatter over the 8 lanes of the key.
+            double v8[8];
+#pragma unroll
+            for (int i = 0; i < BATCH; ++i)
+#pragma unroll
+                for (int h = 0; h < NH; ++h) v8[NH * i + h] = acc[i][h];
+            double v4[4], v2[2];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) v4[m] = v8[2 * m] + dpp_f64<0xb1>(v8[2 * m + 1]);     // partner L ^ 1
+#pragma unroll
+            for (int m = 0; m < 2; ++m) v2[m] = v4[2 * m] + dpp_f64<0x4e>(v4[2 * m + 1]);     // partner L ^ 2
+            const double dot = v2[0] + dpp_f64<0x141>(v2[1]);                                 // partner L ^ 7
+            const int32_t p = p0 + j * kBatchPos + g_step * kKeysPerStep + ks;   // this lane's key
+            if (bt.pg >= 0 && p < p_end) best = max_no_nan(best, dot * scale);
+        };
+        if (kPairs) {
+            // Two batches' loads in flight together; past the last batch the second reads a
+            // discarded row.
+            for (int32_t j = 0; j < n_batches; j += 2) {
+                const Batch<kBf16, BATCH> A = fetch(j);
+                const Batch<kBf16, BATCH> B = fetch(j + 1);
+                consume(A, j);
+                consume(B, j + 1);
+            }
+        } else {
+            for (int32_t j = 0; j < n_batches; ++j) consume(fetch(j), j);
+        }
+    }
+    // Max over the lanes that hold the same head: the 8 key slots (lanes ^ 8, 16, 32) and, within a
+    // key's lanes, those with the same g & 1 (NH = 2: L, L ^ 2, L ^ 5, L ^ 7; NH = 1: all 8).
+    best = max_no_nan(best, shfl_xor_f64(best, 8));
+    best = max_no_nan(best, shfl_xor_f64(best, 16));
+    best = max_no_nan(best, shfl_xor_f64(best, 32));
+    if (NH == 2) {
+        best = max_no_nan(best, shfl_xor_f64(best, 2));
+        best = max_no_nan(best, shfl_xor_f64(best, 5));
+    } else {
+        best = max_no_nan(best, shfl_xor_f64(best, 1));
+        best = max_no_nan(best, shfl_xor_f64(best, 2));
+        best = max_no_nan(best, shfl_xor_f64(best, 4));
+    }
+    // Lane h (h < NH) now holds head h's maximum: g(0) = 0, g(1) = 1.
+    if (lane < NH) a.out[((int64_t)(a.head0 + lane) * a.T + t) * a.max_blocks + b] = best;
+}
+
 // (score, index) order of the selection: higher score first, then lower index.
 __device__ __forceinline__ bool before(double s1, int32_t i1, double s2, int32_t i2)
 {
@@ -288,8 +476,6 @@ __device__ __forceinline__ bool before(double s1, int32_t i1, double s2, int32_t
 // Rows of up to kRankRowBlocks blocks: one work-group per row stages the row in LDS, and every
 // thread computes the rank of each of its candidates (how many candidates are ordered before it); a
 // candidate of rank r < top_k is the r-th pick.  No serial rounds.
-constexpr int kRankRowBlocks = 512;
-
 __global__ __launch_bounds__(kBlock) void index_topk_rank_kernel(const double* scores, int32_t rows, int32_t nb,
                                                                  int32_t top_k, int32_t* ids, int32_t* counts)
 {
@@ -376,16 +562,25 @@ __global__ __launch_bounds__(kBlock) void index_topk_kernel(const double* scores
     if (counts && lane == 0) counts[r] = n;
 }
 
-}  // namespace
+msa_status launch_topk(const double* block_scores, int32_t rows, int32_t max_blocks, int32_t top_k,
+                       int32_t* block_ids, int32_t* counts, hipStream_t stream)
+{
+    const bool rank = max_blocks <= kRankRowBlocks;
+    const dim3 grid(rank ? (unsigned)rows : (unsigned)(((int64_t)rows + kWavesPerBlock - 1) / kWavesPerBlock));
+    void* args[] = {const_cast<double**>(&block_scores), &rows, &max_blocks, &top_k, &block_ids, &counts};
+    const void* fn = rank ? reinterpret_cast<const void*>(&index_topk_rank_kernel)
+                          : reinterpret_cast<const void*>(&index_topk_kernel);
+    const hipError_t e = hipLaunchKernel(fn, grid, dim3(kBlock), args, 0, stream);
+    return e == hipSuccess ? MSA_OK : MSA_ERR_LAUNCH;
+}
 
-extern "C" {
-
-msa_status msa_index_scores(const uint16_t* iq, int32_t num_tokens, int32_t head_dim, int32_t num_iq_heads,
-                            const int32_t* positions, const int32_t* seq_idx,
-                            const int32_t* page_table, int64_t page_table_stride, int32_t num_seqs,
-                            int32_t max_pages_per_seq, int32_t page_size, int64_t num_pages,
-                            const msa_cache_view* ik_cache, int32_t block_tokens, int32_t max_blocks,
-                            double* block_scores, void* stream)
+// msa_index_scores' checks and launches.
+msa_status index_scores(const uint16_t* iq, int32_t num_tokens, int32_t head_dim, int32_t num_iq_heads,
+                        const int32_t* positions, const int32_t* seq_idx,
+                        const int32_t* page_table, int64_t page_table_stride, int32_t num_seqs,
+                        int32_t max_pages_per_seq, int32_t page_size, int64_t num_pages,
+                        const msa_cache_view* ik_cache, int32_t block_tokens, int32_t max_blocks,
+                        double* block_scores, void* stream)
 {
     if (head_dim != kHeadDim) return MSA_ERR_UNSUPPORTED;
     if (num_tokens < 0 || num_iq_heads < 1 || num_iq_heads > 4096 || block_tokens <= 0 || max_blocks < 0)
@@ -432,7 +627,11 @@ msa_status msa_index_scores(const uint16_t* iq, int32_t num_tokens, int32_t head
     a.max_blocks = max_blocks;
     a.ik = ik;
     a.out = block_scores;
-    const dim3 grid((unsigned)((items + kWavesPerBlock / kParts - 1) / (kWavesPerBlock / kParts)));
+    // Batches of 32 / 64 positions never cross a page, and the parts start on batch boundaries.
+    const bool batch_in_page = page_size % 64 == 0 && block_tokens % 64 == 0 && block_tokens <= 64 * 32;
+    const bool in_page = page_size % kKeysPerStep == 0 && block_tokens % kKeysPerStep == 0;
+    const int items_per_group = batch_in_page ? kWavesPerBlock : kWavesPerBlock / kParts;
+    const dim3 grid((unsigned)((items + items_per_group - 1) / items_per_group));
     hipStream_t s = static_cast<hipStream_t>(stream);
     {
         const Span spans[] = {
@@ -454,9 +653,13 @@ msa_status msa_index_scores(const uint16_t* iq, int32_t num_tokens, int32_t head
         const int nh = (group_end - h0 >= kMaxHeadsPerLaunch) ? kMaxHeadsPerLaunch : 1;
         a.head0 = h0;
         void* args[] = {&a};
-        const bool in_page = page_size % kKeysPerStep == 0 && block_tokens % kKeysPerStep == 0;
         const void* fn;
-        if (in_page)
+        if (batch_in_page)
+            fn = ik.is_bf16 ? (nh == 2 ? reinterpret_cast<const void*>(&index_scores_rs_kernel<2, true>)
+                                       : reinterpret_cast<const void*>(&index_scores_rs_kernel<1, true>))
+                            : (nh == 2 ? reinterpret_cast<const void*>(&index_scores_rs_kernel<2, false>)
+                                       : reinterpret_cast<const void*>(&index_scores_rs_kernel<1, false>));
+        else if (in_page)
             fn = ik.is_bf16 ? (nh == 2 ? reinterpret_cast<const void*>(&index_scores_kernel<2, true, true>)
                                        : reinterpret_cast<const void*>(&index_scores_kernel<1, true, true>))
                             : (nh == 2 ? reinterpret_cast<const void*>(&index_scores_kernel<2, false, true>)
@@ -473,6 +676,23 @@ msa_status msa_index_scores(const uint16_t* iq, int32_t num_tokens, int32_t head
     return MSA_OK;
 }
 
+
+}  // namespace
+
+extern "C" {
+
+msa_status msa_index_scores(const uint16_t* iq, int32_t num_tokens, int32_t head_dim, int32_t num_iq_heads,
+                            const int32_t* positions, const int32_t* seq_idx,
+                            const int32_t* page_table, int64_t page_table_stride, int32_t num_seqs,
+                            int32_t max_pages_per_seq, int32_t page_size, int64_t num_pages,
+                            const msa_cache_view* ik_cache, int32_t block_tokens, int32_t max_blocks,
+                            double* block_scores, void* stream)
+{
+    return index_scores(iq, num_tokens, head_dim, num_iq_heads, positions, seq_idx, page_table, page_table_stride,
+                        num_seqs, max_pages_per_seq, page_size, num_pages, ik_cache, block_tokens, max_blocks,
+                        block_scores, stream);
+}
+
 msa_status msa_index_topk(const double* block_scores, int32_t rows, int32_t max_blocks, int32_t top_k,
                           int32_t* block_ids, int32_t* counts, void* stream)
 {
@@ -486,13 +706,7 @@ msa_status msa_index_topk(const double* block_scores, int32_t rows, int32_t max_
                           {counts, nbytes(rows, 4)}};
     const msa_status st = check_operands(spans, 3, static_cast<hipStream_t>(stream));
     if (st != MSA_OK) return st;
-    const bool rank = max_blocks <= kRankRowBlocks;
-    const dim3 grid(rank ? (unsigned)rows : (unsigned)(((int64_t)rows + kWavesPerBlock - 1) / kWavesPerBlock));
-    void* args[] = {const_cast<double**>(&block_scores), &rows, &max_blocks, &top_k, &block_ids, &counts};
-    const void* fn = rank ? reinterpret_cast<const void*>(&index_topk_rank_kernel)
-                          : reinterpret_cast<const void*>(&index_topk_kernel);
-    const hipError_t e = hipLaunchKernel(fn, grid, dim3(kBlock), args, 0, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? MSA_OK : MSA_ERR_LAUNCH;
+    return launch_topk(block_scores, rows, max_blocks, top_k, block_ids, counts, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -120,10 +120,12 @@ def test_producer_then_indexer(make):
     compare("chain", got, oracle_index(wl, r["iq"], host[2], nb))
 
 
-@pytest.mark.parametrize("hiq,hik", [(4, 1), (4, 2), (1, 1), (3, 1)])
-def test_index_head_groups(hiq, hik):
-    """Several index-Q heads per index-K head and several index-K heads (head h reads h // (hiq/hik))."""
-    wl = W.ragged(40, seed=hiq * 10 + hik, heads=(2, 1, hiq, hik), pad_frac=0.1)
+@pytest.mark.parametrize("hiq,hik,dtype", [(4, 1, 0), (4, 2, 0), (1, 1, 0), (3, 1, 0), (1, 1, 1), (3, 1, 1)])
+def test_index_head_groups(hiq, hik, dtype):
+    """Several index-Q heads per index-K head and several index-K heads (head h reads h // (hiq/hik)),
+    fp8 and bf16 keys: launches of two heads and of one (one head per wave takes batches of 8 steps;
+    with bf16 keys one batch at a time)."""
+    wl = W.ragged(40, seed=hiq * 10 + hik, heads=(2, 1, hiq, hik), pad_frac=0.1, cache_dtypes=(0, 0, dtype))
     fill = W.index_cache_fill(wl, seed=hiq)
     iq = W.index_queries(wl.T, hiq, seed=hik)
     nb = W.index_blocks(wl) + 3          # extra, never-visible blocks stay -inf
@@ -134,11 +136,13 @@ def test_index_head_groups(hiq, hik):
     compare(f"groups {hiq}/{hik}", got, oracle_index(wl, iq, fill, nb))
 
 
-@pytest.mark.parametrize("block_tokens", [100, 36, 256, 8, 24, 136, 2048])
+@pytest.mark.parametrize("block_tokens", [100, 36, 256, 8, 24, 136, 2048, 64, 192, 4096])
 def test_index_other_block_sizes(block_tokens):
     """Block sizes that are not multiples of the 8-key step (steps straddle pages: per-key page
     lookups), larger ones, and multiples of 8 whose two wave parts are uneven or (8) leave the
-    second part empty; 2048 spans more than 64 steps per part (page entries fetched in chunks)."""
+    second part empty; 2048 spans more than 64 steps per part (page entries fetched in chunks).
+    Multiples of 64 up to 2048 take the batch-in-page kernel (64: one pair of batches; 192: an odd
+    number of batches, the second of the last pair discarded); 4096 does not."""
     wl = W.ragged(48, seed=block_tokens, pad_frac=0.1)
     fill = W.index_cache_fill(wl, seed=block_tokens)
     iq = W.index_queries(wl.T, wl.hiq, seed=block_tokens)
@@ -150,10 +154,11 @@ def test_index_other_block_sizes(block_tokens):
     compare(f"block {block_tokens}", got, oracle_index(wl, iq, fill, nb, block_tokens=block_tokens))
 
 
-@pytest.mark.parametrize("P", [16, 48, 100])
+@pytest.mark.parametrize("P", [16, 48, 100, 128, 192])
 def test_index_other_page_sizes(P):
     """Page sizes other than 64 under 128-token blocks: a power of two, a multiple of 8 that takes the
-    division path, and one that is not a multiple of the 8-key step (per-key page lookups)."""
+    division path, and one that is not a multiple of the 8-key step (per-key page lookups); 128 and
+    192 take the batch-in-page kernel (192 by division)."""
     wl = W.ragged(48, seed=300 + P, pad_frac=0.1, page_size=P)
     fill = W.index_cache_fill(wl, seed=P)
     iq = W.index_queries(wl.T, wl.hiq, seed=P)
