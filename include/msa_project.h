@@ -17,16 +17,17 @@
  * msa_project_produce runs the same GEMM (same kernel, same accumulation order) and, instead of
  * storing x, hands each head's bf16-rounded row to the producer's arithmetic (msa_produce.h):
  * per-head RMSNorm + neox RoPE on Q, K, index-Q and index-K, compact Q and index-Q, and K, V,
- * index-K into the paged caches.  Its outputs equal msa_produce applied to msa_project's x, except
+ * index-K into the paged caches.  Its outputs equal msa_produce applied to msa_project's x: bit for
+ * bit up to 1,024 tokens (the same operations in the same order), and for larger batches except
  * where a head's binary64 sum of squares is inexact (a head spanning more than about 2^15 in
  * magnitude), where the two sum orders may differ in the last binary64 bit.  The packed row never
  * touches memory.  The pages stop at a single wider GEMM feeding a separate fused producer; this
  * entry point goes one step further.
  *
  * Kernels: for up to 1,024 tokens (the decode and verify batches) two launches, a split-K kernel
- * (heads x 64-token chunks x K slices, partial sums in the workspace) and a kernel that adds the
- * slices in a fixed order and runs the epilogue; for larger batches (prefill) one 256 x 256 tiled
- * kernel.  All on v_mfma_f32_32x32x16_bf16.
+ * (heads x 64-token chunks x K slices, partial sums in the workspace, on v_mfma_f32_32x32x16_bf16)
+ * and a kernel that adds the slices in a fixed order and runs the epilogue in msa_produce's row
+ * layout; for larger batches (prefill) one 256 x 256 tiled kernel on the same matrix instruction.
  *
  * Conventions are those of msa_produce.h (operands checked for residency on eager calls, no allocation,
  * no synchronisation, all checks on the host before any launch, MSA_OK means enqueued,

@@ -17,11 +17,11 @@
 //                          requested into LDS at once with direct global -> LDS loads (the latency
 //                          of the whole slice is paid once), then each wave multiplies 32 of the
 //                          head's features against the chunk; partial sums go to the workspace.
-//   project_reduce_kernel  one work-group per (head, chunk, 32-token block): four waves add the
-//                          slices' partial sums in slice order (the same order on every call) while
-//                          a fifth fetches the epilogue's inputs, then runs the epilogue.  The
-//                          kernel boundary between the two makes the partial sums visible across
-//                          XCDs; no device-scope fence is needed.
+//   project_reduce_rows_kernel  one wave per (head, 8 tokens), in msa_produce's row layout (8
+//                          lanes per head row): each lane adds its 16 features' partial sums in slice
+//                          order (the same order on every call), rounds them to bf16 and runs the
+//                          producer's arithmetic on them.  The kernel boundary between the two makes
+//                          the partial sums visible across XCDs; no device-scope fence is needed.
 //   project_tile_kernel    larger batches: 256 features (2 heads) x 256 tokens per work-group, eight
 //                          waves (two per SIMD) of one head x 64 tokens each, 64-wide K steps
 //                          through two LDS buffers filled by direct global -> LDS loads one step
@@ -98,44 +98,6 @@ __device__ __forceinline__ int stream_of(const Epi& e, int head)
 {
     const int h_k = e.hq, h_v = e.hq + e.hkv, h_iq = e.hq + 2 * e.hkv, h_ik = h_iq + e.hiq;
     return head < h_k ? kQ : head < h_v ? kK : head < h_iq ? kV : head < h_ik ? kIQ : kIK;
-}
-
-// Loads EpiIn (produce mode only).  Lanes of tokens past T read token T - 1 and no slot.
-__device__ __forceinline__ void epilogue_load(const Epi& e, int head, int32_t t, EpiIn& in)
-{
-    const int hh = (threadIdx.x & 63) >> 5;
-    const int st = stream_of(e, head);
-    const bool tok = t < e.T;
-    const bool cache_row = st == kK || st == kV || st == kIK;
-    in.slot = tok && cache_row ? e.slots[t] : -1;
-    // Read here, with the other inputs, rather than at the cast: after the arithmetic it would be one
-    // more memory round trip before the stores.
-    const CacheDev& cd = e.cache[st == kK ? 0 : st == kV ? 1 : 2];
-    in.scale = cache_row && !cd.is_bf16 ? *cd.scale : 1.0f;
-    if (st == kV) return;
-    const uint16_t* wp = e.w[st == kQ ? 0 : st == kK ? 1 : st == kIQ ? 2 : 3] + 4 * hh;
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const uint2 wv = *reinterpret_cast<const uint2*>(wp + 32 * b + 8 * g);
-            in.w[b][4 * g] = bf16_lo(wv.x);
-            in.w[b][4 * g + 1] = bf16_hi(wv.x);
-            in.w[b][4 * g + 2] = bf16_lo(wv.y);
-            in.w[b][4 * g + 3] = bf16_hi(wv.y);
-        }
-    const int32_t tl = tok ? t : e.T - 1;
-    const float* cp = e.cos + (int64_t)tl * kHalf + 4 * hh;
-    const float* sp = e.sin + (int64_t)tl * kHalf + 4 * hh;
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const float4 c4 = *reinterpret_cast<const float4*>(cp + 32 * b + 8 * g);
-            const float4 s4 = *reinterpret_cast<const float4*>(sp + 32 * b + 8 * g);
-            in.c[b][4 * g] = c4.x; in.c[b][4 * g + 1] = c4.y; in.c[b][4 * g + 2] = c4.z; in.c[b][4 * g + 3] = c4.w;
-            in.s[b][4 * g] = s4.x; in.s[b][4 * g + 1] = s4.y; in.s[b][4 * g + 2] = s4.z; in.s[b][4 * g + 3] = s4.w;
-        }
 }
 
 // Where one token's head row goes: dst == nullptr means nowhere (a token past T, or a cache row
@@ -247,31 +209,6 @@ __device__ __forceinline__ RowOut epilogue_math(const Epi& e, int head, int32_t 
     return o;
 }
 
-// Stores the row of epilogue_math from each lane's registers (lane l holds 16 of the row's features
-// in four 4-feature groups per 32-feature block).
-__device__ __forceinline__ void row_store_direct(const RowOut& o, const float (&a)[4][16])
-{
-    if (o.dst == nullptr) return;
-    const int hh = (threadIdx.x & 63) >> 5;
-    if (o.fp8) {
-        uint8_t* dst = o.dst + 4 * hh;
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-                *reinterpret_cast<uint32_t*>(dst + 32 * b + 8 * g) =
-                    e4m3x4(a[b][4 * g] * o.m, a[b][4 * g + 1] * o.m, a[b][4 * g + 2] * o.m, a[b][4 * g + 3] * o.m);
-    } else {
-        uint16_t* dst = reinterpret_cast<uint16_t*>(o.dst) + 4 * hh;
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-                *reinterpret_cast<uint2*>(dst + 32 * b + 8 * g) =
-                    make_uint2(bf16x2(a[b][4 * g], a[b][4 * g + 1]), bf16x2(a[b][4 * g + 2], a[b][4 * g + 3]));
-    }
-}
-
 // Stores the rows of a 32-token block (lane l holds part of token l % 32's row, as above) through
 // this wave's 8 KiB of LDS: every lane first writes its pieces into the row-major block, then each
 // lane stores 16 contiguous bytes of one row, so that a store instruction writes whole rows.  In
@@ -378,8 +315,8 @@ void project_split_kernel(const SplitArgs a)
     uint8_t* lds_a = smem;
     uint8_t* lds_b = smem + (size_t)128 * planes * 8 * 16;
     const uint16_t* wrow = a.w + (int64_t)head * kHeadDim * a.w_stride + k_begin;
-    const uint16_t* hrow = a.h + k_begin;
     const int64_t ws = a.w_stride, hs = a.h_stride;
+    const uint16_t* hrow = a.h + k_begin;
     const int t_first = tc * kChunk, t_last = a.e.T - 1;
     for (int g = 0; g < planes; ++g) {
         plane_to_lds(lds_a, 128, g, [&](int r) { return wrow + r * ws; });
@@ -423,61 +360,147 @@ void project_split_kernel(const SplitArgs a)
     }
 }
 
-// One work-group per (head, chunk, 32-token block).  Waves 0..3 add, in slice order, the partial
-// sums of feature block w and leave them in LDS; meanwhile wave 4 fetches the epilogue's inputs
-// (norm weights, RoPE coefficients, slots), then takes the head rows from LDS and runs the
-// epilogue.
+// One wave per (head, 8 tokens), in the producer's row layout: lane (ts = lane / 8, sub = lane % 8)
+// holds features [8 sub, 8 sub + 8) and [64 + 8 sub, 64 + 8 sub + 8) of token 8 g + ts's head row, so
+// both rotate-half partners sit in one lane and a head's sum of squares is an 8-lane reduction, as
+// in msa_produce (the same operations in the same order: the fused outputs equal msa_produce
+// applied to msa_project's row, bit for bit).  Each lane adds the slices' partial sums of its 16
+// features in slice order (the order of the other reduce kernel), reading them straight from the
+// split kernel's fragment layout: within a 32-feature block, lane l of a fragment holds token l % 32
+// and features 8 q + 4 (l / 32) + [0, 4) at index [q][l].  Many small work-groups spread the
+// partial sums' reads over the whole chip.
 template <bool kProduce>
-__global__ __launch_bounds__(320) void project_reduce_kernel(const SplitArgs a)
+__global__ __launch_bounds__(64) void project_reduce_rows_kernel(const SplitArgs a)
 {
-    __shared__ float xchg[4][16][64];                          // [feature block][i][lane]
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int tb = (int)(blockIdx.x & 1);
-    const int pair = (int)(blockIdx.x >> 1);
-    const int tc = pair % a.n_tc;
-    const int head = pair / a.n_tc;
-    const int32_t t = tc * kChunk + tb * 32 + lane % 32;
-    if (wave < 4) {
-        const f32x4_t* base = reinterpret_cast<const f32x4_t*>(a.part + (int64_t)pair * a.splits * kPartFloats) +
-                              ((wave * 2 + tb) * 4) * 64 + lane;
-        float part[16] = {};
+    const Epi& e = a.e;
+    const int lane = threadIdx.x;
+    const int ts = lane / 8, sub = lane % 8;
+    const int n_tg = (e.T + 7) / 8;
+    const int head = (int)(blockIdx.x / (uint32_t)n_tg);
+    const int g = (int)(blockIdx.x - (uint32_t)head * (uint32_t)n_tg);
+    const int32_t t = g * 8 + ts;
+    const bool tok = t < e.T;
+    const int32_t tc = t / kChunk, t64 = t % kChunk, tb = t64 / 32, t32 = t64 % 32;
+    const int pair = head * a.n_tc + tc;
+
+    // Epilogue inputs first (their addresses need no partial sum).
+    const int st = kProduce ? stream_of(e, head) : 0;
+    uint4 wa = make_uint4(0, 0, 0, 0), wb = make_uint4(0, 0, 0, 0);
+    float4 c4[1][2], s4[1][2];
+    int64_t slot = -1;
+    float scale = 1.0f;
+    if (kProduce) {
+        if (st != kV) {
+            const uint16_t* w = e.w[st == kQ ? 0 : st == kK ? 1 : st == kIQ ? 2 : 3];
+            wa = *reinterpret_cast<const uint4*>(w + sub * 8);
+            wb = *reinterpret_cast<const uint4*>(w + kHalf + sub * 8);
+        }
+        const int32_t tl = tok ? t : e.T - 1;
+        const float4* cp = reinterpret_cast<const float4*>(e.cos + (int64_t)tl * kHalf + sub * 8);
+        const float4* sp = reinterpret_cast<const float4*>(e.sin + (int64_t)tl * kHalf + sub * 8);
+        c4[0][0] = cp[0]; c4[0][1] = cp[1];
+        s4[0][0] = sp[0]; s4[0][1] = sp[1];
+        const bool cache_row = st == kK || st == kV || st == kIK;
+        if (cache_row && tok) slot = e.slots[t];
+        const CacheDev& cd = e.cache[st == kK ? 0 : st == kV ? 1 : 2];
+        if (cache_row && !cd.is_bf16) scale = *cd.scale;
+    }
+
+    // The 16 features' sums over the K slices, in slice order.
+    float v[16];
+    {
+        const f32x4_t* base = reinterpret_cast<const f32x4_t*>(a.part + (int64_t)pair * a.splits * kPartFloats);
+        // fragment index of (32-feature block w, token block tb, q, lane) in 16-byte units
+        auto at = [&](int w, int hh) { return ((w * 2 + tb) * 4 + (sub % 4)) * 64 + t32 + 32 * hh; };
+        const int i00 = at(sub / 4, 0), i01 = at(sub / 4, 1), i10 = at(2 + sub / 4, 0), i11 = at(2 + sub / 4, 1);
+        // Eight slices' loads in flight at once (past the last slice: the last one again, unused).
         for (int s0 = 0; s0 < a.splits; s0 += 8) {
-            f32x4_t v[8][4];
+            f32x4_t x[8][4];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                const int sl = min(s0 + u, a.splits - 1);          // past the last slice: reread it, unused
-#pragma unroll
-                for (int q = 0; q < 4; ++q) v[u][q] = base[(int64_t)sl * (kPartFloats / 4) + q * 64];
+                const f32x4_t* p = base + (int64_t)min(s0 + u, a.splits - 1) * (kPartFloats / 4);
+                x[u][0] = p[i00];
+                x[u][1] = p[i01];
+                x[u][2] = p[i10];
+                x[u][3] = p[i11];
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const bool live = s0 + u < a.splits, first = s0 + u == 0;
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
+                for (int c = 0; c < 4; ++c)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float x = v[u][q][e];
-                        const float sum = first ? x : part[4 * q + e] + x;
-                        part[4 * q + e] = live ? sum : part[4 * q + e];
+                    for (int j = 0; j < 4; ++j) {
+                        const float sum = first ? x[u][c][j] : v[4 * c + j] + x[u][c][j];
+                        v[4 * c + j] = live ? sum : v[4 * c + j];
                     }
             }
         }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) xchg[wave][i][lane] = part[i];
-        __syncthreads();
+    }
+    // The packed row's values: the sums rounded to bf16.
+    uint4 ra = make_uint4(bf16x2(v[0], v[1]), bf16x2(v[2], v[3]), bf16x2(v[4], v[5]), bf16x2(v[6], v[7]));
+    uint4 rb = make_uint4(bf16x2(v[8], v[9]), bf16x2(v[10], v[11]), bf16x2(v[12], v[13]), bf16x2(v[14], v[15]));
+    if (!kProduce) {
+        if (tok) {
+            uint16_t* dst = e.x_out + (int64_t)t * e.x_stride + head * kHeadDim + sub * 8;
+            *reinterpret_cast<uint4*>(dst) = ra;
+            *reinterpret_cast<uint4*>(dst + kHalf) = rb;
+        }
         return;
     }
-    EpiIn in;
-    if (kProduce) epilogue_load(a.e, head, t, in);
-    __syncthreads();
-    float acc[4][16];
+    float x[16];
+    unpack8(ra, x);
+    unpack8(rb, x + 8);
+    float o[16];
+    if (st == kV) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+        for (int j = 0; j < 16; ++j) o[j] = x[j];
+    } else {
+        double acc = 0.0;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[b][i] = xchg[b][i][lane];
-    const RowOut o = epilogue_math<kProduce, false>(a.e, head, t, acc, in);
-    row_store_direct(o, acc);
+        for (int j = 0; j < 16; ++j) acc = __builtin_fma((double)x[j], (double)x[j], acc);
+        const float r = rms_from_ss(head_sum8(acc), e.eps);
+        float wv[16];
+        unpack8(wa, wv);
+        unpack8(wb, wv + 8);
+        const float cf[8] = {c4[0][0].x, c4[0][0].y, c4[0][0].z, c4[0][0].w, c4[0][1].x, c4[0][1].y, c4[0][1].z, c4[0][1].w};
+        const float sf[8] = {s4[0][0].x, s4[0][0].y, s4[0][0].z, s4[0][0].w, s4[0][1].x, s4[0][1].y, s4[0][1].z, s4[0][1].w};
+        float y[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) y[j] = (x[j] * r) * wv[j];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            o[j] = y[j] * cf[j] - y[j + 8] * sf[j];
+            o[j + 8] = y[j + 8] * cf[j] + y[j] * sf[j];
+        }
+    }
+    if (!tok) return;
+    const int h_k = e.hq, h_v = e.hq + e.hkv, h_iq = e.hq + 2 * e.hkv, h_ik = h_iq + e.hiq;
+    if (st == kQ || st == kIQ) {
+        uint16_t* dst = (st == kQ ? e.q_out + ((int64_t)t * e.hq + head) * kHeadDim
+                                  : e.iq_out + ((int64_t)t * e.hiq + (head - h_iq)) * kHeadDim) + sub * 8;
+        *reinterpret_cast<uint4*>(dst) = bf16x8(o);
+        *reinterpret_cast<uint4*>(dst + kHalf) = bf16x8(o + 8);
+        return;
+    }
+    if (slot < 0) return;
+    const int64_t page = slot / e.page_size;
+    if (page >= e.num_pages) return;
+    const int64_t off = slot - page * e.page_size;
+    const CacheDev& cd = e.cache[st == kK ? 0 : st == kV ? 1 : 2];
+    const int hl = st == kK ? head - h_k : st == kV ? head - h_v : head - h_ik;
+    const int64_t elem = page * cd.sp + off * cd.st + (int64_t)hl * cd.sh + sub * 8;
+    if (cd.is_bf16) {
+        uint16_t* dst = reinterpret_cast<uint16_t*>(cd.data) + elem;
+        *reinterpret_cast<uint4*>(dst) = bf16x8(o);
+        *reinterpret_cast<uint4*>(dst + kHalf) = bf16x8(o + 8);
+    } else {
+        uint2 lo, hi;
+        e4m3x16(o, inv_scale(scale), lo, hi);
+        uint8_t* dst = cd.data + elem;
+        *reinterpret_cast<uint2*>(dst) = lo;
+        *reinterpret_cast<uint2*>(dst + kHalf) = hi;
+    }
 }
 
 // ------------------------------------------------------------------ tiled kernel (prefill)
@@ -721,8 +744,8 @@ msa_status launch_projection(const uint16_t* h, int64_t h_row_stride, int32_t T,
         err = hipLaunchKernel(reinterpret_cast<const void*>(&project_split_kernel), dim3((unsigned)(pairs * p.splits)),
                               dim3(256), args, 0, s);
         if (err == hipSuccess)
-            err = hipLaunchKernel(reinterpret_cast<const void*>(&project_reduce_kernel<kProduce>),
-                                  dim3((unsigned)(pairs * 2)), dim3(320), args, 0, s);
+            err = hipLaunchKernel(reinterpret_cast<const void*>(&project_reduce_rows_kernel<kProduce>),
+                                  dim3((unsigned)((int64_t)heads * ((T + 7) / 8))), dim3(64), args, 0, s);
     } else {
         TileArgs a;
         a.h = h;

@@ -196,6 +196,35 @@ def test_project_produce_normal(name):
     assert min(fr) >= 0.95
 
 
+@pytest.mark.parametrize("T", [64, 1000])
+def test_fused_equals_composition_with_wide_head_ranges(T):
+    """Up to 1,024 tokens the fused epilogue runs msa_produce's operations in msa_produce's order, so
+    fused == msa_project + msa_produce bit for bit even where a head's binary64 sum of squares is
+    inexact: here the weight rows of every head's first two features are scaled by 2^12 and 2^-12,
+    so each head's values span about 2^24 and their squares about 2^48."""
+    wl = W.decode_batch64() if T == 64 else W.ragged(T, seed=61, pad_frac=0.1)
+    h, w = W.with_projection(wl, seed=6)
+    wf = H.bf16_bits_to_f32(w).copy()
+    wf[0::128] *= np.float32(2.0 ** 12)
+    wf[1::128] *= np.float32(2.0 ** -12)
+    w = W.to_bf16_bits(wf)
+    say(f"[gpu] msa_project_produce vs composition, wide head ranges: T={wl.T}")
+    d = fused(wl, h, w)
+    d2 = W.to_device(wl)
+    x = torch.empty((wl.T, wl.W), dtype=torch.int16, device="cuda")
+    msa.msa_project(dev16(h), dev16(w), x, workspace=workspace(wl.T, h.shape[1], wl.W // 128))
+    msa.msa_produce(x, d2.positions, d2.seq_idx, d2.page_table, *d2.weights, d2.q_out, d2.iq_out, d2.caches[0],
+                    d2.caches[1], d2.caches[2], k_scale=d2.scales[0], v_scale=d2.scales[1], ik_scale=d2.scales[2],
+                    num_pages=wl.num_pages, rms_eps=wl.eps, rope_theta=wl.theta)
+    torch.cuda.synchronize()
+    xs = H.bf16_bits_to_f32(x.cpu().numpy().view(np.uint16)).reshape(wl.T, -1, 128)
+    mags = np.abs(xs[np.isfinite(xs) & (xs != 0)])
+    assert mags.max() / mags.min() > 2.0 ** 20          # the inputs really span a wide range
+    assert torch.equal(d.q_out, d2.q_out) and torch.equal(d.iq_out, d2.iq_out)
+    for a, b in zip(d.storages, d2.storages):
+        assert (a is None and b is None) or torch.equal(a, b)
+
+
 def test_project_produce_prefill_65536_sampled():
     """The 65,536-token prefill chunk in the launch configuration the bench times (one tiled launch;
     h ~ N(0, 1), w ~ N(0, 1/hidden)): on the device the fused outputs equal msa_project followed by
