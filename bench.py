@@ -234,6 +234,26 @@ def bench_decode_unfused(msa, torch, wls, devs, steps, warmup):
                 steps=steps, warmup=warmup)
 
 
+def copy_reference(torch, nbytes: int, reps: int = 20):
+    """The runtime's device-to-device copy moving the same number of bytes as one prefill launch
+    (half read, half written), timed like the prefill: context for the producer's bandwidth."""
+    n = nbytes // 2 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000 / reps
+    del src, dst
+    return dict(bytes=2 * n * 4, us=us, gbs=2 * n * 4 / (us * 1e-6) / 1e9)
+
+
 def stage_prefill(W, torch):
     log("[bench] staging the 65,536-token prefill chunk (two input sets)")
     sets = [W.prefill_65536(variant=v) for v in range(2)]
@@ -339,7 +359,7 @@ def bench_indexer(msa, W, torch, np, reps):
                 us_per_call=us, algorithmic_bytes_per_call=b,
                 roofline=dict(bound="hbm", achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=gbs / HBM_PEAK_GBS,
                               traffic=counter_traffic("decode_64_indexer_call", INDEX_COUNTERS, INDEX_SRCS),
-                              kernel="index_scores_kernel<2> + index_topk_kernel"))
+                              kernel="index_scores_rs_kernel<2, false> + index_topk_rank_kernel"))
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
@@ -590,6 +610,7 @@ def main():
     pre = bench_prefill(msa, W, torch, args.steps, args.warmup, args.warm_ms, stage_prefill(W, torch),
                         0 if args.no_unfused else 50)
     torch.cuda.empty_cache()
+    cref = copy_reference(torch, pre["bytes"])
     dec = bench_decode(msa, W, torch, args.layers, args.decode_steps, args.decode_warmup)
     us_step = dec["ms_per_step"] * 1000
     us_call = us_step / args.layers
@@ -643,6 +664,8 @@ def main():
             "frac": pre["gbs"] / HBM_PEAK_GBS, "traffic": counter_traffic("prefill_65536"),
             "kernel": "produce_kernel<3, 16, 2, 2, 1> (prefill)", "avg_launch_us": pre["us_per_call"],
             "warm_launches": pre["warm_launches"], "warm_ms": pre["warm_ms"],
+            "reference_copy": {"what": "torch device-to-device copy moving the same bytes (half read, half written)",
+                               "us": cref["us"], "gbs": cref["gbs"], "frac_of_peak": cref["gbs"] / HBM_PEAK_GBS},
         },
         "decode": {
             "steps": args.decode_steps, "warmup": args.decode_warmup, "layers": args.layers,

@@ -110,6 +110,17 @@ __device__ __forceinline__ void store16(void* p, uint4 v)
     }
 }
 
+// Input row loads: nontemporal for large batches (each row is read once).
+template <bool kStream>
+__device__ __forceinline__ uint4 load16(const void* p)
+{
+    if (kStream) {
+        const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+        return make_uint4(v[0], v[1], v[2], v[3]);
+    }
+    return *reinterpret_cast<const uint4*>(p);
+}
+
 template <bool kStream>
 __device__ __forceinline__ void store8(void* p, uint2 v)
 {
