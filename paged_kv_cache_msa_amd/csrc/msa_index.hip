@@ -43,6 +43,7 @@ constexpr int kParts = 2;                  // waves per (token, block), each sco
 constexpr int kMaxTopK = 64;
 constexpr int kMaxRowBlocks = 4096;
 constexpr int kRankRowBlocks = 512;     // rows of up to this many blocks are ranked in LDS
+constexpr int kRankThreads = 512;       // threads of the ranking work-group
 
 struct ScoreArgs {
     const uint16_t* iq;
@@ -106,20 +107,26 @@ struct KeyRaw {
 };
 
 template <bool kBf16>
-__device__ __forceinline__ KeyRaw<kBf16> load_key(const CacheDev& c, int64_t e)
+__device__ __forceinline__ KeyRaw<kBf16> load_key_at(const uint8_t* p)
 {
     KeyRaw<kBf16> r;
     if (kBf16) {
-        const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(c.data) + e);
+        const uint4* src = reinterpret_cast<const uint4*>(p);
         const uint4 lo = src[0], hi = src[1];
         r.w[0] = lo.x; r.w[1] = lo.y; r.w[2] = lo.z; r.w[3] = lo.w;
         r.w[kBf16 ? 4 : 0] = hi.x; r.w[kBf16 ? 5 : 1] = hi.y; r.w[kBf16 ? 6 : 2] = hi.z; r.w[kBf16 ? 7 : 3] = hi.w;
     } else {
-        const uint2 v0 = reinterpret_cast<const uint2*>(c.data + e)[0];
-        const uint2 v1 = reinterpret_cast<const uint2*>(c.data + e)[1];
+        const uint2 v0 = reinterpret_cast<const uint2*>(p)[0];
+        const uint2 v1 = reinterpret_cast<const uint2*>(p)[1];
         r.w[0] = v0.x; r.w[1] = v0.y; r.w[2] = v1.x; r.w[3] = v1.y;
     }
     return r;
+}
+
+template <bool kBf16>
+__device__ __forceinline__ KeyRaw<kBf16> load_key(const CacheDev& c, int64_t e)
+{
+    return load_key_at<kBf16>(c.data + e * (kBf16 ? 2 : 1));
 }
 
 // Decode to binary64 (e4m3 and bf16 values are exact in binary32, hence in binary64).
@@ -370,11 +377,17 @@ void index_scores_rs_kernel(const ScoreArgs a)
             bt.pg = j < n_batches ? __builtin_amdgcn_readlane(batch_pg, j & (kWave - 1)) : -1;
             const int32_t lp = a.page_shift >= 0 ? pb >> a.page_shift : pb / a.page_size;
             const int32_t off0 = pb - lp * a.page_size;
+            // A wave-uniform batch base plus the lane's 32-bit offset within the batch (the host checks
+            // that a batch spans less than 2 GiB): the loads take the base from scalar registers.
+            constexpr int kEs = kBf16 ? 2 : 1;
             const int64_t base = bt.pg >= 0 ? (int64_t)bt.pg * a.ik.sp + head_off + (int64_t)off0 * st : 0;
+            const uint8_t* sb = a.ik.data + base * kEs;
+            const uint32_t st_b = bt.pg >= 0 ? (uint32_t)st * kEs : 0u;
 #pragma unroll
             for (int i = 0; i < BATCH; ++i) {
-                const int key = (i ^ g_step) * kKeysPerStep + ks;       // within the batch
-                bt.raw[i] = load_key<kBf16>(a.ik, (bt.pg >= 0 ? base + (int64_t)key * st : 0) + sub * kElemsPerLane);
+                const uint32_t key = (uint32_t)((i ^ g_step) * kKeysPerStep + ks);       // within the batch
+                const uint8_t* src = sb + (key * st_b + (uint32_t)(sub * kElemsPerLane * kEs));
+                bt.raw[i] = load_key_at<kBf16>(src);
             }
             return bt;
         };
@@ -473,52 +486,59 @@ __device__ __forceinline__ bool before(double s1, int32_t i1, double s2, int32_t
     return s1 > s2 || (s1 == s2 && i1 < i2);
 }
 
-// Rows of up to kRankRowBlocks blocks: one work-group per row stages the row in LDS, and every
-// thread computes the rank of each of its candidates (how many candidates are ordered before it); a
-// candidate of rank r < top_k is the r-th pick.  No serial rounds.
-__global__ __launch_bounds__(kBlock) void index_topk_rank_kernel(const double* scores, int32_t rows, int32_t nb,
-                                                                 int32_t top_k, int32_t* ids, int32_t* counts)
+// Rows of up to kRankRowBlocks blocks: one 512-thread work-group per row stages the row in LDS
+// (padded with -inf) and computes the rank of every candidate (how many candidates are ordered
+// before it); a candidate of rank r < top_k is the r-th pick, with no serial rounds.  S threads share
+// a candidate (S = 4 up to 128 blocks, 2 up to 256, else 1), each comparing it against every S-th
+// pair of entries, and their counts are summed over the S lanes.
+template <int S>
+__global__ __launch_bounds__(kRankThreads) void index_topk_rank_kernel(const double* scores, int32_t rows, int32_t nb,
+                                                                        int32_t top_k, int32_t* ids, int32_t* counts)
 {
-    __shared__ __attribute__((aligned(16))) double row_lds[kRankRowBlocks];
-    __shared__ int32_t n_lds[kWavesPerBlock];
+    static_assert(S == 1 || S == 2 || S == 4, "1, 2 or 4 threads per candidate");
+    constexpr int kCands = kRankThreads / S;            // candidates per pass
+    __shared__ __attribute__((aligned(16))) double row_lds[kRankRowBlocks + 2 * S];
+    __shared__ int32_t n_lds[kRankThreads / kWave];
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
     const int32_t r = (int32_t)blockIdx.x;
     if (r >= rows) return;   // uniform over the work-group
     const double* row = scores + (int64_t)r * nb;
+    const int32_t npad = (nb + 2 * S - 1) / (2 * S) * (2 * S);   // whole pairs for every thread of a candidate
     int n_local = 0;
-    for (int32_t i0 = 0; i0 < nb; i0 += kBlock) {
+    for (int32_t i0 = 0; i0 < npad; i0 += kRankThreads) {
         const int32_t i = i0 + tid;
         const double v = i < nb ? row[i] : -INFINITY;
         const bool cand = v > -INFINITY;              // -inf and NaN are never picked
-        if (i < nb) row_lds[i] = cand ? v : -INFINITY;
+        if (i < npad) row_lds[i] = cand ? v : -INFINITY;
         n_local += __popcll(__ballot(cand));          // the wave's candidates, counted once per wave
     }
     if (lane == 0) n_lds[wave] = n_local;
     __syncthreads();
     int32_t n = 0;
 #pragma unroll
-    for (int w = 0; w < kWavesPerBlock; ++w) n += n_lds[w];
+    for (int w = 0; w < kRankThreads / kWave; ++w) n += n_lds[w];
     const int32_t picked = n < top_k ? n : top_k;
     int32_t* out = ids + (int64_t)r * top_k;
-    for (int32_t k = picked + tid; k < top_k; k += kBlock) out[k] = -1;
-    for (int32_t i = tid; i < nb; i += kBlock) {
-        const double si = row_lds[i];
-        if (!(si > -INFINITY)) continue;
+    for (int32_t k = picked + tid; k < top_k; k += kRankThreads) out[k] = -1;
+    const int part = tid % S;
+    const int32_t n_pairs = npad / (2 * S);           // pairs per thread
+    const double2* rp = reinterpret_cast<const double2*>(row_lds) + part;
+    for (int32_t c0 = 0; c0 < nb; c0 += kCands) {     // uniform over the work-group
+        const int32_t i = c0 + tid / S;
+        const double si = i < nb ? row_lds[i] : -INFINITY;
         int32_t rank = 0;
-        int32_t j = 0;
-#pragma unroll 4
-        for (; j + 1 < nb; j += 2) {                  // two entries per 16-byte LDS read
-            const double2 sj = *reinterpret_cast<const double2*>(&row_lds[j]);
-            rank += (sj.x > si || (sj.x == si && j < i)) ? 1 : 0;   // -inf entries never count
+#pragma unroll 8
+        for (int32_t m = 0; m < n_pairs; ++m) {       // -inf entries never count
+            const double2 sj = rp[S * m];
+            const int32_t j = 2 * (S * m + part);
+            rank += (sj.x > si || (sj.x == si && j < i)) ? 1 : 0;
             rank += (sj.y > si || (sj.y == si && j + 1 < i)) ? 1 : 0;
         }
-        if (j < nb) {
-            const double sj = row_lds[j];
-            rank += (sj > si || (sj == si && j < i)) ? 1 : 0;
-        }
-        if (rank < top_k) out[rank] = i;
+        if (S >= 2) rank += __shfl_xor(rank, 1);
+        if (S >= 4) rank += __shfl_xor(rank, 2);
+        if (part == 0 && si > -INFINITY && rank < top_k) out[rank] = i;
     }
     if (counts && tid == 0) counts[r] = picked;
 }
@@ -568,9 +588,11 @@ msa_status launch_topk(const double* block_scores, int32_t rows, int32_t max_blo
     const bool rank = max_blocks <= kRankRowBlocks;
     const dim3 grid(rank ? (unsigned)rows : (unsigned)(((int64_t)rows + kWavesPerBlock - 1) / kWavesPerBlock));
     void* args[] = {const_cast<double**>(&block_scores), &rows, &max_blocks, &top_k, &block_ids, &counts};
-    const void* fn = rank ? reinterpret_cast<const void*>(&index_topk_rank_kernel)
-                          : reinterpret_cast<const void*>(&index_topk_kernel);
-    const hipError_t e = hipLaunchKernel(fn, grid, dim3(kBlock), args, 0, stream);
+    const void* fn = !rank ? reinterpret_cast<const void*>(&index_topk_kernel)
+                     : max_blocks <= kRankThreads / 4 ? reinterpret_cast<const void*>(&index_topk_rank_kernel<4>)
+                     : max_blocks <= kRankThreads / 2 ? reinterpret_cast<const void*>(&index_topk_rank_kernel<2>)
+                                                      : reinterpret_cast<const void*>(&index_topk_rank_kernel<1>);
+    const hipError_t e = hipLaunchKernel(fn, grid, dim3(rank ? kRankThreads : kBlock), args, 0, stream);
     return e == hipSuccess ? MSA_OK : MSA_ERR_LAUNCH;
 }
 
@@ -628,7 +650,8 @@ msa_status index_scores(const uint16_t* iq, int32_t num_tokens, int32_t head_dim
     a.ik = ik;
     a.out = block_scores;
     // Batches of 32 / 64 positions never cross a page, and the parts start on batch boundaries.
-    const bool batch_in_page = page_size % 64 == 0 && block_tokens % 64 == 0 && block_tokens <= 64 * 32;
+    const bool batch_in_page = page_size % 64 == 0 && block_tokens % 64 == 0 && block_tokens <= 64 * 32 &&
+                               (int64_t)64 * ik.st * (ik.is_bf16 ? 2 : 1) + 256 <= 0x7fffffffLL;
     const bool in_page = page_size % kKeysPerStep == 0 && block_tokens % kKeysPerStep == 0;
     const int items_per_group = batch_in_page ? kWavesPerBlock : kWavesPerBlock / kParts;
     const dim3 grid((unsigned)((items + items_per_group - 1) / items_per_group));

@@ -196,10 +196,11 @@ def test_index_special_values(dtype):
     compare(f"special values ({'fp8' if dtype == W.FP8_E4M3 else 'bf16'})", got, ref)
 
 
-@pytest.mark.parametrize("nb", [100, 512, 513, 4096])
+@pytest.mark.parametrize("nb", [7, 72, 100, 128, 129, 255, 256, 257, 511, 512, 513, 4096])
 def test_topk_rows_with_ties_and_gaps(nb):
-    """Rows with repeated scores, -inf gaps and NaN entries; row lengths on both sides of the switch
-    between the rank-based (<= 512 blocks) and the round-based selection."""
+    """Rows with repeated scores, -inf gaps and NaN entries; row lengths on both sides of each switch:
+    4, 2 and 1 threads per candidate in the rank-based selection (<= 128, <= 256, <= 512 blocks; odd
+    lengths pad the last pairs) and the round-based selection beyond."""
     rng = np.random.default_rng(8 + nb)
     rows = 64
     bs = rng.integers(-20, 20, (rows, nb)).astype(np.float64)      # many exact ties
