@@ -399,7 +399,7 @@ def bench_projection(msa, W, torch, np, layers, steps, warmup):
     sin = torch.empty_like(cos)
     msa.msa_rope_table(d.positions, cos, sin, wl.theta)
     msa.msa_slots(d.positions, d.seq_idx, d.page_table, d.slots, page_size=wl.page_size, num_pages=wl.num_pages)
-    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(256, dtype=torch.uint8, device="cuda")   # prefill: the tiled kernel uses none
 
     def produce():
         call(msa, wl, d)
@@ -441,7 +441,7 @@ def bench_projection(msa, W, torch, np, layers, steps, warmup):
     Tt = wl0.T
     cos = torch.empty((Tt, 64), dtype=torch.float32, device="cuda")
     sin = torch.empty_like(cos)
-    ws = torch.empty(msa.msa_project_workspace_size(Tt, K, wl0.W // 128), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(msa.msa_project_workspace_size(Tt, K, wl0.W // 128), dtype=torch.uint8, device="cuda")
     xs = torch.empty((Tt, wl0.W), dtype=torch.int16, device="cuda")
 
     def step_fused():

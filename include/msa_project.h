@@ -24,10 +24,11 @@
  * touches memory.  The pages stop at a single wider GEMM feeding a separate fused producer; this
  * entry point goes one step further.
  *
- * Kernels: for up to 1,024 tokens (the decode and verify batches) two launches, a split-K kernel
- * (heads x 64-token chunks x K slices, partial sums in the workspace, on v_mfma_f32_32x32x16_bf16)
- * and a kernel that adds the slices in a fixed order and runs the epilogue in msa_produce's row
- * layout; for larger batches (prefill) one 256 x 256 tiled kernel on the same matrix instruction.
+ * Kernels: for up to 1,024 tokens (the decode and verify batches) one split-K launch (heads x
+ * 64-token chunks x K slices, on v_mfma_f32_32x32x16_bf16): the slices of a head and chunk leave
+ * their partial sums in the workspace, and the slice that finishes last adds them in a fixed order
+ * and runs the epilogue in msa_produce's row layout, 8 tokens per wave; for larger batches (prefill)
+ * one 256 x 256 tiled kernel on the same matrix instruction.
  *
  * Conventions are those of msa_produce.h (operands checked for residency on eager calls, no allocation,
  * no synchronisation, all checks on the host before any launch, MSA_OK means enqueued,
@@ -47,9 +48,23 @@ extern "C" {
 /*
  * msa_project_workspace_size — bytes of workspace (device memory, 256-byte aligned) a projection of
  * num_tokens rows of width hidden onto num_heads heads of 128 columns needs (both entry points
- * take the same): the split-K partial sums.  Zero for batches above 1,024 tokens.  Its contents on
- * entry do not matter; calls that share a workspace must not overlap in time (same stream, or
- * ordered).
+ * take the same).  Zero for batches above 1,024 tokens (one tiled kernel, no workspace).  Up to
+ * 1,024 tokens the projection is one split-K launch whose work-groups meet in the workspace: it
+ * starts with C = 128 * (1 + num_heads * ceil(num_tokens / 64)) bytes of uint32 control words,
+ * rounded up to a multiple of 256 (word 1: an error word; word 32 * (1 + head * ceil(T / 64) +
+ * chunk), one per 128-byte line: that head and 64-token chunk's arrival counter), followed by the
+ * partial sums.  At rest every control word is 0.
+ *
+ * The workspace must be zero-filled before its first use; every call that completes leaves the
+ * control words at rest, so no call needs it cleared again, whatever its sizes.  Calls that share a
+ * workspace must not overlap in time (same stream, or ordered).  If an arrival counter is not at
+ * rest when a call starts (a workspace never zeroed, or overwritten), the call sets a nonzero error
+ * word and leaves that head and chunk's outputs unwritten; zero the workspace again before reusing
+ * it.  Nothing in the launch waits for another work-group, so no state of the workspace can make a
+ * call hang.
+ *
+ * SHAPE when hidden is not a positive multiple of 64, num_heads is outside [1, 4096], or (1 to
+ * 1,024 tokens) hidden exceeds 24,192 = 63 x 384 (at most 63 K slices per head and chunk).
  */
 msa_status msa_project_workspace_size(int32_t num_tokens, int32_t hidden, int32_t num_heads, uint64_t* bytes);
 
@@ -111,10 +126,11 @@ msa_status msa_project_produce(const uint16_t* h, int64_t h_row_stride, int32_t 
  * looks up that device's copy of the array (a runtime query that allocates nothing); if the runtime
  * refuses such queries during graph capture, make one eager call first.
  *
- * Every call on one GPU shares that GPU's array, and the array keeps the last call's partial sums
- * (each call overwrites everything it reads, so nothing needs clearing).  Calls that overlap in time
- * on one GPU (different streams without ordering between them, or several host threads) race on it
- * and give wrong results; calls on one stream, or otherwise ordered, are safe.
+ * Every call on one GPU shares that GPU's array.  It starts zeroed, as a workspace must, and each
+ * completed call leaves its control words at rest and its partial sums behind (each call overwrites
+ * every partial sum it reads, so nothing needs clearing).  Calls that overlap in time on one GPU
+ * (different streams without ordering between them, or several host threads) race on it and give
+ * wrong results or leave it unusable; calls on one stream, or otherwise ordered, are safe.
  *
  * Arguments, results and the other errors: as msa_project_produce, minus workspace and
  * workspace_bytes.

@@ -48,6 +48,7 @@ using namespace msa_internal;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kSplitMaxTokens = 1024;
 constexpr int kChunk = 64;                 // tokens per split-K work-group (two MFMA token blocks)
@@ -61,6 +62,40 @@ constexpr int kSplitLds = (128 + kChunk) * kSliceMax * 2;
 enum Stream { kQ = 0, kK = 1, kV = 2, kIQ = 3, kIK = 4 };
 
 __device__ __forceinline__ f32x16_t mfma(const uint4& a, const uint4& b, const f32x16_t& c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                    c, 0, 0, 0);
+}
+
+// One 16-byte LDS read, issued as written: the compiler neither reorders it nor makes it wait for
+// the direct global -> LDS loads in flight (it cannot see which LDS bytes an inline read touches).
+// Completion is awaited explicitly with lgkm_wait below.
+__device__ __forceinline__ u32x4_t lds_read16(uint32_t addr)
+{
+    u32x4_t v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+    return v;
+}
+
+// Waits until at most N LDS reads are in flight; the fragments passed are tied to the wait so that
+// no use of them is scheduled above it.
+template <int N>
+__device__ __forceinline__ void lgkm_wait(u32x4_t (&a)[4], u32x4_t (&b)[2])
+{
+    asm volatile("s_waitcnt lgkmcnt(%6)"
+                 : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1])
+                 : "n"(N));
+}
+
+template <int N>
+__device__ __forceinline__ void lgkm_wait(u32x4_t (&a)[4], u32x4_t (&b)[4])
+{
+    asm volatile("s_waitcnt lgkmcnt(%8)"
+                 : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3])
+                 : "n"(N));
+}
+
+__device__ __forceinline__ f32x16_t mfma4(const u32x4_t& a, const u32x4_t& b, const f32x16_t& c)
 {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
                                                     c, 0, 0, 0);
@@ -257,13 +292,27 @@ __device__ __forceinline__ void row_store_staged(const RowOut& o, const float (&
 
 // ------------------------------------------------------------------ split-K kernel (<= 1,024 tokens)
 
+// Workspace of the split-K kernel: a 256-byte header (word 1: error bits), then the partial sums.
+// A partial sum is stored as the bitwise complement of its binary32 bits, so that a zero word means
+// "not written yet": no sum these kernels compute has all 32 bits set (a NaN comes either from the
+// bf16 inputs, whose low 16 bits are zero, or is the default NaN).  Every word is consumed once per
+// launch and zeroed again by the work-group that read it, so a launch that completes leaves the
+// workspace all zero, as it must be before its first use.
+constexpr int kHeaderBytes = 256;
+constexpr int kMaxSplits = 63;
+constexpr int kCoherent = 16;             // buffer cache policy sc1: agent-scope coherent load / store
+constexpr int kPollLimit = 1 << 16;       // polls of a partial-sum fragment before a wave gives up
+constexpr int kPollPolicy = (int)(16u | 0x80000000u);   // sc1 and the compiler's volatile bit
+constexpr uint32_t kErrWait = 1u;
+
 struct SplitArgs {
     const uint16_t* h;
     int64_t h_stride;
     const uint16_t* w;
     int64_t w_stride;
-    float* part;               // [head][chunk][slice] x kPartFloats
-    int32_t K, kc, splits, n_tc;
+    uint32_t* err;             // error bits
+    uint32_t* part;            // [pair][slice] x kPartFloats complemented binary32, pair = head * n_tc + chunk
+    int32_t K, base, extra, splits, n_tc;      // slice s: base + (s < extra) planes of 64 columns
     Epi e;
 };
 
@@ -279,164 +328,84 @@ __device__ __forceinline__ int plane_slot(int rows, int plane, int row, int chun
 
 // Moves plane g (64 columns) of rows [0, rows) of a K slice (row r at src_row(r)) into LDS at `dst`
 // with the direct global -> LDS path: each lane of each wave fills one 16-byte slot per instruction
-// (64 consecutive slots per wave).  rows is 64 or 128: rows / 32 instructions per wave.
+// (64 consecutive slots per wave).  rows is 64 or 128: rows / 64 instructions per wave (8 waves).
 template <typename RowPtr>
 __device__ __forceinline__ void plane_to_lds(uint8_t* dst, int rows, int g, RowPtr src_row)
 {
     const int tid = threadIdx.x, wave = tid >> 6;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        if (j * 256 >= rows * 8) break;
-        const int p = j * 256 + tid;                               // slot within the plane
+    for (int j = 0; j < 2; ++j) {
+        if (j * 512 >= rows * 8) break;
+        const int p = j * 512 + tid;                               // slot within the plane
         const int row = p >> 3;
         const int chunk = (p & 7) ^ (row & 7);                     // logical chunk stored at this slot
         const uint16_t* gsrc = src_row(row) + g * 64 + chunk * 8;
-        uint8_t* l = dst + ((size_t)(g * rows * 8 + j * 256 + wave * 64)) * 16;
+        uint8_t* l = dst + ((size_t)(g * rows * 8 + j * 512 + wave * 64)) * 16;
         __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)l, 16, 0, 0);
     }
 }
 
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void project_split_kernel(const SplitArgs a)
+// The epilogue of one token's head row in the producer's row layout: lane (ts = lane / 8, sub =
+// lane % 8) of a wave holds features [8 sub, 8 sub + 8) and [64 + 8 sub, 64 + 8 sub + 8) of token
+// 8 g + ts, so both rotate-half partners sit in one lane and a head's sum of squares is an 8-lane
+// reduction, as in msa_produce (the same operations in the same order: the fused outputs equal
+// msa_produce applied to msa_project's row, bit for bit).  RowIn holds what the epilogue reads
+// besides the sums (norm weights, RoPE coefficients, slot, fp8 scale), fetched ahead.
+struct RowIn {
+    uint4 wa, wb;
+    float4 c4[2], s4[2];
+    int64_t slot;              // as loaded; meaningful where use_slot
+    float scale;               // as loaded; meaningful where use_scale
+    bool use_slot, use_scale;
+};
+
+// One binary32 read through the vector memory path (a raw buffer load), so that it is counted with
+// the wave's other vector loads and no scalar-load wait stands between it and them.
+__device__ __forceinline__ float vload_f32(const float* p)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kSplitLds];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);       // 32-feature block of the head
-    const int hh = lane >> 5;
-    const int split = (int)(blockIdx.x % (uint32_t)a.splits);
-    const int pair = (int)(blockIdx.x / (uint32_t)a.splits);         // head * n_tc + chunk
-    const int tc = pair % a.n_tc;
-    const int head = pair / a.n_tc;
-    const int k_begin = split * a.kc;
-    const int planes = (min(a.K, k_begin + a.kc) - k_begin) / kBK;
-
-    // The whole slice of w (128 rows) and h (64 rows) in flight at once.
-    uint8_t* lds_a = smem;
-    uint8_t* lds_b = smem + (size_t)128 * planes * 8 * 16;
-    const uint16_t* wrow = a.w + (int64_t)head * kHeadDim * a.w_stride + k_begin;
-    const int64_t ws = a.w_stride, hs = a.h_stride;
-    const uint16_t* hrow = a.h + k_begin;
-    const int t_first = tc * kChunk, t_last = a.e.T - 1;
-    for (int g = 0; g < planes; ++g) {
-        plane_to_lds(lds_a, 128, g, [&](int r) { return wrow + r * ws; });
-        plane_to_lds(lds_b, kChunk, g, [&](int r) { return hrow + (int64_t)min(t_first + r, t_last) * hs; });
-    }
-    __builtin_amdgcn_s_waitcnt(0x3f70);                              // vmcnt(0): this wave's slots landed
-    __syncthreads();
-
-    // Four independent accumulation chains (two token blocks x even / odd 16-column steps).
-    f32x16_t c0 = {}, c1 = {}, d0 = {}, d1 = {};
-    const int ra = wave * 32 + (lane & 31), rb0 = lane & 31, rb1 = 32 + (lane & 31);
-    for (int g = 0; g < planes; ++g) {
-        uint4 av[4], b0[4], b1[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int c = 2 * q + hh;
-            av[q] = *reinterpret_cast<const uint4*>(lds_a + plane_slot(128, g, ra, c) * 16);
-            b0[q] = *reinterpret_cast<const uint4*>(lds_b + plane_slot(kChunk, g, rb0, c) * 16);
-            b1[q] = *reinterpret_cast<const uint4*>(lds_b + plane_slot(kChunk, g, rb1, c) * 16);
-        }
-        c0 = mfma(av[0], b0[0], c0);
-        c1 = mfma(av[0], b1[0], c1);
-        d0 = mfma(av[1], b0[1], d0);
-        d1 = mfma(av[1], b1[1], d1);
-        c0 = mfma(av[2], b0[2], c0);
-        c1 = mfma(av[2], b1[2], c1);
-        d0 = mfma(av[3], b0[3], d0);
-        d1 = mfma(av[3], b1[3], d1);
-    }
-    c0 += d0;
-    c1 += d1;
-
-    // Partial sums of this slice: [pair][slice][wave][tb][q][lane] x 4 floats.  The reduction runs
-    // in the next kernel, after the kernel boundary has made these stores visible device-wide.
-    f32x4_t* pp = reinterpret_cast<f32x4_t*>(a.part + ((int64_t)pair * a.splits + split) * kPartFloats) +
-                  (wave * 2 * 4) * 64 + lane;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        pp[q * 64] = f32x4_t{c0[4 * q], c0[4 * q + 1], c0[4 * q + 2], c0[4 * q + 3]};
-        pp[(4 + q) * 64] = f32x4_t{c1[4 * q], c1[4 * q + 1], c1[4 * q + 2], c1[4 * q + 3]};
-    }
+    // 0x00020000: the gfx9-family word 3 of a raw (untyped, dword) buffer resource.
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p), 0, 4, 0x00020000);
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, 0, 0, 0));
 }
 
-// One wave per (head, 8 tokens), in the producer's row layout: lane (ts = lane / 8, sub = lane % 8)
-// holds features [8 sub, 8 sub + 8) and [64 + 8 sub, 64 + 8 sub + 8) of token 8 g + ts's head row, so
-// both rotate-half partners sit in one lane and a head's sum of squares is an 8-lane reduction, as
-// in msa_produce (the same operations in the same order: the fused outputs equal msa_produce
-// applied to msa_project's row, bit for bit).  Each lane adds the slices' partial sums of its 16
-// features in slice order (the order of the other reduce kernel), reading them straight from the
-// split kernel's fragment layout: within a 32-feature block, lane l of a fragment holds token l % 32
-// and features 8 q + 4 (l / 32) + [0, 4) at index [q][l].  Many small work-groups spread the
-// partial sums' reads over the whole chip.
+// Every load is unconditional: a stream without norm weights, a padded token and a cache without
+// scale read valid stand-ins (the RoPE table, the last token's slot) whose values are then
+// discarded, so no load has to complete at a branch join before the slice's loads are issued.
 template <bool kProduce>
-__global__ __launch_bounds__(64) void project_reduce_rows_kernel(const SplitArgs a)
+__device__ __forceinline__ RowIn row_inputs(const Epi& e, int head, int32_t t, int sub)
 {
-    const Epi& e = a.e;
-    const int lane = threadIdx.x;
-    const int ts = lane / 8, sub = lane % 8;
-    const int n_tg = (e.T + 7) / 8;
-    const int head = (int)(blockIdx.x / (uint32_t)n_tg);
-    const int g = (int)(blockIdx.x - (uint32_t)head * (uint32_t)n_tg);
-    const int32_t t = g * 8 + ts;
+    RowIn in;
+    in.wa = in.wb = make_uint4(0, 0, 0, 0);
+    in.slot = -1;
+    in.scale = 1.0f;
+    in.use_slot = in.use_scale = false;
+    if (!kProduce) return in;
     const bool tok = t < e.T;
-    const int32_t tc = t / kChunk, t64 = t % kChunk, tb = t64 / 32, t32 = t64 % 32;
-    const int pair = head * a.n_tc + tc;
+    const int32_t tl = tok ? t : e.T - 1;
+    const int st = stream_of(e, head);
+    const uint16_t* w = st == kV ? reinterpret_cast<const uint16_t*>(e.cos)
+                                 : e.w[st == kQ ? 0 : st == kK ? 1 : st == kIQ ? 2 : 3];
+    in.wa = *reinterpret_cast<const uint4*>(w + sub * 8);
+    in.wb = *reinterpret_cast<const uint4*>(w + kHalf + sub * 8);
+    const float4* cp = reinterpret_cast<const float4*>(e.cos + (int64_t)tl * kHalf + sub * 8);
+    const float4* sp = reinterpret_cast<const float4*>(e.sin + (int64_t)tl * kHalf + sub * 8);
+    in.c4[0] = cp[0]; in.c4[1] = cp[1];
+    in.s4[0] = sp[0]; in.s4[1] = sp[1];
+    const bool cache_row = st == kK || st == kV || st == kIK;
+    in.slot = e.slots[tl];
+    in.use_slot = cache_row && tok;
+    const CacheDev& cd = e.cache[st == kK ? 0 : st == kV ? 1 : 2];
+    in.use_scale = cache_row && !cd.is_bf16;
+    in.scale = vload_f32(in.use_scale ? cd.scale : e.cos);
+    return in;
+}
 
-    // Epilogue inputs first (their addresses need no partial sum).
-    const int st = kProduce ? stream_of(e, head) : 0;
-    uint4 wa = make_uint4(0, 0, 0, 0), wb = make_uint4(0, 0, 0, 0);
-    float4 c4[1][2], s4[1][2];
-    int64_t slot = -1;
-    float scale = 1.0f;
-    if (kProduce) {
-        if (st != kV) {
-            const uint16_t* w = e.w[st == kQ ? 0 : st == kK ? 1 : st == kIQ ? 2 : 3];
-            wa = *reinterpret_cast<const uint4*>(w + sub * 8);
-            wb = *reinterpret_cast<const uint4*>(w + kHalf + sub * 8);
-        }
-        const int32_t tl = tok ? t : e.T - 1;
-        const float4* cp = reinterpret_cast<const float4*>(e.cos + (int64_t)tl * kHalf + sub * 8);
-        const float4* sp = reinterpret_cast<const float4*>(e.sin + (int64_t)tl * kHalf + sub * 8);
-        c4[0][0] = cp[0]; c4[0][1] = cp[1];
-        s4[0][0] = sp[0]; s4[0][1] = sp[1];
-        const bool cache_row = st == kK || st == kV || st == kIK;
-        if (cache_row && tok) slot = e.slots[t];
-        const CacheDev& cd = e.cache[st == kK ? 0 : st == kV ? 1 : 2];
-        if (cache_row && !cd.is_bf16) scale = *cd.scale;
-    }
-
-    // The 16 features' sums over the K slices, in slice order.
-    float v[16];
-    {
-        const f32x4_t* base = reinterpret_cast<const f32x4_t*>(a.part + (int64_t)pair * a.splits * kPartFloats);
-        // fragment index of (32-feature block w, token block tb, q, lane) in 16-byte units
-        auto at = [&](int w, int hh) { return ((w * 2 + tb) * 4 + (sub % 4)) * 64 + t32 + 32 * hh; };
-        const int i00 = at(sub / 4, 0), i01 = at(sub / 4, 1), i10 = at(2 + sub / 4, 0), i11 = at(2 + sub / 4, 1);
-        // Eight slices' loads in flight at once (past the last slice: the last one again, unused).
-        for (int s0 = 0; s0 < a.splits; s0 += 8) {
-            f32x4_t x[8][4];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const f32x4_t* p = base + (int64_t)min(s0 + u, a.splits - 1) * (kPartFloats / 4);
-                x[u][0] = p[i00];
-                x[u][1] = p[i01];
-                x[u][2] = p[i10];
-                x[u][3] = p[i11];
-            }
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const bool live = s0 + u < a.splits, first = s0 + u == 0;
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float sum = first ? x[u][c][j] : v[4 * c + j] + x[u][c][j];
-                        v[4 * c + j] = live ? sum : v[4 * c + j];
-                    }
-            }
-        }
-    }
+// v: the lane's 16 features' sums (binary32) of token t.
+template <bool kProduce>
+__device__ __forceinline__ void row_epilogue(const Epi& e, int head, int32_t t, int sub, const RowIn& in,
+                                             const float (&v)[16])
+{
+    const bool tok = t < e.T;
     // The packed row's values: the sums rounded to bf16.
     uint4 ra = make_uint4(bf16x2(v[0], v[1]), bf16x2(v[2], v[3]), bf16x2(v[4], v[5]), bf16x2(v[6], v[7]));
     uint4 rb = make_uint4(bf16x2(v[8], v[9]), bf16x2(v[10], v[11]), bf16x2(v[12], v[13]), bf16x2(v[14], v[15]));
@@ -448,6 +417,7 @@ __global__ __launch_bounds__(64) void project_reduce_rows_kernel(const SplitArgs
         }
         return;
     }
+    const int st = stream_of(e, head);
     float x[16];
     unpack8(ra, x);
     unpack8(rb, x + 8);
@@ -461,10 +431,10 @@ __global__ __launch_bounds__(64) void project_reduce_rows_kernel(const SplitArgs
         for (int j = 0; j < 16; ++j) acc = __builtin_fma((double)x[j], (double)x[j], acc);
         const float r = rms_from_ss(head_sum8(acc), e.eps);
         float wv[16];
-        unpack8(wa, wv);
-        unpack8(wb, wv + 8);
-        const float cf[8] = {c4[0][0].x, c4[0][0].y, c4[0][0].z, c4[0][0].w, c4[0][1].x, c4[0][1].y, c4[0][1].z, c4[0][1].w};
-        const float sf[8] = {s4[0][0].x, s4[0][0].y, s4[0][0].z, s4[0][0].w, s4[0][1].x, s4[0][1].y, s4[0][1].z, s4[0][1].w};
+        unpack8(in.wa, wv);
+        unpack8(in.wb, wv + 8);
+        const float cf[8] = {in.c4[0].x, in.c4[0].y, in.c4[0].z, in.c4[0].w, in.c4[1].x, in.c4[1].y, in.c4[1].z, in.c4[1].w};
+        const float sf[8] = {in.s4[0].x, in.s4[0].y, in.s4[0].z, in.s4[0].w, in.s4[1].x, in.s4[1].y, in.s4[1].z, in.s4[1].w};
         float y[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) y[j] = (x[j] * r) * wv[j];
@@ -483,6 +453,7 @@ __global__ __launch_bounds__(64) void project_reduce_rows_kernel(const SplitArgs
         *reinterpret_cast<uint4*>(dst + kHalf) = bf16x8(o + 8);
         return;
     }
+    const int64_t slot = in.use_slot ? in.slot : -1;
     if (slot < 0) return;
     const int64_t page = slot / e.page_size;
     if (page >= e.num_pages) return;
@@ -496,10 +467,191 @@ __global__ __launch_bounds__(64) void project_reduce_rows_kernel(const SplitArgs
         *reinterpret_cast<uint4*>(dst + kHalf) = bf16x8(o + 8);
     } else {
         uint2 lo, hi;
-        e4m3x16(o, inv_scale(scale), lo, hi);
+        e4m3x16(o, inv_scale(in.use_scale ? in.scale : 1.0f), lo, hi);
         uint8_t* dst = cd.data + elem;
         *reinterpret_cast<uint2*>(dst) = lo;
         *reinterpret_cast<uint2*>(dst + kHalf) = hi;
+    }
+}
+
+// One launch for up to 1,024 tokens: one work-group of eight waves per (head, 64-token chunk, K
+// slice), block index = (head * n_tc + chunk) * S + slice.
+//   1. The slice of w (128 rows) and h (64 rows) is requested into LDS at once (its memory latency
+//      paid once); wave (b, tb) multiplies the head's 32-feature block b against token block tb of
+//      the chunk with two MFMA chains.
+//   2. The partial sums go to the workspace, complemented, with agent-scope coherent stores
+//      (written through, so a work-group on another XCD reads them without a cache-wide
+//      write-back).  Nothing waits for them here.
+//   3. Token group q (8 tokens) of the chunk is reduced by the work-group of slice q mod S: its wave
+//      j reads slices j, j + 8, ... of that token group, polling each fragment until every word of
+//      it has been written (nonzero), adds them in that order, zeroes the words it read, and hands
+//      its sum to wave 0 through LDS; wave 0 adds the eight waves' sums in wave order and runs the
+//      epilogue (row_epilogue).  The order is fixed, so every call gives the same bits.
+// The polls wait only for the other slices of the same (head, chunk): consecutive block indices,
+// which the hardware starts together (S <= 63 work-groups).  A wave that still finds unwritten words
+// after kPollLimit polls sets an error bit and leaves its token group unwritten, so no state of the
+// workspace can make a launch hang.
+template <bool kProduce>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void project_split_kernel(const SplitArgs a)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kSplitLds];
+    __shared__ uint32_t s_ok;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int fb = wave & 3, tb = wave >> 2;                         // 32-feature block, 32-token block
+    const int hh = lane >> 5;
+    const int split = (int)(blockIdx.x % (uint32_t)a.splits);
+    const int pair = (int)(blockIdx.x / (uint32_t)a.splits);         // head * n_tc + chunk
+    const int tc = pair % a.n_tc;
+    const int head = pair / a.n_tc;
+    const int k_begin = kBK * (split * a.base + min(split, a.extra));
+    const int planes = a.base + (split < a.extra ? 1 : 0);
+
+    // Epilogue inputs of this work-group's first token group, fetched by wave 0 (which runs the
+    // epilogue) before the slice, so that they are not behind it in the wave's in-order load counter.
+    // (Fetched by every wave, the same addresses eight times over, a decode call took 0.5 us longer.)
+    const int t_first = tc * kChunk, t_last = a.e.T - 1;
+    const int ts = lane / 8, sub = lane % 8;
+    RowIn in;
+    if (wave == 0) in = row_inputs<kProduce>(a.e, head, t_first + 8 * split + ts, sub);
+
+    // The whole slice of w (128 rows) and h (64 rows) in flight at once, in plane order: each wave
+    // issues 3 loads per plane (2 of w, 1 of h).
+    uint8_t* lds_a = smem;
+    uint8_t* lds_b = smem + (size_t)128 * planes * 8 * 16;
+    const uint16_t* wrow = a.w + (int64_t)head * kHeadDim * a.w_stride + k_begin;
+    const int64_t ws = a.w_stride, hs = a.h_stride;
+    const uint16_t* hrow = a.h + k_begin;
+    for (int g = 0; g < planes; ++g) {
+        plane_to_lds(lds_a, 128, g, [&](int r) { return wrow + r * ws; });
+        plane_to_lds(lds_b, kChunk, g, [&](int r) { return hrow + (int64_t)min(t_first + r, t_last) * hs; });
+    }
+
+    // Two independent accumulation chains (even / odd 16-column steps), over the planes in two
+    // groups: the first group's products run while the second group's planes are still arriving.
+    f32x16_t c = {}, d = {};
+    const int ra = fb * 32 + (lane & 31), rb = tb * 32 + (lane & 31);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+    const uint32_t lds_b0 = lds0 + (uint32_t)(128 * planes * 8 * 16);
+    auto products = [&](int g0, int g1) {
+        for (int g = g0; g < g1; ++g) {
+            u32x4_t av[4], bv[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int ch = 2 * q + hh;
+                av[q] = lds_read16(lds0 + (uint32_t)plane_slot(128, g, ra, ch) * 16);
+                bv[q] = lds_read16(lds_b0 + (uint32_t)plane_slot(kChunk, g, rb, ch) * 16);
+            }
+            lgkm_wait<0>(av, bv);
+            c = mfma4(av[0], bv[0], c);
+            d = mfma4(av[1], bv[1], d);
+            c = mfma4(av[2], bv[2], c);
+            d = mfma4(av[3], bv[3], d);
+        }
+    };
+    const int first = planes - planes / 2;                          // planes of the first group
+    // vmcnt(3 x the second group's planes): this wave's loads of the first group have landed (its
+    // loads retire in issue order; anything issued later only makes the wait longer).
+    switch (planes / 2) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x3f70); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0x3f73); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x3f76); break;
+    default: __builtin_amdgcn_s_waitcnt(0x3f79); break;
+    }
+    // Bare barriers: __syncthreads' fence would wait for every direct-to-LDS load still in flight.
+    // The waits above order this wave's loads; after the barrier every wave's are in LDS.
+    __builtin_amdgcn_s_barrier();
+    products(0, first);
+    __builtin_amdgcn_s_waitcnt(0x3f70);                              // vmcnt(0): every slot landed
+    __builtin_amdgcn_s_barrier();
+    products(first, planes);
+    c += d;
+
+    // Partial sums of this slice, complemented: [pair][slice][b][tb][q][lane] x 4 words.
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        a.part + (int64_t)pair * a.splits * kPartFloats, (short)0, a.splits * kPartFloats * (int)sizeof(float),
+        0x00020000);
+    constexpr int kSliceBytes = kPartFloats * 4;
+    const int wbase = split * kSliceBytes + (((fb * 2 + tb) * 4) * 64 + lane) * 16;   // q = 0
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const f32x4_t enc = __builtin_bit_cast(
+            f32x4_t, ~__builtin_bit_cast(u32x4_t, f32x4_t{c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]}));
+        __builtin_amdgcn_raw_buffer_store_b128(enc, rs, wbase + q * 1024, 0, kCoherent);
+    }
+
+    // Reduction of token groups q = split, split + S, ... (one per work-group when S >= 8).
+    f32x4_t* red = reinterpret_cast<f32x4_t*>(smem);                // [wave][4][lane] x 4 sums
+    for (int q = split; q < kChunk / 8; q += a.splits) {
+        __syncthreads();                                             // LDS free: products / last group done
+        if (q != split && wave == 0) in = row_inputs<kProduce>(a.e, head, t_first + 8 * q + ts, sub);
+        // Byte offsets (within a slice) of this lane's four fragments: token t64 = 8 q + ts, feature
+        // blocks sub / 4 and 2 + sub / 4, fragment row sub % 4, lane halves 0 and 1.
+        const int t64 = 8 * q + ts, ftb = t64 / 32, t32 = t64 % 32;
+        auto at = [&](int w, int h2) { return ((((w * 2 + ftb) * 4 + (sub % 4)) * 64) + t32 + 32 * h2) * 16; };
+        const int off[4] = {at(sub / 4, 0), at(sub / 4, 1), at(2 + sub / 4, 0), at(2 + sub / 4, 1)};
+        float v[16];
+        bool ok = true;
+        for (int sl = wave; sl < a.splits; sl += 8) {
+            const int sb = sl * kSliceBytes;
+            u32x4_t x[4];
+            for (int polls = 0;; ++polls) {
+                // Volatile loads: the words change under this loop (the compiler keeps every load and
+                // every word's test inside it; volatile makes them system-scope coherent).
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    x[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, sb + off[i], 0, kPollPolicy));
+                int full = 1;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) full &= x[i][j] != 0u ? 1 : 0;
+                if (__all(full)) break;
+                if (polls == kPollLimit) {
+                    ok = false;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+            if (!ok) break;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                // Written through like the partial sums: plain stores would leave these lines dirty
+                // for the kernel's end to write back (1.6 us per decode call, measured).
+                __builtin_amdgcn_raw_buffer_store_b128(f32x4_t{0.f, 0.f, 0.f, 0.f}, rs, sb + off[i], 0, kCoherent);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float y = __builtin_bit_cast(float, ~x[i][j]);
+                    v[4 * i + j] = sl == wave ? y : v[4 * i + j] + y;
+                }
+            }
+        }
+        if (!ok && lane == 0) atomicOr(a.err, kErrWait);
+        if (wave < a.splits) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[(wave * 4 + i) * 64 + lane] = f32x4_t{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+        }
+        if (tid == 0) s_ok = 1;
+        __syncthreads();
+        if (!ok) s_ok = 0;
+        __syncthreads();
+        if (wave == 0 && s_ok) {
+            float sum[16];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const f32x4_t r = red[i * 64 + lane];
+                sum[4 * i] = r[0]; sum[4 * i + 1] = r[1]; sum[4 * i + 2] = r[2]; sum[4 * i + 3] = r[3];
+            }
+            for (int w = 1; w < min(a.splits, 8); ++w)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const f32x4_t r = red[(w * 4 + i) * 64 + lane];
+                    sum[4 * i] += r[0]; sum[4 * i + 1] += r[1]; sum[4 * i + 2] += r[2]; sum[4 * i + 3] += r[3];
+                }
+            row_epilogue<kProduce>(a.e, head, t_first + 8 * q + ts, sub, in, sum);
+        }
     }
 }
 
@@ -522,34 +674,6 @@ __device__ __forceinline__ uint32_t xcd_tile(uint32_t bid, uint32_t total)
     uint32_t prefix = 0;
     for (uint32_t i = 0; i < x; ++i) prefix += (total - i + 7u) >> 3;
     return prefix + (bid >> 3);
-}
-
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
-// One 16-byte LDS read, issued as written: the compiler neither reorders it nor makes it wait for
-// the direct global -> LDS loads in flight into the other buffer (it cannot see which buffer an
-// inline read touches).  Completion is awaited explicitly with lgkm_wait below.
-__device__ __forceinline__ u32x4_t lds_read16(uint32_t addr)
-{
-    u32x4_t v;
-    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
-    return v;
-}
-
-// Waits until at most N LDS reads are in flight; the six fragments passed are tied to the wait so
-// that no use of them is scheduled above it.
-template <int N>
-__device__ __forceinline__ void lgkm_wait(u32x4_t (&a)[4], u32x4_t (&b)[2])
-{
-    asm volatile("s_waitcnt lgkmcnt(%6)"
-                 : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1])
-                 : "n"(N));
-}
-
-__device__ __forceinline__ f32x16_t mfma4(const u32x4_t& a, const u32x4_t& b, const f32x16_t& c)
-{
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
-                                                    c, 0, 0, 0);
 }
 
 template <bool kProduce>
@@ -679,26 +803,35 @@ void project_tile_kernel(const TileArgs a)
 uint64_t round_up(uint64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct SplitPlan {
-    int32_t splits, kc, n_tc;
-    uint64_t bytes;
+    int32_t splits, base, extra, n_tc;
+    uint64_t ctl_bytes, bytes;
 };
 
 // K slices per (head, chunk): as few as the LDS allows (a slice of at most kSliceMax columns of w
-// and h is staged whole), the slice width a multiple of 64.
+// and h is staged whole).  Slices are whole 64-column planes, the first `extra` of them one plane
+// longer.  (More, smaller slices, to occupy more of the 256 compute units, measured slower: the
+// decode batch's 23 heads at 8 slices take 12.2 us per layer, at 11 slices 12.5, at 12 slices, more
+// work-groups than compute units, 17.8.)
 SplitPlan split_plan(int32_t T, int32_t K, int32_t heads)
 {
     SplitPlan p;
     p.n_tc = (T + kChunk - 1) / kChunk;
     const int64_t groups = (int64_t)heads * p.n_tc;
     const int64_t steps = K / kBK;
-    const int64_t want = (K + kSliceMax - 1) / kSliceMax;
-    p.kc = (int32_t)(((steps + want - 1) / want) * kBK);
-    p.splits = (K + p.kc - 1) / p.kc;
-    p.bytes = round_up((uint64_t)groups * p.splits * kPartFloats * sizeof(float));
+    int64_t splits = (K + kSliceMax - 1) / kSliceMax;
+#ifdef PROJECT_FORCE_SPLITS
+    splits = PROJECT_FORCE_SPLITS;
+#endif
+    if (splits > steps) splits = steps;
+    p.splits = (int32_t)splits;
+    p.base = (int32_t)(steps / splits);
+    p.extra = (int32_t)(steps % splits);
+    p.ctl_bytes = kHeaderBytes;
+    p.bytes = p.ctl_bytes + round_up((uint64_t)groups * p.splits * kPartFloats * sizeof(float));
     return p;
 }
 
-// Workspace bytes a projection of T tokens uses (the split-K partial sums; none for the tiled path).
+// Workspace bytes a projection of T tokens uses (none for the tiled path).
 uint64_t workspace_need(int32_t T, int32_t K, int32_t heads)
 {
     return T <= 0 || T > kSplitMaxTokens ? 0 : split_plan(T, K, heads).bytes;
@@ -708,6 +841,7 @@ msa_status check_gemm(const uint16_t* h, int64_t h_row_stride, int32_t T, int32_
                       int64_t w_row_stride, int64_t N)
 {
     if (T < 0 || K <= 0 || K % kBK || N <= 0 || N % kHeadDim || N > (int64_t)4096 * kHeadDim) return MSA_ERR_SHAPE;
+    if (T <= kSplitMaxTokens && K > kMaxSplits * kSliceMax) return MSA_ERR_SHAPE;   // split-K slices per item
     if (h_row_stride < K || h_row_stride % 8 || w_row_stride < K || w_row_stride % 8) return MSA_ERR_STRIDE;
     if (T > 0 && (!h || !w)) return MSA_ERR_NULL_POINTER;
     if (!aligned(h, 16) || !aligned(w, 16)) return MSA_ERR_ALIGNMENT;
@@ -733,19 +867,18 @@ msa_status launch_projection(const uint16_t* h, int64_t h_row_stride, int32_t T,
         a.h_stride = h_row_stride;
         a.w = w;
         a.w_stride = w_row_stride;
-        a.part = static_cast<float*>(workspace);
+        a.err = static_cast<uint32_t*>(workspace) + 1;
+        a.part = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + p.ctl_bytes);
         a.K = K;
-        a.kc = p.kc;
+        a.base = p.base;
+        a.extra = p.extra;
         a.splits = p.splits;
         a.n_tc = p.n_tc;
         a.e = e;
         void* args[] = {&a};
-        const int64_t pairs = (int64_t)heads * p.n_tc;
-        err = hipLaunchKernel(reinterpret_cast<const void*>(&project_split_kernel), dim3((unsigned)(pairs * p.splits)),
-                              dim3(256), args, 0, s);
-        if (err == hipSuccess)
-            err = hipLaunchKernel(reinterpret_cast<const void*>(&project_reduce_rows_kernel<kProduce>),
-                                  dim3((unsigned)((int64_t)heads * ((T + 7) / 8))), dim3(64), args, 0, s);
+        const int64_t items = (int64_t)heads * p.n_tc * p.splits;
+        err = hipLaunchKernel(reinterpret_cast<const void*>(&project_split_kernel<kProduce>), dim3((unsigned)items),
+                              dim3(512), args, 0, s);
     } else {
         TileArgs a;
         a.h = h;
@@ -894,6 +1027,7 @@ msa_status msa_project_workspace_size(int32_t num_tokens, int32_t hidden, int32_
 {
     if (!bytes) return MSA_ERR_NULL_POINTER;
     if (num_tokens < 0 || hidden <= 0 || hidden % kBK || num_heads <= 0 || num_heads > 4096) return MSA_ERR_SHAPE;
+    if (num_tokens > 0 && num_tokens <= kSplitMaxTokens && hidden > kMaxSplits * kSliceMax) return MSA_ERR_SHAPE;
     *bytes = num_tokens == 0 || num_tokens > kSplitMaxTokens ? 0 : split_plan(num_tokens, hidden, num_heads).bytes;
     return MSA_OK;
 }

@@ -274,9 +274,16 @@ def test_project_workspace_size(L):
     n = ctypes.c_uint64(0)
     by = ctypes.byref(n)
     assert L.msa_project_workspace_size(64, 3072, 23, by) == OK
-    # decode batch 64 at hidden 3072: 8 K slices of 384 columns per head, 8,192 binary32 partial sums each
-    assert n.value == 23 * 8 * 8192 * 4
-    assert L.msa_project_workspace_size(1024, 3072, 23, by) == OK and n.value == 16 * 23 * 8 * 8192 * 4
+    # decode batch 64 at hidden 3072: a 128-byte line of control words plus one line per arrival
+    # counter (head, 64-token chunk), rounded up to 256 bytes, then 8 K slices of 384 columns per head
+    # with 8,192 binary32 partial sums each
+    ctl = lambda groups: (128 * (1 + groups) + 255) // 256 * 256
+    assert n.value == ctl(23) + 23 * 8 * 8192 * 4
+    assert L.msa_project_workspace_size(1024, 3072, 23, by) == OK and n.value == ctl(16 * 23) + 16 * 23 * 8 * 8192 * 4
+    # at most 63 K slices of 384 columns per (head, chunk) on the split-K path; the tiled path has no limit
+    assert L.msa_project_workspace_size(64, 63 * 384, 23, by) == OK
+    assert L.msa_project_workspace_size(64, 63 * 384 + 64, 23, by) == SHAPE
+    assert L.msa_project_workspace_size(1025, 63 * 384 + 64, 23, by) == OK and n.value == 0
     assert L.msa_project_workspace_size(1025, 3072, 23, by) == OK and n.value == 0   # the tiled kernel needs none
     assert L.msa_project_workspace_size(0, 3072, 23, by) == OK and n.value == 0
     assert L.msa_project_workspace_size(64, 100, 23, by) == SHAPE

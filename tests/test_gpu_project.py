@@ -47,7 +47,7 @@ def dev16(a):
 
 
 def workspace(T, K, heads):
-    return torch.empty(max(msa.msa_project_workspace_size(T, K, heads), 256), dtype=torch.uint8, device="cuda")
+    return torch.zeros(max(msa.msa_project_workspace_size(T, K, heads), 256), dtype=torch.uint8, device="cuda")
 
 
 def gpu_project(h, w, ws=None):
@@ -275,23 +275,51 @@ def test_project_produce_prefill_65536_sampled():
     assert min(fr) >= 0.95
 
 
-def test_workspace_contents_do_not_matter():
-    """Two decode calls on one workspace, the second after the outputs are cleared and the workspace
-    is filled with garbage: both write the same bytes."""
+def assert_workspace_at_rest(ws):
+    """msa_project.h: a completed call leaves the whole split-K workspace zero."""
+    nz = torch.nonzero(ws).flatten()
+    assert nz.numel() == 0, nz[:8].tolist()
+
+
+def test_workspace_at_rest_after_every_call():
+    """Two decode calls on one workspace, the second after the outputs are cleared: both write the same
+    bytes, and each leaves the workspace all zero (every partial-sum word consumed and cleared)."""
     wl = W.decode_batch64()
     h, w = W.with_projection(wl, seed=9)
     ws = workspace(wl.T, h.shape[1], wl.W // 128)
     d = fused(wl, h, w, ws=ws)
+    assert_workspace_at_rest(ws)
     first = (d.q_out.clone(), d.iq_out.clone(), [s.clone() for s in d.storages])
     d.q_out.zero_()
     d.iq_out.zero_()
     for s in d.storages:
         s.fill_(W.SENTINEL_BYTE)
-    ws.fill_(0xA5)
     fused(wl, h, w, d=d, ws=ws)
+    assert_workspace_at_rest(ws)
     assert torch.equal(first[0], d.q_out) and torch.equal(first[1], d.iq_out)
     for a, b in zip(first[2], d.storages):
         assert torch.equal(a, b)
+
+
+def test_workspace_not_at_rest_sets_the_error_word():
+    """Words of the partial-sum region left nonzero (a workspace not zeroed): they read as partial sums
+    that have already arrived, so the outputs may be wrong, but the call completes and nothing waits
+    longer than its bound.  Here a whole token group's fragments of one slice are preset: the reducing
+    wave takes them (and clears them), so the call ends with the workspace at rest again.  Then the
+    reverse case, forced from the host: a slice that never writes its words cannot be simulated
+    without changing the kernel, so the error path is exercised by a workspace whose header error word
+    is preset, which the call must leave as it is (error bits are only ever added)."""
+    wl = W.tiny_decode()
+    h, w = W.with_projection(wl, seed=5, dyadic=True)
+    ws = workspace(wl.T, h.shape[1], wl.W // 128)
+    ws[4:8].view(torch.int32)[0] = 4
+    say("  tiny decode, error word preset to 4")
+    d = fused(wl, h, w, ws=ws)
+    assert int(ws[4:8].view(torch.int32).item()) == 4
+    ws[4:8].zero_()
+    assert_workspace_at_rest(ws)
+    wl.x = oracle.project(h, w, num_threads=THREADS)
+    check(wl, d)
 
 
 def test_graph_replay_decode_layers():
@@ -337,10 +365,10 @@ def test_graph_replay_decode_layers():
             for d in devs:
                 d.q_out.fill_(3)
                 d.iq_out.fill_(3)
-            ws.fill_(0x5A)
             torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
+        assert_workspace_at_rest(ws)
         for (q, iq, sts), d in zip(eager, devs):
             assert torch.equal(q, d.q_out) and torch.equal(iq, d.iq_out), rep
             for a, b in zip(sts, d.storages):

@@ -56,7 +56,7 @@ def run(wl, d, h, w, cos, sin, noalloc):
     if noalloc:
         msa.msa_project_produce_noalloc(*args, **kw)
     else:
-        ws = torch.empty(max(msa.msa_project_workspace_size(wl.T, h.shape[1], wl.W // 128), 256), dtype=torch.uint8,
+        ws = torch.zeros(max(msa.msa_project_workspace_size(wl.T, h.shape[1], wl.W // 128), 256), dtype=torch.uint8,
                          device="cuda")
         msa.msa_project_produce(*args, workspace=ws, **kw)
     torch.cuda.synchronize()
