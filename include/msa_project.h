@@ -26,9 +26,9 @@
  *
  * Kernels: for up to 1,024 tokens (the decode and verify batches) one split-K launch (heads x
  * 64-token chunks x K slices, on v_mfma_f32_32x32x16_bf16): the slices of a head and chunk leave
- * their partial sums in the workspace, and the slice that finishes last adds them in a fixed order
- * and runs the epilogue in msa_produce's row layout, 8 tokens per wave; for larger batches (prefill)
- * one 256 x 256 tiled kernel on the same matrix instruction.
+ * their partial sums in the workspace, then each adds one group of 8 tokens over all slices in a
+ * fixed order and runs the epilogue in msa_produce's row layout; for larger batches (prefill) one
+ * 256 x 256 tiled kernel on the same matrix instruction.
  *
  * Conventions are those of msa_produce.h (operands checked for residency on eager calls, no allocation,
  * no synchronisation, all checks on the host before any launch, MSA_OK means enqueued,
@@ -49,19 +49,20 @@ extern "C" {
  * msa_project_workspace_size — bytes of workspace (device memory, 256-byte aligned) a projection of
  * num_tokens rows of width hidden onto num_heads heads of 128 columns needs (both entry points
  * take the same).  Zero for batches above 1,024 tokens (one tiled kernel, no workspace).  Up to
- * 1,024 tokens the projection is one split-K launch whose work-groups meet in the workspace: it
- * starts with C = 128 * (1 + num_heads * ceil(num_tokens / 64)) bytes of uint32 control words,
- * rounded up to a multiple of 256 (word 1: an error word; word 32 * (1 + head * ceil(T / 64) +
- * chunk), one per 128-byte line: that head and 64-token chunk's arrival counter), followed by the
- * partial sums.  At rest every control word is 0.
+ * 1,024 tokens the projection is one split-K launch whose work-groups exchange partial sums in the
+ * workspace: a 256-byte header (uint32 word 1: an error word), then the partial sums, each stored
+ * as the bitwise complement of its binary32 bits so that a zero word means "not written yet".
+ * Every partial sum is read once and cleared by the work-group that reads it.
  *
- * The workspace must be zero-filled before its first use; every call that completes leaves the
- * control words at rest, so no call needs it cleared again, whatever its sizes.  Calls that share a
- * workspace must not overlap in time (same stream, or ordered).  If an arrival counter is not at
- * rest when a call starts (a workspace never zeroed, or overwritten), the call sets a nonzero error
- * word and leaves that head and chunk's outputs unwritten; zero the workspace again before reusing
- * it.  Nothing in the launch waits for another work-group, so no state of the workspace can make a
- * call hang.
+ * The workspace must be zero-filled before its first use; every call that completes leaves it all
+ * zero again, so no call needs it cleared, whatever its sizes.  Calls that share a workspace must
+ * not overlap in time (same stream, or ordered).  A work-group waits (polls) only for the other K
+ * slices of its own head and 64-token chunk, a bounded number of times: if a call starts on a
+ * workspace that is not all zero, its outputs may be wrong and the workspace is left dirty, and if
+ * a wait gives up (the device cannot hold one head's slices at once, at most 63 work-groups), the
+ * call sets error bits in the error word and leaves that token group's outputs unwritten.  No
+ * state of the workspace can make a call hang.  The error word is only ever set, never cleared,
+ * by the library.
  *
  * SHAPE when hidden is not a positive multiple of 64, num_heads is outside [1, 4096], or (1 to
  * 1,024 tokens) hidden exceeds 24,192 = 63 x 384 (at most 63 K slices per head and chunk).
@@ -127,10 +128,9 @@ msa_status msa_project_produce(const uint16_t* h, int64_t h_row_stride, int32_t 
  * refuses such queries during graph capture, make one eager call first.
  *
  * Every call on one GPU shares that GPU's array.  It starts zeroed, as a workspace must, and each
- * completed call leaves its control words at rest and its partial sums behind (each call overwrites
- * every partial sum it reads, so nothing needs clearing).  Calls that overlap in time on one GPU
- * (different streams without ordering between them, or several host threads) race on it and give
- * wrong results or leave it unusable; calls on one stream, or otherwise ordered, are safe.
+ * completed call leaves it all zero again.  Calls that overlap in time on one GPU (different
+ * streams without ordering between them, or several host threads) race on it, give wrong results
+ * and may leave it dirty for later calls; calls on one stream, or otherwise ordered, are safe.
  *
  * Arguments, results and the other errors: as msa_project_produce, minus workspace and
  * workspace_bytes.

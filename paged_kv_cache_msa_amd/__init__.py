@@ -464,8 +464,8 @@ def msa_produce_unfused(x, positions, slots, q_norm_weight, k_norm_weight, iq_no
 
 def msa_project_workspace_size(num_tokens: int, hidden: int, num_heads: int) -> int:
     """Bytes of (256-byte aligned) workspace the projection needs; 0 above 1,024 tokens.  Allocate it
-    zero-filled (torch.zeros) before its first use: it holds the split-K launch's control words, which
-    every completed call leaves as it found them."""
+    zero-filled (torch.zeros) before its first use: the split-K launch exchanges partial sums in it and
+    every completed call leaves it all zero again."""
     n = ctypes.c_uint64(0)
     st = lib().msa_project_workspace_size(int(num_tokens), int(hidden), int(num_heads), ctypes.byref(n))
     if st != 0:

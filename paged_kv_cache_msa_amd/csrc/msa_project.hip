@@ -12,16 +12,17 @@
 // rotate-half partners (f, f + 64) sit in the same lane (row blocks b and b + 2, same register).
 //
 // Kernels.
-//   project_split_kernel   up to 1,024 tokens: one work-group per (head, 64-token chunk, K slice of
-//                          at most 384 columns).  The slice of w (128 rows) and h (64 rows) is
-//                          requested into LDS at once with direct global -> LDS loads (the latency
-//                          of the whole slice is paid once), then each wave multiplies 32 of the
-//                          head's features against the chunk; partial sums go to the workspace.
-//   project_reduce_rows_kernel  one wave per (head, 8 tokens), in msa_produce's row layout (8
-//                          lanes per head row): each lane adds its 16 features' partial sums in slice
-//                          order (the same order on every call), rounds them to bf16 and runs the
-//                          producer's arithmetic on them.  The kernel boundary between the two makes
-//                          the partial sums visible across XCDs; no device-scope fence is needed.
+//   project_split_kernel   up to 1,024 tokens, one launch: one work-group of eight waves per (head,
+//                          64-token chunk, K slice of at most 384 columns).  The slice of w (128
+//                          rows) and h (64 rows) is requested into LDS at once with direct global ->
+//                          LDS loads (products start on its first half while the second lands);
+//                          each wave multiplies a 32-feature block of the head against 32 tokens.
+//                          The partial sums go to the workspace; the work-group of slice q then
+//                          adds token group q (8 tokens) over all slices in a fixed order and runs
+//                          the producer's arithmetic on the bf16-rounded sums in msa_produce's row
+//                          layout (8 lanes per head row).  Work-groups on different XCDs exchange
+//                          the partial sums with agent-scope coherent stores and polled loads, no
+//                          cache-wide fence (see the kernel's comment).
 //   project_tile_kernel    larger batches: 256 features (2 heads) x 256 tokens per work-group, eight
 //                          waves (two per SIMD) of one head x 64 tokens each, 64-wide K steps
 //                          through two LDS buffers filled by direct global -> LDS loads one step
@@ -477,20 +478,25 @@ __device__ __forceinline__ void row_epilogue(const Epi& e, int head, int32_t t, 
 // One launch for up to 1,024 tokens: one work-group of eight waves per (head, 64-token chunk, K
 // slice), block index = (head * n_tc + chunk) * S + slice.
 //   1. The slice of w (128 rows) and h (64 rows) is requested into LDS at once (its memory latency
-//      paid once); wave (b, tb) multiplies the head's 32-feature block b against token block tb of
-//      the chunk with two MFMA chains.
+//      paid once), in two plane groups; wave (b, tb) multiplies the head's 32-feature block b
+//      against token block tb of the chunk with two MFMA chains, starting on the first group while
+//      the second is still arriving.
 //   2. The partial sums go to the workspace, complemented, with agent-scope coherent stores
 //      (written through, so a work-group on another XCD reads them without a cache-wide
 //      write-back).  Nothing waits for them here.
 //   3. Token group q (8 tokens) of the chunk is reduced by the work-group of slice q mod S: its wave
 //      j reads slices j, j + 8, ... of that token group, polling each fragment until every word of
 //      it has been written (nonzero), adds them in that order, zeroes the words it read, and hands
-//      its sum to wave 0 through LDS; wave 0 adds the eight waves' sums in wave order and runs the
-//      epilogue (row_epilogue).  The order is fixed, so every call gives the same bits.
-// The polls wait only for the other slices of the same (head, chunk): consecutive block indices,
-// which the hardware starts together (S <= 63 work-groups).  A wave that still finds unwritten words
-// after kPollLimit polls sets an error bit and leaves its token group unwritten, so no state of the
-// workspace can make a launch hang.
+//      its sum to wave 0 through LDS; wave 0 adds the eight waves' sums in wave order (for S <= 8,
+//      slice order) and runs the epilogue (row_epilogue).  The order is fixed, so every call gives
+//      the same bits.
+// A work-group polls only for the other S - 1 slices of its own (head, chunk), which hold the
+// adjacent block indices.  Work-groups start in block order as compute units free up, and each one
+// holds a compute unit only until its token group is reduced, so the polls end as long as S work-
+// groups of this kernel fit on the device at once (S <= 63; at most 8 at hidden sizes up to 3,072).
+// A wave that still finds unwritten words after kPollLimit polls (only possible if that does not
+// hold, or if the workspace was not zero on entry) sets an error bit and leaves its token group
+// unwritten: no state of the device or the workspace can make a launch hang.
 template <bool kProduce>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void project_split_kernel(const SplitArgs a)
@@ -986,8 +992,9 @@ msa_status project_produce(const uint16_t* h, int64_t h_row_stride, int32_t num_
 // ------------------------------------------------------------------ the library's own scratch
 
 // Split-K partial sums of msa_project_produce_noalloc: one array per device, resident from the
-// code object's load until the process ends.  32 MiB holds the partial sums of 23 heads x 3,072
-// hidden columns for up to 256 tokens (64 tokens: 5.9 MB).  Host code never names `scratch` where
+// code object's load until the process ends; it starts zero (static storage), the state every call
+// needs on entry and leaves behind.  32 MiB holds the partial sums of 23 heads x 3,072 hidden
+// columns for up to 256 tokens (64 tokens: 5.9 MB).  Host code never names `scratch` where
 // it needs the memory: the name is a host-side stand-in, and each device's address comes from the
 // runtime (scratch_address).
 constexpr uint64_t kScratchBytes = 32ull << 20;
