@@ -481,6 +481,15 @@ def bench_projection(msa, W, torch, np, layers, steps, warmup):
             us = timed(g.replay, 50, 10, stream=s_)
         res[name + "_us_per_step"] = us
         res[name + "_us_per_layer"] = us / layers
+    # Algorithmic bytes of one fused layer call: the packed weight and the hidden rows, each token's RoPE
+    # coefficients (2 x 64 binary32) and slot, and the producer's outputs (its bytes minus the packed
+    # row it no longer reads and its per-token metadata).
+    ab = (wl0.W * K * 2 + Tt * K * 2 + Tt * (2 * 64 * 4 + 8)
+          + wl0.algorithmic_bytes() - Tt * wl0.W * 2 - Tt * 12)
+    gbs = ab / (res["fused_us_per_layer"] * 1e-6) / 1e9
+    res["algorithmic_bytes_per_layer_call"] = ab
+    res["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                       "traffic": None, "kernel": "project_split_kernel<true> (msa_project_produce, 64 x 3,072 x 2,944)"}
     out["decode"] = res
     log(f"[bench] projection decode-64: fused {res['fused_us_per_layer']:.2f} us/layer, "
         f"msa_project + produce {res['msa_project_plus_produce_us_per_layer']:.2f}, "
