@@ -36,6 +36,7 @@ def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert set(names) >= {"msa_produce", "msa_rope_table", "msa_quantize", "msa_rms_scale", "msa_status_string",
                           "msa_status_str", "msa_check_device_pointers", "msa_index_scores", "msa_index_topk",
+                          "msa_index_scores_grouped",
                           "msa_slots", "msa_produce_unfused", "msa_produce_unfused_workspace_size"}
     for n in names:
         assert hasattr(L, n), n
@@ -192,6 +193,16 @@ def test_index_entry_points_validate(L):
                               None) == SHAPE
     assert L.msa_index_scores(Q + 8, 0, 128, 2, POS, SEQ, PT, 160, 64, 160, 64, 10240, ref(ik), 128, 72, SLOTS, None) == ALIGN
     assert L.msa_index_scores(Q, 0, 128, 2, POS, SEQ, PT, 160, 64, 160, 64, 10240, ref(ik), 128, 72, SLOTS, None) == OK
+    # the grouped entry point: the same checks first, then its group size (1 ..= 8)
+    G = L.msa_index_scores_grouped
+    assert G(Q, 64, 64, 2, POS, SEQ, PT, 160, 64, 160, 64, 10240, ref(ik), 128, 72, 4, SLOTS, None) == UNSUP
+    assert G(Q, 0, 128, 3, POS, SEQ, PT, 160, 64, 160, 64, 10240, ref(view(sp=2 * 64 * 128)), 128, 72, 4, SLOTS,
+             None) == SHAPE
+    assert G(Q + 8, 0, 128, 2, POS, SEQ, PT, 160, 64, 160, 64, 10240, ref(ik), 128, 72, 4, SLOTS, None) == ALIGN
+    for g in (0, 9, -1):
+        assert G(Q, 0, 128, 2, POS, SEQ, PT, 160, 64, 160, 64, 10240, ref(ik), 128, 72, g, SLOTS, None) == SHAPE
+    for g in (1, 4, 8):
+        assert G(Q, 0, 128, 2, POS, SEQ, PT, 160, 64, 160, 64, 10240, ref(ik), 128, 72, g, SLOTS, None) == OK
     assert L.msa_index_topk(SLOTS, 10, 72, 0, Q, None, None) == SHAPE
     assert L.msa_index_topk(SLOTS, 10, 72, 65, Q, None, None) == SHAPE
     assert L.msa_index_topk(SLOTS, 10, 5000, 16, Q, None, None) == SHAPE
@@ -274,12 +285,10 @@ def test_project_workspace_size(L):
     n = ctypes.c_uint64(0)
     by = ctypes.byref(n)
     assert L.msa_project_workspace_size(64, 3072, 23, by) == OK
-    # decode batch 64 at hidden 3072: a 128-byte line of control words plus one line per arrival
-    # counter (head, 64-token chunk), rounded up to 256 bytes, then 8 K slices of 384 columns per head
-    # with 8,192 binary32 partial sums each
-    ctl = lambda groups: (128 * (1 + groups) + 255) // 256 * 256
-    assert n.value == ctl(23) + 23 * 8 * 8192 * 4
-    assert L.msa_project_workspace_size(1024, 3072, 23, by) == OK and n.value == ctl(16 * 23) + 16 * 23 * 8 * 8192 * 4
+    # decode batch 64 at hidden 3072: a 256-byte header (the error word), then 8 K slices of 384 columns
+    # per head with 8,192 binary32 partial sums each
+    assert n.value == 256 + 23 * 8 * 8192 * 4
+    assert L.msa_project_workspace_size(1024, 3072, 23, by) == OK and n.value == 256 + 16 * 23 * 8 * 8192 * 4
     # at most 63 K slices of 384 columns per (head, chunk) on the split-K path; the tiled path has no limit
     assert L.msa_project_workspace_size(64, 63 * 384, 23, by) == OK
     assert L.msa_project_workspace_size(64, 63 * 384 + 64, 23, by) == SHAPE
