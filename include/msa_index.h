@@ -59,6 +59,29 @@ msa_status msa_index_scores(const uint16_t* iq, int32_t num_tokens, int32_t head
                             double* block_scores, void* stream);
 
 /*
+ * msa_index_scores_grouped — msa_index_scores, with keys shared by groups of tokens.  Same arguments
+ * and results (every block score bit for bit), plus:
+ *
+ * group_tokens      1 ..= 8: tokens t = g * group_tokens + i (i < group_tokens) are scored together.
+ *                   Tokens of a group that belong to one sequence read each key once for all of
+ *                   them, which is what a speculative-decoding verify window (1 + draft_len
+ *                   consecutive positions of one sequence, stored next to each other) needs: pass
+ *                   its length.  A group whose tokens come from several sequences takes one pass per
+ *                   sequence, and padded tokens select nothing, as in msa_index_scores, so any
+ *                   grouping gives the same scores; only the speed depends on it.
+ *
+ * Layouts other than pages and selection blocks of multiples of 64 tokens (blocks of at most 2,048
+ * tokens), and group_tokens = 1, run msa_index_scores' kernels.  Errors: those of
+ * msa_index_scores; MSA_ERR_SHAPE for group_tokens outside [1, 8].
+ */
+msa_status msa_index_scores_grouped(const uint16_t* iq, int32_t num_tokens, int32_t head_dim, int32_t num_iq_heads,
+                                    const int32_t* positions, const int32_t* seq_idx,
+                                    const int32_t* page_table, int64_t page_table_stride, int32_t num_seqs,
+                                    int32_t max_pages_per_seq, int32_t page_size, int64_t num_pages,
+                                    const msa_cache_view* ik_cache, int32_t block_tokens, int32_t max_blocks,
+                                    int32_t group_tokens, double* block_scores, void* stream);
+
+/*
  * msa_index_topk — the top_k blocks of every row of block_scores (as msa_index_scores writes it).
  *
  * block_scores      device double [rows, max_blocks] (rows = num_iq_heads * T), 8-B aligned.

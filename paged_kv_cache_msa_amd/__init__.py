@@ -13,7 +13,8 @@ Entry points (same names as the C ABI):
   msa_quantize(...)     the output casts alone.
   msa_rms_scale(...)    the RMSNorm scale alone.
   msa_index_scores(...) indexer: block max of the exact dot products of index-Q with the visible keys
-                        of the index-K cache (include/msa_index.h).
+                        of the index-K cache (include/msa_index.h); group_tokens > 1 calls
+                        msa_index_scores_grouped (the same scores, key loads shared within groups).
   msa_index_topk(...)   indexer: the top-k blocks of every (index-Q head, token) row.
   msa_project(...)      the packed projection x = bf16(h w^T) on the matrix cores (include/msa_project.h).
   msa_project_produce(...)  the same projection with the producer as its epilogue: the packed row
@@ -92,6 +93,9 @@ def lib() -> ctypes.CDLL:
         L.msa_rms_scale.restype = ctypes.c_int
         L.msa_index_scores.argtypes = [p, i32, i32, i32, p, p, p, i64, i32, i32, i32, i64, cv, i32, i32, p, p]
         L.msa_index_scores.restype = ctypes.c_int
+        L.msa_index_scores_grouped.argtypes = [p, i32, i32, i32, p, p, p, i64, i32, i32, i32, i64, cv, i32, i32, i32,
+                                               p, p]
+        L.msa_index_scores_grouped.restype = ctypes.c_int
         L.msa_index_topk.argtypes = [p, i32, i32, i32, p, p, p]
         L.msa_index_topk.restype = ctypes.c_int
         u64 = ctypes.c_uint64
@@ -351,10 +355,12 @@ def msa_rms_scale(sum_sq, r_out, rms_eps: float, head_dim: int = 128, stream=Non
 
 
 def msa_index_scores(iq, positions, seq_idx, page_table, ik_cache, block_scores, *, ik_scale=None,
-                     num_pages: Optional[int] = None, block_tokens: int = 128, stream=None) -> None:
+                     num_pages: Optional[int] = None, block_tokens: int = 128, group_tokens: int = 1,
+                     stream=None) -> None:
     """Indexer block scores.  iq [T, Hiq, 128] bf16; ik_cache a 4-D index-K cache view
     [num_pages, Hik, page_size, 128] (1-byte fp8 with a float32 [1] scale, or 2-byte bf16);
-    block_scores float64 [Hiq, T, max_blocks]."""
+    block_scores float64 [Hiq, T, max_blocks].  group_tokens > 1 calls msa_index_scores_grouped
+    (the same scores; consecutive tokens of one sequence share their key loads, e.g. verify windows)."""
     _tensor("iq", iq, size=2, dim=3, contiguous=True)
     T, hiq = iq.shape[0], iq.shape[1]
     _need(iq.shape[2] == 128, f"iq must be [T, Hiq, 128], got {tuple(iq.shape)}")
@@ -369,12 +375,15 @@ def msa_index_scores(iq, positions, seq_idx, page_table, ik_cache, block_scores,
     _same_device(iq, positions, seq_idx, page_table, ik_cache, ik_scale if ik_cache.element_size() == 1 else None,
                  block_scores)
     view = cache_view(ik_cache, ik_scale)
-    st = lib().msa_index_scores(_ptr(iq), T, 128, hiq, _ptr(positions), _ptr(seq_idx), _ptr(page_table),
-                                page_table.stride(0), page_table.shape[0], page_table.shape[1], page_size,
-                                pages, ctypes.byref(view), int(block_tokens), block_scores.shape[-1],
-                                _ptr(block_scores), _stream(stream))
+    common = (_ptr(iq), T, 128, hiq, _ptr(positions), _ptr(seq_idx), _ptr(page_table), page_table.stride(0),
+              page_table.shape[0], page_table.shape[1], page_size, pages, ctypes.byref(view), int(block_tokens),
+              block_scores.shape[-1])
+    if group_tokens == 1:
+        st = lib().msa_index_scores(*common, _ptr(block_scores), _stream(stream))
+    else:
+        st = lib().msa_index_scores_grouped(*common, int(group_tokens), _ptr(block_scores), _stream(stream))
     if st != 0:
-        raise MsaError(st, "msa_index_scores")
+        raise MsaError(st, "msa_index_scores" if group_tokens == 1 else "msa_index_scores_grouped")
 
 
 def msa_index_topk(block_scores, block_ids, counts=None, stream=None) -> None:

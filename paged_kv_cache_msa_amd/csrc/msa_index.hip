@@ -480,6 +480,225 @@ void index_scores_rs_kernel(const ScoreArgs a)
     if (lane < NH) a.out[((int64_t)(a.head0 + lane) * a.T + t) * a.max_blocks + b] = best;
 }
 
+// ------------------------------------------------------------------ grouped score kernel
+
+// Tokens that read the same keys (a verify window: the 1 + draft_len consecutive positions of one
+// sequence) are scored together: one wave per (group of G consecutive tokens, block) computes the
+// dot products of every (token, head) query of the group (G x NH <= 8 items) with each key it loads,
+// so a key is loaded and decoded once per group instead of once per token.
+//
+// 16 lanes per key (8 elements each), 4 keys per step.  Every lane holds all 8 queries' 8 elements
+// in binary64 (128 registers) and forms the 8 partial dot products of its key; the items are summed
+// over the key's 16 lanes with the reduce-scatter of the batch kernel extended by one step: lane L
+// keeps item s ^ g(L & 7) in slot s (queries loaded in that order), three exchanges within each
+// 8-lane half (partners L ^ 1, L ^ 2, L ^ 7) leave lane L with item g(L & 7) summed over its half,
+// and a fourth (partner L ^ 8, the DPP row rotation by 8) adds the other half, which holds the same
+// item.  Each dot product is still the exact binary64 sum, so the block scores equal the per-token
+// kernels' bit for bit.
+//
+// The keys a pass loads are those of one sequence; the group's tokens of that sequence are scored in
+// the pass (a key counts for token i only up to its own position), the others in later passes, so
+// any grouping of tokens gives the per-token result; a verify window takes one pass.
+constexpr int kGLanes = 16;                       // lanes per key
+constexpr int kGKeys = kWave / kGLanes;           // keys per step
+constexpr int kGElems = kHeadDim / kGLanes;       // elements per lane
+constexpr int kGItems = 8;                        // (token, head) queries per wave
+constexpr int kGSteps = 8;                        // steps per batch
+constexpr int kGBatchPos = kGSteps * kGKeys;      // 32 positions, never across a page
+constexpr int kMaxGroupTokens = 8;
+
+template <bool kBf16>
+struct GKeyRaw {
+    uint32_t w[kBf16 ? 4 : 2];
+};
+
+template <bool kBf16>
+struct GBatch {
+    GKeyRaw<kBf16> raw[kGSteps];
+    int32_t pg;
+};
+
+template <int NH, bool kBf16>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void index_scores_group_kernel(const ScoreArgs a, int32_t group, int32_t n_groups)
+{
+    // Single-head bf16 batches hold 32 raw registers each; two would not fit beside the queries.
+    constexpr bool kPairs = !kBf16;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t item = blockIdx.x * kWavesPerBlock + (uint32_t)wave;   // block-major, as the others
+    if (item >= (uint32_t)n_groups * (uint32_t)a.max_blocks) return;      // wave-uniform
+    const int32_t b = (int32_t)(item / (uint32_t)n_groups);
+    const int32_t t0 = (int32_t)(item - (uint32_t)b * (uint32_t)n_groups) * group;
+    const int ks = lane / kGLanes;
+    const int sub = lane % kGLanes;
+    const int g = slot_map(sub & 7);                  // this lane's item after the reduce-scatter
+    const int n_items = group * NH;                   // <= kGItems
+
+    // Queries first: slot s holds item s ^ g (token (s ^ g) / NH, head (s ^ g) % NH); slots past the
+    // group's items (or past T) read token t0's first head and are never counted.
+    uint4 qraw[kGItems];
+#pragma unroll
+    for (int s = 0; s < kGItems; ++s) {
+        const int j = s ^ g;
+        const int ti = j < n_items ? j / NH : 0;
+        const int h = j < n_items ? j % NH : 0;
+        const int32_t t = min(t0 + ti, a.T - 1);
+        qraw[s] = *reinterpret_cast<const uint4*>(a.iq + ((int64_t)t * a.hiq + a.head0 + h) * kHeadDim + sub * kGElems);
+    }
+    // The group's token metadata, lane i for token t0 + i; then wave-uniform copies.
+    int32_t m_pos = -1, m_seq = -1, m_ok = 0;
+    if (lane < group && t0 + lane < a.T) {
+        m_pos = a.pos[t0 + lane];
+        m_seq = a.seq[t0 + lane];
+        int32_t unused;
+        m_ok = page_of(a, m_seq, m_pos, &unused) >= 0 ? 1 : 0;
+    }
+    uint32_t valid = 0;                               // bit i: token t0 + i has a slot of its own
+    int32_t tpos[kMaxGroupTokens], tseq[kMaxGroupTokens];
+#pragma unroll
+    for (int i = 0; i < kMaxGroupTokens; ++i) {
+        tpos[i] = __builtin_amdgcn_readlane(m_pos, i);
+        tseq[i] = __builtin_amdgcn_readlane(m_seq, i);
+        valid |= (uint32_t)(__builtin_amdgcn_readlane(m_ok, i) & (i < group ? 1 : 0)) << i;
+    }
+    // This lane's item: its token and position (selected by value, no indexed registers).
+    const int my_tok = g < n_items ? g / NH : kMaxGroupTokens;
+    int32_t my_pos = -1;
+#pragma unroll
+    for (int i = 0; i < kMaxGroupTokens; ++i) my_pos = my_tok == i ? tpos[i] : my_pos;
+
+    double qs[kGItems][kGElems];
+#pragma unroll
+    for (int s = 0; s < kGItems; ++s) {
+        const uint32_t w[4] = {qraw[s].x, qraw[s].y, qraw[s].z, qraw[s].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            qs[s][2 * i] = (double)__uint_as_float(w[i] << 16);
+            qs[s][2 * i + 1] = (double)__uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+    const double scale = kBf16 ? 1.0 : (double)*a.ik.scale;
+    const int64_t head_off = (int64_t)(a.head0 / a.group) * a.ik.sh;
+    const int64_t p0_64 = (int64_t)b * a.block_tokens;
+    const int32_t p0 = (int32_t)min(p0_64, (int64_t)INT32_MAX);   // exact whenever the block is scored
+    double best = -INFINITY;                          // item g of this lane
+
+    uint32_t done = 0;
+    for (int pass = 0; pass < kMaxGroupTokens; ++pass) {                   // wave-uniform
+        const uint32_t left = valid & ~done;
+        if (!left) break;
+        const int lead = __builtin_ctz(left);
+        int32_t pass_seq = tseq[0];
+#pragma unroll
+        for (int i = 1; i < kMaxGroupTokens; ++i) pass_seq = lead == i ? tseq[i] : pass_seq;
+        uint32_t act = 0;
+        int32_t max_pos = -1;
+#pragma unroll
+        for (int i = 0; i < kMaxGroupTokens; ++i) {
+            const bool in = (left >> i & 1u) && tseq[i] == pass_seq;
+            act |= (in ? 1u : 0u) << i;
+            max_pos = in && tpos[i] > max_pos ? tpos[i] : max_pos;
+        }
+        done |= act;
+        const bool mine = my_tok < kMaxGroupTokens && (act >> my_tok & 1u);   // this lane's item scored now
+        const int32_t p_end = (int32_t)min(p0_64 + a.block_tokens, (int64_t)max_pos + 1);
+        if (p0_64 >= p_end) continue;
+        // Page-table entries of the pass's batches (lane j: batch j), one request.
+        int32_t batch_pg = -1;
+        {
+            const int64_t ps = p0_64 + (int64_t)lane * kGBatchPos;
+            int32_t unused;
+            if (ps < p_end) batch_pg = (int32_t)page_of(a, pass_seq, (int32_t)ps, &unused);
+        }
+        const int32_t n_batches = (p_end - p0 + kGBatchPos - 1) / kGBatchPos;
+        auto fetch = [&](int32_t j) {
+            GBatch<kBf16> bt;
+            const int32_t pb = p0 + j * kGBatchPos;
+            bt.pg = j < n_batches ? __builtin_amdgcn_readlane(batch_pg, j & (kWave - 1)) : -1;
+            const int32_t lp = a.page_shift >= 0 ? pb >> a.page_shift : pb / a.page_size;
+            const int32_t off0 = pb - lp * a.page_size;
+            constexpr int kEs = kBf16 ? 2 : 1;
+            const int64_t base = bt.pg >= 0 ? (int64_t)bt.pg * a.ik.sp + head_off + (int64_t)off0 * a.ik.st : 0;
+            const uint8_t* sb = a.ik.data + base * kEs;
+            const uint32_t st_b = bt.pg >= 0 ? (uint32_t)a.ik.st * kEs : 0u;
+#pragma unroll
+            for (int i = 0; i < kGSteps; ++i) {
+                const uint32_t key = (uint32_t)(i * kGKeys + ks);
+                const uint8_t* src = sb + (key * st_b + (uint32_t)(sub * kGElems * kEs));
+                if (kBf16) {
+                    const uint4 v = *reinterpret_cast<const uint4*>(src);
+                    bt.raw[i].w[0] = v.x; bt.raw[i].w[kBf16 ? 1 : 0] = v.y;
+                    bt.raw[i].w[kBf16 ? 2 : 0] = v.z; bt.raw[i].w[kBf16 ? 3 : 0] = v.w;
+                } else {
+                    const uint2 v = *reinterpret_cast<const uint2*>(src);
+                    bt.raw[i].w[0] = v.x; bt.raw[i].w[1] = v.y;
+                }
+            }
+            return bt;
+        };
+        auto consume = [&](const GBatch<kBf16>& bt, int32_t j) {
+#pragma unroll
+            for (int i = 0; i < kGSteps; ++i) {
+                double k[kGElems];
+                if (kBf16) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        k[2 * e] = (double)__uint_as_float(bt.raw[i].w[e] << 16);
+                        k[2 * e + 1] = (double)__uint_as_float(bt.raw[i].w[e] & 0xffff0000u);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)bt.raw[i].w[e], false);
+                        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)bt.raw[i].w[e], true);
+                        k[4 * e] = (double)lo[0];
+                        k[4 * e + 1] = (double)lo[1];
+                        k[4 * e + 2] = (double)hi[0];
+                        k[4 * e + 3] = (double)hi[1];
+                    }
+                }
+                double v8[kGItems];
+#pragma unroll
+                for (int s = 0; s < kGItems; ++s) {
+                    double acc = 0.0;
+#pragma unroll
+                    for (int e = 0; e < kGElems; ++e) acc = __builtin_fma(qs[s][e], k[e], acc);
+                    v8[s] = acc;
+                }
+                double v4[4], v2[2];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) v4[m] = v8[2 * m] + dpp_f64<0xb1>(v8[2 * m + 1]);   // partner L ^ 1
+#pragma unroll
+                for (int m = 0; m < 2; ++m) v2[m] = v4[2 * m] + dpp_f64<0x4e>(v4[2 * m + 1]);   // partner L ^ 2
+                const double half = v2[0] + dpp_f64<0x141>(v2[1]);                             // partner L ^ 7
+                const double dot = half + dpp_f64<0x128>(half);                                // partner L ^ 8
+                const int32_t p = p0 + j * kGBatchPos + i * kGKeys + ks;                       // this lane's key
+                if (mine && bt.pg >= 0 && p < p_end && p <= my_pos) best = max_no_nan(best, dot * scale);
+            }
+        };
+        if (kPairs) {
+            for (int32_t j = 0; j < n_batches; j += 2) {
+                const GBatch<kBf16> A = fetch(j);
+                const GBatch<kBf16> B = fetch(j + 1);
+                consume(A, j);
+                consume(B, j + 1);
+            }
+        } else {
+            for (int32_t j = 0; j < n_batches; ++j) consume(fetch(j), j);
+        }
+    }
+    // Max over the lanes that hold the same item: the other half of the key's lanes and the other key
+    // slots.  Lane L < 8 then holds item g(L)'s maximum.
+    best = max_no_nan(best, shfl_xor_f64(best, 8));
+    best = max_no_nan(best, shfl_xor_f64(best, 16));
+    best = max_no_nan(best, shfl_xor_f64(best, 32));
+    if (lane < 8 && g < n_items) {
+        const int32_t t = t0 + g / NH;
+        if (t < a.T) a.out[((int64_t)(a.head0 + g % NH) * a.T + t) * a.max_blocks + b] = best;
+    }
+}
+
 // (score, index) order of the selection: higher score first, then lower index.
 __device__ __forceinline__ bool before(double s1, int32_t i1, double s2, int32_t i2)
 {
@@ -597,12 +816,20 @@ msa_status launch_topk(const double* block_scores, int32_t rows, int32_t max_blo
 }
 
 // msa_index_scores' checks and launches.
-msa_status index_scores(const uint16_t* iq, int32_t num_tokens, int32_t head_dim, int32_t num_iq_heads,
-                        const int32_t* positions, const int32_t* seq_idx,
-                        const int32_t* page_table, int64_t page_table_stride, int32_t num_seqs,
-                        int32_t max_pages_per_seq, int32_t page_size, int64_t num_pages,
-                        const msa_cache_view* ik_cache, int32_t block_tokens, int32_t max_blocks,
-                        double* block_scores, void* stream)
+// Every check of a score call, then its kernel arguments and layout (items == 0: nothing to launch).
+struct ScorePlan {
+    ScoreArgs a;
+    int64_t items;
+    bool batch_in_page;   // pages and blocks of multiples of 64 tokens, blocks of at most 2,048
+    bool in_page;         // pages and blocks of multiples of 8 tokens
+};
+
+msa_status prepare_scores(const uint16_t* iq, int32_t num_tokens, int32_t head_dim, int32_t num_iq_heads,
+                          const int32_t* positions, const int32_t* seq_idx,
+                          const int32_t* page_table, int64_t page_table_stride, int32_t num_seqs,
+                          int32_t max_pages_per_seq, int32_t page_size, int64_t num_pages,
+                          const msa_cache_view* ik_cache, int32_t block_tokens, int32_t max_blocks,
+                          double* block_scores, hipStream_t s, ScorePlan* plan)
 {
     if (head_dim != kHeadDim) return MSA_ERR_UNSUPPORTED;
     if (num_tokens < 0 || num_iq_heads < 1 || num_iq_heads > 4096 || block_tokens <= 0 || max_blocks < 0)
@@ -628,9 +855,10 @@ msa_status index_scores(const uint16_t* iq, int32_t num_tokens, int32_t head_dim
     if (__builtin_mul_overflow((int64_t)num_tokens, (int64_t)max_blocks, &items) || items + kWavesPerBlock > 0x7fffffffLL)
         return MSA_ERR_SHAPE;
     if (num_seqs > 0 && __builtin_mul_overflow((int64_t)num_seqs, page_table_stride, &tmp)) return MSA_ERR_OVERFLOW;
+    plan->items = items;
     if (items == 0) return MSA_OK;
 
-    ScoreArgs a;
+    ScoreArgs& a = plan->a;
     std::memset(&a, 0, sizeof(a));
     a.iq = iq;
     a.pos = positions;
@@ -650,48 +878,50 @@ msa_status index_scores(const uint16_t* iq, int32_t num_tokens, int32_t head_dim
     a.ik = ik;
     a.out = block_scores;
     // Batches of 32 / 64 positions never cross a page, and the parts start on batch boundaries.
-    const bool batch_in_page = page_size % 64 == 0 && block_tokens % 64 == 0 && block_tokens <= 64 * 32 &&
-                               (int64_t)64 * ik.st * (ik.is_bf16 ? 2 : 1) + 256 <= 0x7fffffffLL;
-    const bool in_page = page_size % kKeysPerStep == 0 && block_tokens % kKeysPerStep == 0;
-    const int items_per_group = batch_in_page ? kWavesPerBlock : kWavesPerBlock / kParts;
-    const dim3 grid((unsigned)((items + items_per_group - 1) / items_per_group));
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    {
-        const Span spans[] = {
-            {iq, nbytes((int64_t)num_tokens * num_iq_heads * kHeadDim, 2)},
-            {positions, nbytes(num_tokens, 4)},
-            {seq_idx, nbytes(num_tokens, 4)},
-            {page_table, num_seqs > 0 ? row_bytes(num_seqs, page_table_stride, max_pages_per_seq, 4) : 0},
-            {ik.data, ik_span},
-            {ik.scale, 4},
-            {block_scores, nbytes((int64_t)num_iq_heads * items, 8)},
-        };
-        const msa_status cs = check_operands(spans, sizeof(spans) / sizeof(spans[0]), s);
-        if (cs != MSA_OK) return cs;
-    }
-    // Launches over pairs of index-Q heads that read the same index-K head (two heads' queries fit
-    // the registers at once).
-    for (int32_t h0 = 0; h0 < num_iq_heads;) {
+    plan->batch_in_page = page_size % 64 == 0 && block_tokens % 64 == 0 && block_tokens <= 64 * 32 &&
+                          (int64_t)64 * ik.st * (ik.is_bf16 ? 2 : 1) + 256 <= 0x7fffffffLL;
+    plan->in_page = page_size % kKeysPerStep == 0 && block_tokens % kKeysPerStep == 0;
+    const Span spans[] = {
+        {iq, nbytes((int64_t)num_tokens * num_iq_heads * kHeadDim, 2)},
+        {positions, nbytes(num_tokens, 4)},
+        {seq_idx, nbytes(num_tokens, 4)},
+        {page_table, num_seqs > 0 ? row_bytes(num_seqs, page_table_stride, max_pages_per_seq, 4) : 0},
+        {ik.data, ik_span},
+        {ik.scale, 4},
+        {block_scores, nbytes((int64_t)num_iq_heads * items, 8)},
+    };
+    return check_operands(spans, sizeof(spans) / sizeof(spans[0]), s);
+}
+
+// Per-token kernels: one launch per pair of index-Q heads that read the same index-K head (two heads'
+// queries fit the registers at once).
+msa_status launch_scores(ScorePlan& p, hipStream_t s)
+{
+    ScoreArgs& a = p.a;
+    const int items_per_group = p.batch_in_page ? kWavesPerBlock : kWavesPerBlock / kParts;
+    const dim3 grid((unsigned)((p.items + items_per_group - 1) / items_per_group));
+    const bool bf = a.ik.is_bf16;
+    for (int32_t h0 = 0; h0 < a.hiq;) {
         const int32_t group_end = (h0 / a.group + 1) * a.group;
         const int nh = (group_end - h0 >= kMaxHeadsPerLaunch) ? kMaxHeadsPerLaunch : 1;
         a.head0 = h0;
         void* args[] = {&a};
         const void* fn;
-        if (batch_in_page)
-            fn = ik.is_bf16 ? (nh == 2 ? reinterpret_cast<const void*>(&index_scores_rs_kernel<2, true>)
-                                       : reinterpret_cast<const void*>(&index_scores_rs_kernel<1, true>))
-                            : (nh == 2 ? reinterpret_cast<const void*>(&index_scores_rs_kernel<2, false>)
-                                       : reinterpret_cast<const void*>(&index_scores_rs_kernel<1, false>));
-        else if (in_page)
-            fn = ik.is_bf16 ? (nh == 2 ? reinterpret_cast<const void*>(&index_scores_kernel<2, true, true>)
-                                       : reinterpret_cast<const void*>(&index_scores_kernel<1, true, true>))
-                            : (nh == 2 ? reinterpret_cast<const void*>(&index_scores_kernel<2, false, true>)
-                                       : reinterpret_cast<const void*>(&index_scores_kernel<1, false, true>));
+        if (p.batch_in_page)
+            fn = bf ? (nh == 2 ? reinterpret_cast<const void*>(&index_scores_rs_kernel<2, true>)
+                               : reinterpret_cast<const void*>(&index_scores_rs_kernel<1, true>))
+                    : (nh == 2 ? reinterpret_cast<const void*>(&index_scores_rs_kernel<2, false>)
+                               : reinterpret_cast<const void*>(&index_scores_rs_kernel<1, false>));
+        else if (p.in_page)
+            fn = bf ? (nh == 2 ? reinterpret_cast<const void*>(&index_scores_kernel<2, true, true>)
+                               : reinterpret_cast<const void*>(&index_scores_kernel<1, true, true>))
+                    : (nh == 2 ? reinterpret_cast<const void*>(&index_scores_kernel<2, false, true>)
+                               : reinterpret_cast<const void*>(&index_scores_kernel<1, false, true>));
         else
-            fn = ik.is_bf16 ? (nh == 2 ? reinterpret_cast<const void*>(&index_scores_kernel<2, true, false>)
-                                       : reinterpret_cast<const void*>(&index_scores_kernel<1, true, false>))
-                            : (nh == 2 ? reinterpret_cast<const void*>(&index_scores_kernel<2, false, false>)
-                                       : reinterpret_cast<const void*>(&index_scores_kernel<1, false, false>));
+            fn = bf ? (nh == 2 ? reinterpret_cast<const void*>(&index_scores_kernel<2, true, false>)
+                               : reinterpret_cast<const void*>(&index_scores_kernel<1, true, false>))
+                    : (nh == 2 ? reinterpret_cast<const void*>(&index_scores_kernel<2, false, false>)
+                               : reinterpret_cast<const void*>(&index_scores_kernel<1, false, false>));
         const hipError_t e = hipLaunchKernel(fn, grid, dim3(kBlock), args, 0, s);
         if (e != hipSuccess) return MSA_ERR_LAUNCH;
         h0 += nh;
@@ -699,6 +929,30 @@ msa_status index_scores(const uint16_t* iq, int32_t num_tokens, int32_t head_dim
     return MSA_OK;
 }
 
+// Grouped kernel: groups of `group` tokens, two index-Q heads per launch where the group and the
+// head grouping allow it (group x heads <= 8 items), else one.
+msa_status launch_scores_grouped(ScorePlan& p, int32_t group, hipStream_t s)
+{
+    ScoreArgs& a = p.a;
+    const int32_t n_groups = (a.T + group - 1) / group;
+    const int64_t waves = (int64_t)n_groups * a.max_blocks;
+    const dim3 grid((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock));
+    const bool bf = a.ik.is_bf16;
+    for (int32_t h0 = 0; h0 < a.hiq;) {
+        const int32_t group_end = (h0 / a.group + 1) * a.group;
+        const int nh = (group_end - h0 >= 2 && 2 * group <= kGItems) ? 2 : 1;
+        a.head0 = h0;
+        void* args[] = {&a, &group, const_cast<int32_t*>(&n_groups)};
+        const void* fn = bf ? (nh == 2 ? reinterpret_cast<const void*>(&index_scores_group_kernel<2, true>)
+                                       : reinterpret_cast<const void*>(&index_scores_group_kernel<1, true>))
+                            : (nh == 2 ? reinterpret_cast<const void*>(&index_scores_group_kernel<2, false>)
+                                       : reinterpret_cast<const void*>(&index_scores_group_kernel<1, false>));
+        const hipError_t e = hipLaunchKernel(fn, grid, dim3(kBlock), args, 0, s);
+        if (e != hipSuccess) return MSA_ERR_LAUNCH;
+        h0 += nh;
+    }
+    return MSA_OK;
+}
 
 }  // namespace
 
@@ -711,9 +965,32 @@ msa_status msa_index_scores(const uint16_t* iq, int32_t num_tokens, int32_t head
                             const msa_cache_view* ik_cache, int32_t block_tokens, int32_t max_blocks,
                             double* block_scores, void* stream)
 {
-    return index_scores(iq, num_tokens, head_dim, num_iq_heads, positions, seq_idx, page_table, page_table_stride,
-                        num_seqs, max_pages_per_seq, page_size, num_pages, ik_cache, block_tokens, max_blocks,
-                        block_scores, stream);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    ScorePlan p;
+    const msa_status st = prepare_scores(iq, num_tokens, head_dim, num_iq_heads, positions, seq_idx, page_table,
+                                         page_table_stride, num_seqs, max_pages_per_seq, page_size, num_pages,
+                                         ik_cache, block_tokens, max_blocks, block_scores, s, &p);
+    if (st != MSA_OK || p.items == 0) return st;
+    return launch_scores(p, s);
+}
+
+msa_status msa_index_scores_grouped(const uint16_t* iq, int32_t num_tokens, int32_t head_dim, int32_t num_iq_heads,
+                                    const int32_t* positions, const int32_t* seq_idx,
+                                    const int32_t* page_table, int64_t page_table_stride, int32_t num_seqs,
+                                    int32_t max_pages_per_seq, int32_t page_size, int64_t num_pages,
+                                    const msa_cache_view* ik_cache, int32_t block_tokens, int32_t max_blocks,
+                                    int32_t group_tokens, double* block_scores, void* stream)
+{
+    if (group_tokens < 1 || group_tokens > kMaxGroupTokens) return MSA_ERR_SHAPE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    ScorePlan p;
+    const msa_status st = prepare_scores(iq, num_tokens, head_dim, num_iq_heads, positions, seq_idx, page_table,
+                                         page_table_stride, num_seqs, max_pages_per_seq, page_size, num_pages,
+                                         ik_cache, block_tokens, max_blocks, block_scores, s, &p);
+    if (st != MSA_OK || p.items == 0) return st;
+    // One token per group, or a layout the grouped kernel does not take: the per-token kernels.
+    if (group_tokens == 1 || !p.batch_in_page) return launch_scores(p, s);
+    return launch_scores_grouped(p, group_tokens, s);
 }
 
 msa_status msa_index_topk(const double* block_scores, int32_t rows, int32_t max_blocks, int32_t top_k,

@@ -62,12 +62,6 @@ constexpr int kSplitLds = (128 + kChunk) * kSliceMax * 2;
 
 enum Stream { kQ = 0, kK = 1, kV = 2, kIQ = 3, kIK = 4 };
 
-__device__ __forceinline__ f32x16_t mfma(const uint4& a, const uint4& b, const f32x16_t& c)
-{
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
-                                                    c, 0, 0, 0);
-}
-
 // One 16-byte LDS read, issued as written: the compiler neither reorders it nor makes it wait for
 // the direct global -> LDS loads in flight (it cannot see which LDS bytes an inline read touches).
 // Completion is awaited explicitly with lgkm_wait below.
