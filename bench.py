@@ -308,11 +308,33 @@ def bench_prefill(msa, W, torch, iters, warmup, warm_ms, staged, unfused_iters=0
     return out
 
 
-def bench_indexer(msa, W, torch, np, reps):
-    """Indexer at decode batch 64 (positions 7000..9199, about 8k keys per sequence in a pre-populated
-    fp8 index-K cache): msa_index_scores + msa_index_topk (top 16 of 128-token blocks), 20 calls per
-    captured graph, `reps` graph replays timed after 5 warm ones."""
-    wl = W.decode_batch64()
+def _indexer_graph_us(msa, torch, score, topk, reps, per_graph=20):
+    """us per (score + top-k) call: `per_graph` calls captured in one graph, `reps` replays timed
+    after 5 warm ones."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        score()
+        topk()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(per_graph):
+                score()
+                topk()
+        for _ in range(5):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(reps):
+            g.replay()
+        e1.record(s)
+        torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1000 / (reps * per_graph)
+
+
+def _indexer_inputs(msa, W, torch, np, wl):
     fill = W.index_cache_fill(wl)
     iq = torch.from_numpy(W.index_queries(wl.T, wl.hiq).view(np.int16)).cuda()
     nb = W.index_blocks(wl)
@@ -326,28 +348,21 @@ def bench_indexer(msa, W, torch, np, reps):
     bs = torch.empty((wl.hiq, wl.T, nb), dtype=torch.float64, device="cuda")
     ids = torch.empty((wl.hiq, wl.T, 16), dtype=torch.int32, device="cuda")
     cnt = torch.empty((wl.hiq, wl.T), dtype=torch.int32, device="cuda")
-    per_graph = 20
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(s):
-        msa.msa_index_scores(iq, pos, seq, pt, view, bs, ik_scale=scale, num_pages=wl.num_pages)
-        msa.msa_index_topk(bs, ids, cnt)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g, stream=s):
-            for _ in range(per_graph):
-                msa.msa_index_scores(iq, pos, seq, pt, view, bs, ik_scale=scale, num_pages=wl.num_pages)
-                msa.msa_index_topk(bs, ids, cnt)
-        for _ in range(5):
-            g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(s)
-        for _ in range(reps):
-            g.replay()
-        e1.record(s)
-        torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1000 / (reps * per_graph)
+    return dict(store=store, iq=iq, nb=nb, view=view, scale=scale, pos=pos, seq=seq, pt=pt, bs=bs, ids=ids, cnt=cnt)
+
+
+def bench_indexer(msa, W, torch, np, reps):
+    """Indexer at decode batch 64 (positions 7000..9199, about 8k keys per sequence in a pre-populated
+    fp8 index-K cache): msa_index_scores + msa_index_topk (top 16 of 128-token blocks), 20 calls per
+    captured graph, `reps` graph replays timed after 5 warm ones."""
+    wl = W.decode_batch64()
+    d = _indexer_inputs(msa, W, torch, np, wl)
+    nb = d["nb"]
+    us = _indexer_graph_us(
+        msa, torch,
+        lambda: msa.msa_index_scores(d["iq"], d["pos"], d["seq"], d["pt"], d["view"], d["bs"], ik_scale=d["scale"],
+                                     num_pages=wl.num_pages),
+        lambda: msa.msa_index_topk(d["bs"], d["ids"], d["cnt"]), reps)
     keys = int((wl.positions.astype(np.int64) + 1).sum())
     # keys (128 B each, shared by both index-Q heads) + index-Q rows + token metadata + one page-table
     # entry per 64 keys + the block-score table written and read back + the selected ids
@@ -360,6 +375,36 @@ def bench_indexer(msa, W, torch, np, reps):
                 roofline=dict(bound="hbm", achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=gbs / HBM_PEAK_GBS,
                               traffic=counter_traffic("decode_64_indexer_call", INDEX_COUNTERS, INDEX_SRCS),
                               kernel="index_scores_rs_kernel<2, false> + index_topk_rank_kernel"))
+
+
+def bench_indexer_verify(msa, W, torch, np, reps, draft_len=3):
+    """Indexer on speculative-decoding verify windows (64 sequences x (1 + draft_len) consecutive
+    tokens, positions 7000..9200): msa_index_scores (keys loaded per token) against
+    msa_index_scores_grouped with one window per group (keys loaded once per window), each followed by
+    msa_index_topk, 20 calls per captured graph."""
+    wl = W.verify_window(draft_len=draft_len)
+    L = 1 + draft_len
+    d = _indexer_inputs(msa, W, torch, np, wl)
+    nb = d["nb"]
+    out = {"workload": f"verify windows: 64 sequences x {L} tokens, 2 index-Q heads, {nb} blocks of 128 tokens, "
+                       f"top 16", "tokens": wl.T}
+    topk = lambda: msa.msa_index_topk(d["bs"], d["ids"], d["cnt"])
+    for name, group in (("per_token", 1), ("grouped", L)):
+        out[name + "_us_per_call"] = _indexer_graph_us(
+            msa, torch,
+            lambda g=group: msa.msa_index_scores(d["iq"], d["pos"], d["seq"], d["pt"], d["view"], d["bs"],
+                                                 ik_scale=d["scale"], num_pages=wl.num_pages, group_tokens=g),
+            topk, reps)
+    # keys visible to the window's last token, read once per window: the grouped call's algorithmic bytes
+    last = wl.positions.reshape(-1, L)[:, -1].astype(np.int64)
+    keys = int((last + 1).sum())
+    b = (keys * 128 + wl.T * wl.hiq * 256 + wl.T * 8 + keys // 64 * 4 + 2 * wl.hiq * wl.T * nb * 8
+         + wl.hiq * wl.T * (16 * 4 + 4))
+    gbs = b / (out["grouped_us_per_call"] * 1e-6) / 1e9
+    out["algorithmic_bytes_per_call"] = b
+    out["roofline"] = dict(bound="hbm", achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=gbs / HBM_PEAK_GBS,
+                           traffic=None, kernel="index_scores_group_kernel<2, false> + index_topk_rank_kernel")
+    return out
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
@@ -636,6 +681,11 @@ def main():
     import numpy as np
     idx = None if args.no_indexer else bench_indexer(msa, W, torch, np, 50)
     torch.cuda.empty_cache()
+    idx_ver = None if args.no_indexer or args.no_verify else bench_indexer_verify(msa, W, torch, np, 50)
+    torch.cuda.empty_cache()
+    if idx_ver:
+        log(f"[bench] indexer on verify windows ({idx_ver['tokens']} tokens): per token "
+            f"{idx_ver['per_token_us_per_call']:.2f} us, grouped {idx_ver['grouped_us_per_call']:.2f} us per call")
     proj = None if args.no_projection else bench_projection(msa, W, torch, np, args.layers, args.steps, args.warmup)
     torch.cuda.empty_cache()
     cpu = None if args.no_cpu_baseline else cpu_baseline(W, args.cpu_seconds)
@@ -698,6 +748,7 @@ def main():
         "verify": ver,
         "projection": proj,
         "indexer": idx,
+        "indexer_verify": idx_ver,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
