@@ -815,7 +815,6 @@ msa_status launch_topk(const double* block_scores, int32_t rows, int32_t max_blo
     return e == hipSuccess ? MSA_OK : MSA_ERR_LAUNCH;
 }
 
-// msa_index_scores' checks and launches.
 // Every check of a score call, then its kernel arguments and layout (items == 0: nothing to launch).
 struct ScorePlan {
     ScoreArgs a;
