@@ -23,14 +23,15 @@
 //                          layout (8 lanes per head row).  Work-groups on different XCDs exchange
 //                          the partial sums with agent-scope coherent stores and polled loads, no
 //                          cache-wide fence (see the kernel's comment).
-//   project_tile_kernel    larger batches: 256 features (2 heads) x 256 tokens per work-group, eight
-//                          waves (two per SIMD) of one head x 64 tokens each, 64-wide K steps
-//                          through two LDS buffers filled by direct global -> LDS loads one step
-//                          ahead, fragments read one 16-column step ahead of the products.  The
-//                          output rows leave through LDS so that each store writes whole rows, and
-//                          the tile order is chosen so that the work-groups of one XCD walk the
-//                          feature tiles of the same token rows (their h panel stays in that XCD's
-//                          L2).
+//   project_tile_kernel    larger batches: 256 features (2 heads) x 256 tokens per work-group, four
+//                          waves (one per SIMD) of one head x 128 tokens each (16 products per
+//                          16-column step, 256 accumulator registers), 64-column K stages through
+//                          two LDS buffers filled by direct global -> LDS loads, fragments read one
+//                          step ahead of the products, and every load, copy and wait in a fixed
+//                          slot between the products.  The output rows leave through LDS so that
+//                          each store writes whole rows, and the tile order is chosen so that the
+//                          work-groups of one XCD walk the feature tiles of the same token rows
+//                          (their h panel stays in that XCD's L2).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -676,122 +677,149 @@ __device__ __forceinline__ uint32_t xcd_tile(uint32_t bid, uint32_t total)
     return prefix + (bid >> 3);
 }
 
+// One 16-byte LDS read at an immediate offset from addr (see lds_read16).
+template <int O>
+__device__ __forceinline__ u32x4_t lds_read16o(uint32_t addr)
+{
+    u32x4_t v;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(O));
+    return v;
+}
+
+// Waits until at most N LDS reads are in flight, tied to eight fragments (see lgkm_wait).
+template <int N>
+__device__ __forceinline__ void lgkm_wait8(u32x4_t (&a)[8])
+{
+    asm volatile("s_waitcnt lgkmcnt(%8)"
+                 : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7])
+                 : "n"(N));
+}
+
 template <bool kProduce>
-__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void project_tile_kernel(const TileArgs a)
 {
-    // [buffer][w | h] stages of 256 rows x 64 columns: each row 8 chunks of 16 B, chunk c of row r at
-    // position c ^ ((r >> 1) & 7) (fragment reads of 32 rows at one chunk are free of bank
-    // conflicts; measured), no padding.  After the last step the same memory stages the output rows.
-    constexpr int kStageBytes = kTile * 8 * 16;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kStageBytes];
+    // Two stages, each [w | h] x 256 rows x 64 columns: 128-byte rows, chunk c of row r at position
+    // c ^ ((r >> 1) & 7) (fragment reads of 32 rows at one chunk are free of bank conflicts;
+    // measured).  After the last step the first 32 KiB stage the output rows.
+    constexpr int kOp = kTile * 128;
+    constexpr int kStage = 2 * kOp;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage];
     const uint32_t L = xcd_tile(blockIdx.x, (uint32_t)(a.n_tt * a.n_tf));
     const int tile_t = (int)(L / (uint32_t)a.n_tf);
     const int tile_f = (int)(L - (uint32_t)tile_t * (uint32_t)a.n_tf);
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wf = wave & 1, wt = wave >> 1;                  // head of the tile, 64-token slab
-    const int hh = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hh = lane >> 5, r = lane & 31;
+    const int wf = wave & 1, wt = wave >> 1;            // head of the tile, 128-token half
     const int f_base = tile_f * kTile, t_base = tile_t * kTile;
 
-    // Direct global -> LDS copy of one stage: instruction j of wave w fills slots j * 512 + 64 w +
-    // lane of each operand; slot p holds row p >> 3 and logical chunk (p & 7) ^ ((row >> 1) & 7),
-    // the same chunk for all four instructions of a thread.  Rows past the matrix read its last row.
+    // Stage copy instruction i (0..15) of a thread: i < 8 copies w, else h; it fills slot
+    // (i & 7) * 256 + tid of that operand, which holds row 32 (i & 7) + (tid >> 3) and, at position
+    // tid & 7, logical chunk (tid & 7) ^ ((row >> 1) & 7).  Rows past the matrix read its last row.
     const int prow = tid >> 3;
     const int pchunk = (tid & 7) ^ ((tid >> 4) & 7);
-    const uint16_t* ga = a.w + pchunk * 8;
-    const uint16_t* gb = a.h + pchunk * 8;
-    const int64_t ws = a.w_stride, hs = a.h_stride;
-    auto dma_stage = [&](int st, int k0) {
+    const uint16_t* ga = a.w + (int64_t)min(f_base + prow, a.N - 1) * a.w_stride + pchunk * 8;
+    const uint16_t* gb = a.h + (int64_t)min(t_base + prow, a.e.T - 1) * a.h_stride + pchunk * 8;
+    const int wlast = a.N - 1 - f_base - prow, hlast = a.e.T - 1 - t_base - prow;
+    // The row offset is selected as an integer: hipcc (ROCm 7.2, gfx950) dropped the bound of the
+    // last row group when the same choice was written as a select between two pointers.
+    auto copy = [&](int buf, int k0, int i) {
+        const int j = i & 7;
+        const uint16_t* p = i < 8 ? ga + (int64_t)min(j * 32, max(wlast, 0)) * a.w_stride
+                                  : gb + (int64_t)min(j * 32, max(hlast, 0)) * a.h_stride;
+        __builtin_amdgcn_global_load_lds(p + k0, (lds_void*)(&lds[buf * kStage + (i >> 3) * kOp + (j * 256 + wave * 64) * 16]),
+                                         16, 0, 0);
+    };
+    // Fragment f of 16-column step ks: f < 4 is the head's 32-feature block f, else 32-token block f - 4.
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)&lds[0];
+    const int sw = (r >> 1) & 7;
+    uint32_t fa[4], fb[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint16_t* pa = ga + (int64_t)min(f_base + prow + 64 * j, a.N - 1) * ws + k0;
-            const uint16_t* pb = gb + (int64_t)min(t_base + prow + 64 * j, a.e.T - 1) * hs + k0;
-            __builtin_amdgcn_global_load_lds(pa, (lds_void*)(&lds[st][0][(j * 512 + wave * 64) * 16]), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(pb, (lds_void*)(&lds[st][1][(j * 512 + wave * 64) * 16]), 16, 0, 0);
+    for (int ks = 0; ks < 4; ++ks) {
+        fa[ks] = lds0 + (uint32_t)((wf * 128 + r) * 128 + (((2 * ks + hh) ^ sw) * 16));
+        fb[ks] = lds0 + (uint32_t)(kOp + (wt * 128 + r) * 128 + (((2 * ks + hh) ^ sw) * 16));
+    }
+    auto frag = [&](int buf, int ks, int f) -> u32x4_t {
+        const uint32_t pa = fa[ks] + (uint32_t)(buf * kStage), pb = fb[ks] + (uint32_t)(buf * kStage);
+        switch (f) {
+        case 0: return lds_read16o<0>(pa);
+        case 1: return lds_read16o<4096>(pa);
+        case 2: return lds_read16o<8192>(pa);
+        case 3: return lds_read16o<12288>(pa);
+        case 4: return lds_read16o<0>(pb);
+        case 5: return lds_read16o<4096>(pb);
+        case 6: return lds_read16o<8192>(pb);
+        default: return lds_read16o<12288>(pb);
         }
     };
-    // LDS byte addresses of this lane's fragments: feature block b (or token block tb), 16-column step ks.
-    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)&lds[0][0][0];
-    auto frag_addr = [&](int st, int m, int row, int ks) {
-        const int chunk = 2 * ks + hh;
-        return lds0 + (uint32_t)(((st * 2 + m) * kStageBytes) + (row * 8 + (chunk ^ ((row >> 1) & 7))) * 16);
-    };
-    const int arow = wf * 128 + (lane & 31), brow = wt * 64 + (lane & 31);
-    auto read_frags = [&](int st, int ks, u32x4_t (&af)[4], u32x4_t (&bf)[2]) {
-#pragma unroll
-        for (int b = 0; b < 4; ++b) af[b] = lds_read16(frag_addr(st, 0, arow + b * 32, ks));
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) bf[tb] = lds_read16(frag_addr(st, 1, brow + tb * 32, ks));
-    };
 
-    f32x16_t acc[4][2];
+    f32x16_t acc[4][4];
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) acc[b][tb] = f32x16_t{};
-
+        for (int tb = 0; tb < 4; ++tb) acc[b][tb] = f32x16_t{};
     const int nk = a.K / kBK;
-    dma_stage(0, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) copy(0, 0, i);
     __builtin_amdgcn_s_waitcnt(0x3f70);                          // vmcnt(0)
-    __syncthreads();
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int i = 0; i < 12; ++i) copy(1, min(1, nk - 1) * kBK, i);
+    u32x4_t F0[8], F1[8];
+#pragma unroll
+    for (int f = 0; f < 8; ++f) F0[f] = frag(0, 0, f);
+    // Stage kt is in buffer kt & 1.  Each step issues its 16 products one per slot, and the other
+    // instructions sit in fixed slots between them (sched_barrier keeps the order):
+    //   steps 0-2, slots 0-7: the next step's fragments;
+    //   step 0, slots 0-3: the last four copy instructions of stage kt + 1;
+    //   step 3, slot 3: wait for this wave's copies of stage kt + 1, then the barrier (every
+    //     wave's copies landed, every wave's reads of stage kt done);
+    //   step 3, slots 4-11: stage kt + 1's first fragments; slots 4-15: the first twelve copy
+    //     instructions of stage kt + 2, into the buffer the barrier released.
+    // Past the last stage the copies reload the last stage's columns (unused).  A stage's copies
+    // so go out about four steps before the wait for them (issued at the top of the stage before,
+    // two and a half steps ahead, the kernel was 6% slower; all sixteen after the barrier, 3%).
     for (int kt = 0; kt < nk; ++kt) {
-        const int s = kt & 1;
-        // The next stage into the other buffer (every wave finished reading it before the barrier
-        // that ended the previous step; the last step reloads its own columns there, unused).
-        dma_stage(s ^ 1, (kt + 1 < nk ? kt + 1 : kt) * kBK);
-        // Fragments one 16-column step ahead of the products.  The products run at raised wave
-        // priority (reset before the barrier), so that the SIMD's other wave issues its loads around
-        // them rather than between them (1% faster, measured).
-        u32x4_t a0[4], b0[2], a1[4], b1[2];
-        read_frags(s, 0, a0, b0);
-        read_frags(s, 1, a1, b1);
-        lgkm_wait<6>(a0, b0);
-        __builtin_amdgcn_s_setprio(1);
+        const int buf = kt & 1, nb = buf ^ 1;
+        const int k1 = min(kt + 1, nk - 1) * kBK, k2 = min(kt + 2, nk - 1) * kBK;
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int ks = 0; ks < 4; ++ks) {
+            u32x4_t (&C)[8] = (ks & 1) ? F1 : F0;
+            u32x4_t (&N)[8] = (ks & 1) ? F0 : F1;
+            lgkm_wait8<0>(C);
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb) acc[b][tb] = mfma4(a0[b], b0[tb], acc[b][tb]);
-        read_frags(s, 2, a0, b0);
-        lgkm_wait<6>(a1, b1);
-        __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb) acc[b][tb] = mfma4(a1[b], b1[tb], acc[b][tb]);
-        read_frags(s, 3, a1, b1);
-        lgkm_wait<6>(a0, b0);
-        __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb) acc[b][tb] = mfma4(a0[b], b0[tb], acc[b][tb]);
-        lgkm_wait<0>(a1, b1);
-        __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb) acc[b][tb] = mfma4(a1[b], b1[tb], acc[b][tb]);
-        __builtin_amdgcn_s_setprio(0);
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(0x3f70);                      // vmcnt(0): this wave's share landed
-        __syncthreads();
+            for (int i = 0; i < 16; ++i) {
+                acc[i >> 2][i & 3] = mfma4(C[i >> 2], C[4 + (i & 3)], acc[i >> 2][i & 3]);
+                if (ks < 3) {
+                    if (i < 8) N[i] = frag(buf, ks + 1, i);
+                    if (ks == 0 && i < 4) copy(nb, k1, 12 + i);
+                } else {
+                    if (i == 3) {
+                        __builtin_amdgcn_s_waitcnt(0x3f70);      // vmcnt(0)
+                        __builtin_amdgcn_s_barrier();
+                    }
+                    if (i >= 4 && i < 12) N[i - 4] = frag(nb, 0, i - 4);
+                    if (i >= 4) copy(buf, k2, i - 4);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
     }
+    __builtin_amdgcn_s_waitcnt(0x3f70);                          // vmcnt(0): every copy landed
+    lgkm_wait8<0>(F0);
+    __syncthreads();
 
-    // Every wave has finished reading the stages (the barrier above) and the last copies have landed:
-    // the first 8 KiB per wave now stage its output rows.
     const int head = tile_f * 2 + wf;
     if (head >= a.heads) return;
-    uint8_t* stage = &lds[0][0][0] + wave * 8192;
+    uint8_t* stage = &lds[0] + wave * 8192;
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
+    for (int tb = 0; tb < 4; ++tb) {
         float v[4][16];
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
             for (int i = 0; i < 16; ++i) v[b][i] = acc[b][tb][i];
-        const int32_t t = t_base + wt * 64 + tb * 32 + (lane & 31);
+        const int32_t t = t_base + wt * 128 + tb * 32 + r;
         EpiIn unused;
         const RowOut o = epilogue_math<kProduce, true>(a.e, head, t, v, unused);
         row_store_staged(o, v, stage);
@@ -893,7 +921,7 @@ msa_status launch_projection(const uint16_t* h, int64_t h_row_stride, int32_t T,
         a.e = e;
         void* args[] = {&a};
         const dim3 grid((unsigned)((int64_t)a.n_tt * a.n_tf));
-        err = hipLaunchKernel(reinterpret_cast<const void*>(&project_tile_kernel<kProduce>), grid, dim3(512), args, 0,
+        err = hipLaunchKernel(reinterpret_cast<const void*>(&project_tile_kernel<kProduce>), grid, dim3(256), args, 0,
                               s);
     }
     return err == hipSuccess ? MSA_OK : MSA_ERR_LAUNCH;
