@@ -79,6 +79,9 @@ msa_status msa_project_workspace_size(int32_t num_tokens, int32_t hidden, int32_
  * num_cols     N: a positive multiple of 128, at most 4096 * 128.
  * x_out        device bf16 [T, num_cols], row stride x_row_stride (>= num_cols, multiple of 8), 16-B aligned.
  * workspace    as msa_project_workspace_size states; may be NULL when it gives 0.
+ *
+ * STRIDE also when T > 1,024 and h_row_stride or w_row_stride is 2^22 elements or more (the tiled
+ * kernel addresses a tile's 256 rows with 32-bit offsets).
  */
 msa_status msa_project(const uint16_t* h, int64_t h_row_stride, int32_t num_tokens, int32_t hidden,
                        const uint16_t* w, int64_t w_row_stride, int32_t num_cols,

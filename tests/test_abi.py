@@ -321,6 +321,8 @@ def call_project(L, **kw):
     (dict(ws=3071), STRIDE),
     (dict(xs=2940), STRIDE),
     (dict(xs=2948), STRIDE),
+    (dict(T=1025, hs=1 << 22), STRIDE),             # the tiled kernel's 32-bit row offsets
+    (dict(T=1025, ws=1 << 22), STRIDE),
     (dict(T=64, h=None), NULLP),
     (dict(T=64, x=None), NULLP),
     (dict(h=HID + 8), ALIGN),
@@ -356,6 +358,7 @@ def call_project_produce(L, **kw):
     (dict(eps=-1.0), SHAPE),
     (dict(K=100), SHAPE),
     (dict(hs=3076), STRIDE),
+    (dict(T=1025, hs=1 << 22), STRIDE),
     (dict(T=64, cos=None), NULLP),
     (dict(T=64, slots=None), NULLP),
     (dict(T=64, q=None), NULLP),
