@@ -92,6 +92,31 @@ __device__ __forceinline__ void lgkm_wait(u32x4_t (&a)[4], u32x4_t (&b)[4])
                  : "n"(N));
 }
 
+// One 16-byte LDS read at an immediate offset from addr (see lds_read16).
+template <int O>
+__device__ __forceinline__ u32x4_t lds_read16o(uint32_t addr)
+{
+    u32x4_t v;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(O));
+    return v;
+}
+
+// Waits until at most N LDS reads are in flight, tied to eight fragments (see lgkm_wait).
+template <int N>
+__device__ __forceinline__ void lgkm_wait8(u32x4_t (&a)[8])
+{
+    asm volatile("s_waitcnt lgkmcnt(%8)"
+                 : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7])
+                 : "n"(N));
+}
+
+// Waits until at most N LDS reads are in flight, tied to four fragments (see lgkm_wait).
+template <int N>
+__device__ __forceinline__ void lgkm_wait4(u32x4_t (&a)[4])
+{
+    asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]) : "n"(N));
+}
+
 __device__ __forceinline__ f32x16_t mfma4(const u32x4_t& a, const u32x4_t& b, const f32x16_t& c)
 {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
@@ -144,7 +169,7 @@ struct RowOut {
 // (hh = lane / 32) of `head`, token t.  Rounds the row to bf16 (the packed row's values), then, in
 // produce mode, runs the producer arithmetic on it; returns the row's destination.  The norm
 // weights, RoPE coefficients and slot come from `in` (kInline false: fetched ahead by
-// epilogue_load) or are loaded here where they are used (kInline true: fewer live registers).
+// the caller) or are loaded here where they are used (kInline true: fewer live registers).
 template <bool kProduce, bool kInline>
 __device__ __forceinline__ RowOut epilogue_math(const Epi& e, int head, int32_t t, float (&a)[4][16], const EpiIn& in)
 {
@@ -250,6 +275,7 @@ __device__ __forceinline__ RowOut epilogue_math(const Epi& e, int head, int32_t 
 __device__ __forceinline__ void row_store_staged(const RowOut& o, const float (&a)[4][16], uint8_t* stage)
 {
     const int lane = threadIdx.x & 63;
+    const uint32_t st0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)stage;
     const int hh = lane >> 5, r = lane & 31;
     const uint32_t dlo = (uint32_t)reinterpret_cast<uintptr_t>(o.dst);
     const uint32_t dhi = (uint32_t)(reinterpret_cast<uintptr_t>(o.dst) >> 32);
@@ -261,13 +287,20 @@ __device__ __forceinline__ void row_store_staged(const RowOut& o, const float (&
                 *reinterpret_cast<uint32_t*>(stage + r * 128 + (((2 * b + (g >> 1)) ^ (r & 7)) * 16) + (g & 1) * 8 + 4 * hh) =
                     e4m3x4(a[b][4 * g] * o.m, a[b][4 * g + 1] * o.m, a[b][4 * g + 2] * o.m, a[b][4 * g + 3] * o.m);
         __builtin_amdgcn_wave_barrier();
+        // All reads and row addresses first, then the stores: no wait between the stores.
+        u32x4_t v[4];
+        uintptr_t d[4];
+        const int c = lane & 7;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int rr = 8 * i + (lane >> 3), c = lane & 7;
-            const uint4 v = *reinterpret_cast<const uint4*>(stage + rr * 128 + ((c ^ (rr & 7)) * 16));
-            const uintptr_t d = ((uintptr_t)(uint32_t)__shfl((int)dhi, rr) << 32) | (uint32_t)__shfl((int)dlo, rr);
-            if (d != 0) *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(d) + c * 16) = v;
+            const int rr = 8 * i + (lane >> 3);
+            v[i] = lds_read16(st0 + (uint32_t)(rr * 128 + ((c ^ (rr & 7)) * 16)));
+            d[i] = ((uintptr_t)(uint32_t)__shfl((int)dhi, rr) << 32) | (uint32_t)__shfl((int)dlo, rr);
         }
+        lgkm_wait4<0>(v);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (d[i] != 0) *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint8_t*>(d[i]) + c * 16) = v[i];
     } else {
 #pragma unroll
         for (int b = 0; b < 4; ++b)
@@ -276,13 +309,19 @@ __device__ __forceinline__ void row_store_staged(const RowOut& o, const float (&
                 *reinterpret_cast<uint2*>(stage + r * 256 + (((4 * b + g) ^ (r & 15)) * 16) + 8 * hh) =
                     make_uint2(bf16x2(a[b][4 * g], a[b][4 * g + 1]), bf16x2(a[b][4 * g + 2], a[b][4 * g + 3]));
         __builtin_amdgcn_wave_barrier();
+        u32x4_t v[8];
+        uintptr_t d[8];
+        const int c = lane & 15;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int rr = 4 * i + (lane >> 4), c = lane & 15;
-            const uint4 v = *reinterpret_cast<const uint4*>(stage + rr * 256 + ((c ^ (rr & 15)) * 16));
-            const uintptr_t d = ((uintptr_t)(uint32_t)__shfl((int)dhi, rr) << 32) | (uint32_t)__shfl((int)dlo, rr);
-            if (d != 0) *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(d) + c * 16) = v;
+            const int rr = 4 * i + (lane >> 4);
+            v[i] = lds_read16(st0 + (uint32_t)(rr * 256 + ((c ^ (rr & 15)) * 16)));
+            d[i] = ((uintptr_t)(uint32_t)__shfl((int)dhi, rr) << 32) | (uint32_t)__shfl((int)dlo, rr);
         }
+        lgkm_wait8<0>(v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (d[i] != 0) *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint8_t*>(d[i]) + c * 16) = v[i];
     }
     __builtin_amdgcn_wave_barrier();
 }
@@ -676,24 +715,6 @@ __device__ __forceinline__ uint32_t xcd_tile(uint32_t bid, uint32_t total)
     uint32_t prefix = 0;
     for (uint32_t i = 0; i < x; ++i) prefix += (total - i + 7u) >> 3;
     return prefix + (bid >> 3);
-}
-
-// One 16-byte LDS read at an immediate offset from addr (see lds_read16).
-template <int O>
-__device__ __forceinline__ u32x4_t lds_read16o(uint32_t addr)
-{
-    u32x4_t v;
-    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(O));
-    return v;
-}
-
-// Waits until at most N LDS reads are in flight, tied to eight fragments (see lgkm_wait).
-template <int N>
-__device__ __forceinline__ void lgkm_wait8(u32x4_t (&a)[8])
-{
-    asm volatile("s_waitcnt lgkmcnt(%8)"
-                 : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7])
-                 : "n"(N));
 }
 
 template <bool kProduce>
