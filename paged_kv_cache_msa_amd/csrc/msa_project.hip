@@ -168,9 +168,10 @@ struct RowOut {
 // One head's row for one token per lane pair: a[b][i] is feature 32 b + 8 (i / 4) + 4 hh + i % 4
 // (hh = lane / 32) of `head`, token t.  Rounds the row to bf16 (the packed row's values), then, in
 // produce mode, runs the producer arithmetic on it; returns the row's destination.  The norm
-// weights, RoPE coefficients and slot come from `in` (kInline false: fetched ahead by
-// the caller) or are loaded here where they are used (kInline true: fewer live registers).
-template <bool kProduce, bool kInline>
+// weights, RoPE coefficients and slot come from `in` (kInline 0: fetched ahead by the caller), are
+// loaded here where they are used (kInline 1: fewer live registers), or the norm weights are loaded
+// here and the rest comes from `in` (kInline 2).
+template <bool kProduce, int kInline>
 __device__ __forceinline__ RowOut epilogue_math(const Epi& e, int head, int32_t t, float (&a)[4][16], const EpiIn& in)
 {
     const int hh = (threadIdx.x & 63) >> 5;
@@ -211,7 +212,7 @@ __device__ __forceinline__ RowOut epilogue_math(const Epi& e, int head, int32_t 
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 float w4[4];
-                if (kInline) {
+                if (kInline != 0) {
                     const uint2 wv = *reinterpret_cast<const uint2*>(wp + 32 * b + 8 * g);
                     w4[0] = bf16_lo(wv.x); w4[1] = bf16_hi(wv.x); w4[2] = bf16_lo(wv.y); w4[3] = bf16_hi(wv.y);
                 } else {
@@ -230,7 +231,7 @@ __device__ __forceinline__ RowOut epilogue_math(const Epi& e, int head, int32_t 
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 float c[4], sn[4];
-                if (kInline) {
+                if (kInline == 1) {
                     const float4 c4 = *reinterpret_cast<const float4*>(cp + 32 * b + 8 * g);
                     const float4 s4 = *reinterpret_cast<const float4*>(sp + 32 * b + 8 * g);
                     c[0] = c4.x; c[1] = c4.y; c[2] = c4.z; c[3] = c4.w;
@@ -254,7 +255,7 @@ __device__ __forceinline__ RowOut epilogue_math(const Epi& e, int head, int32_t 
                                                     : e.iq_out + ((int64_t)t * e.hiq + (head - h_iq)) * kHeadDim);
         return o;
     }
-    const int64_t slot = kInline ? e.slots[t] : in.slot;
+    const int64_t slot = kInline == 1 ? e.slots[t] : in.slot;
     if (slot < 0) return o;
     const int64_t page = slot / e.page_size;
     if (page >= e.num_pages) return o;
@@ -262,7 +263,7 @@ __device__ __forceinline__ RowOut epilogue_math(const Epi& e, int head, int32_t 
     const int hl = st == kK ? head - h_k : st == kV ? head - h_v : head - h_ik;
     const int64_t elem = page * cd.sp + off * cd.st + (int64_t)hl * cd.sh;
     o.dst = cd.data + (o.fp8 ? elem : 2 * elem);
-    if (o.fp8) o.m = kInline ? inv_scale_of(cd.scale) : inv_scale(in.scale);
+    if (o.fp8) o.m = kInline == 1 ? inv_scale_of(cd.scale) : inv_scale(in.scale);
     return o;
 }
 
@@ -726,7 +727,8 @@ void project_tile_kernel(const TileArgs a)
     // measured).  After the last step the first 32 KiB stage the output rows.
     constexpr int kOp = kTile * 128;
     constexpr int kStage = 2 * kOp;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage];
+    // Produce mode: 32 KiB more, the output staging while the stages hold the RoPE coefficients.
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage + (kProduce ? 32768 : 0)];
     const uint32_t L = xcd_tile(blockIdx.x, (uint32_t)(a.n_tt * a.n_tf));
     const int tile_t = (int)(L / (uint32_t)a.n_tf);
     const int tile_f = (int)(L - (uint32_t)tile_t * (uint32_t)a.n_tf);
@@ -760,6 +762,28 @@ void project_tile_kernel(const TileArgs a)
         if (i < 8) __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, dst, 16, woff[j], k0 * 2, 0, 0);
         else __builtin_amdgcn_raw_ptr_buffer_load_lds(hr, dst, 16, hoff[j], k0 * 2, 0, 0);
     };
+    const int nk = a.K / kBK;
+    // Produce mode: the epilogue's RoPE coefficients, for the tile's 256 tokens, are copied into the
+    // stage buffers in place of the two stages past the last one: "stage" nk + h holds tokens
+    // 128 h .. 128 h + 127 (token u's 512-byte row: 16 chunks of cos, then 16 of sin, logical chunk
+    // c at position c ^ (u & 15), so that the 32 tokens of a fragment read spread over the banks).
+    // One copy per token for both heads, in whole rows, and started while the last products run.
+    // Tiles of V heads only skip them; the plain kernel copies nothing past the last stage.
+    const bool rope = kProduce && (stream_of(a.e, tile_f * 2) != kV ||
+                                   (tile_f * 2 + 1 < a.heads && stream_of(a.e, tile_f * 2 + 1) != kV));
+    // (The table pointers are copied out of the argument block first: selected per lane straight
+    // from it, each copy would load the pointer from memory and wait for it.)
+    const float* const cos_t = a.e.cos;
+    const float* const sin_t = a.e.sin;
+    const int32_t t_last = a.e.T - 1;
+    auto rope_copy = [&](int h, int i) {     // copy i (0..15) of the coefficients of tokens 128 h ..
+        if (!rope) return;
+        const int u = 128 * h + 2 * (i * 4 + wave) + (lane >> 5);
+        const int c = (lane & 31) ^ (u & 15);
+        const int32_t tl = min(t_base + u, t_last);
+        const float* src = (c < 16 ? cos_t : sin_t) + (int64_t)tl * kHalf + (c & 15) * 4;
+        __builtin_amdgcn_global_load_lds(src, (lds_void*)(&lds[((nk + h) & 1) * kStage + (i * 4 + wave) * 1024]), 16, 0, 0);
+    };
     // Fragment f of 16-column step ks: f < 4 is the head's 32-feature block f, else 32-token block f - 4.
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)&lds[0];
     const int sw = (r >> 1) & 7;
@@ -788,13 +812,17 @@ void project_tile_kernel(const TileArgs a)
     for (int b = 0; b < 4; ++b)
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) acc[b][tb] = f32x16_t{};
-    const int nk = a.K / kBK;
 #pragma unroll
     for (int i = 0; i < 16; ++i) copy(0, 0, i);
     __builtin_amdgcn_s_waitcnt(0x3f70);                          // vmcnt(0)
     __builtin_amdgcn_s_barrier();
+    if (nk > 1) {
 #pragma unroll
-    for (int i = 0; i < 12; ++i) copy(1, min(1, nk - 1) * kBK, i);
+        for (int i = 0; i < 12; ++i) copy(1, kBK, i);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 12; ++i) rope_copy(0, i);
+    }
     u32x4_t F0[8], F1[8];
 #pragma unroll
     for (int f = 0; f < 8; ++f) F0[f] = frag(0, 0, f);
@@ -806,12 +834,15 @@ void project_tile_kernel(const TileArgs a)
     //     wave's copies landed, every wave's reads of stage kt done);
     //   step 3, slots 4-11: stage kt + 1's first fragments; slots 4-15: the first twelve copy
     //     instructions of stage kt + 2, into the buffer the barrier released.
-    // Past the last stage the copies reload the last stage's columns (unused).  A stage's copies
+    // Past the last stage nothing is copied, or the RoPE coefficients (above).  A stage's copies
     // so go out about four steps before the wait for them (issued at the top of the stage before,
     // two and a half steps ahead, the kernel was 6% slower; all sixteen after the barrier, 3%).
-    for (int kt = 0; kt < nk; ++kt) {
+    // The loop body for stage kt: M = 0 while stage kt + 2 exists, 1 for kt = nk - 2, 2 for the last
+    // stage (the copies past the last stage are the RoPE coefficients' or none, without a branch
+    // among the products).
+    auto stage = [&](int kt, auto M) {
+        constexpr int m = decltype(M)::value;
         const int buf = kt & 1, nb = buf ^ 1;
-        const int k1 = min(kt + 1, nk - 1) * kBK, k2 = min(kt + 2, nk - 1) * kBK;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             u32x4_t (&C)[8] = (ks & 1) ? F1 : F0;
@@ -822,37 +853,107 @@ void project_tile_kernel(const TileArgs a)
                 acc[i >> 2][i & 3] = mfma4(C[i >> 2], C[4 + (i & 3)], acc[i >> 2][i & 3]);
                 if (ks < 3) {
                     if (i < 8) N[i] = frag(buf, ks + 1, i);
-                    if (ks == 0 && i < 4) copy(nb, k1, 12 + i);
+                    if (ks == 0 && i < 4) {
+                        if (m < 2) copy(nb, (kt + 1) * kBK, 12 + i);
+                        else rope_copy(0, 12 + i);
+                    }
                 } else {
                     if (i == 3) {
                         __builtin_amdgcn_s_waitcnt(0x3f70);      // vmcnt(0)
                         __builtin_amdgcn_s_barrier();
                     }
                     if (i >= 4 && i < 12) N[i - 4] = frag(nb, 0, i - 4);
-                    if (i >= 4) copy(buf, k2, i - 4);
+                    if (i >= 4) {
+                        if (m == 0) copy(buf, (kt + 2) * kBK, i - 4);
+                        else rope_copy(m - 1, i - 4);
+                    }
+                    if (m == 2 && i >= 12) rope_copy(1, i);     // all sixteen: no stage follows
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-    }
+    };
+    for (int kt = 0; kt < nk - 2; ++kt) stage(kt, std::integral_constant<int, 0>{});
+    if (nk > 1) stage(nk - 2, std::integral_constant<int, 1>{});
+    stage(nk - 1, std::integral_constant<int, 2>{});
     __builtin_amdgcn_s_waitcnt(0x3f70);                          // vmcnt(0): every copy landed
     lgkm_wait8<0>(F0);
     __syncthreads();
+    // The accumulators stay in the accumulator registers up to here: left free, the register
+    // allocator pulls some towards the epilogue's vector registers and then moves them inside the
+    // loop.
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) asm volatile("" : "+a"(acc[b][tb]));
 
     const int head = tile_f * 2 + wf;
-    if (head >= a.heads) return;
-    uint8_t* stage = &lds[0] + wave * 8192;
+    if constexpr (kProduce) {
+        const Epi& e = a.e;
+        const int st = stream_of(e, min(head, a.heads - 1));
+        EpiIn in;
+        in.scale = 1.0f;
+        if (st == kK || st == kV || st == kIK) {
+            const CacheDev& cd = e.cache[st == kK ? 0 : st == kV ? 1 : 2];
+            if (!cd.is_bf16) in.scale = *cd.scale;
+        }
+        __builtin_amdgcn_s_waitcnt(0x3f70);                      // vmcnt(0): this wave's coefficient copies
+        __syncthreads();                                         // everyone's
+        if (head >= a.heads) return;
+        uint8_t* stage = &lds[2 * kStage] + wave * 8192;
+        const uint32_t lds0e = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)&lds[0];
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-        float v[4][16];
+        for (int tb = 0; tb < 4; ++tb) {
+            float v[4][16];
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+            for (int b = 0; b < 4; ++b)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) v[b][i] = acc[b][tb][i];
-        const int32_t t = t_base + wt * 128 + tb * 32 + r;
-        EpiIn unused;
-        const RowOut o = epilogue_math<kProduce, true>(a.e, head, t, v, unused);
-        row_store_staged(o, v, stage);
+                for (int i = 0; i < 16; ++i) v[b][i] = acc[b][tb][i];
+            const int u = wt * 128 + tb * 32 + r;
+            const int32_t t = t_base + u;
+            const uint32_t cs0 = lds0e + (uint32_t)(((nk + wt) & 1) * kStage + (u & 127) * 512);
+            in.slot = (st == kK || st == kV || st == kIK) && t < e.T ? e.slots[t] : -1;
+            if (st != kV) {
+                const int hh = lane >> 5;
+                u32x4_t cv[8], sv[8];
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int cc = 8 * b + 2 * g + hh;
+                        cv[4 * b + g] = lds_read16(cs0 + (uint32_t)((cc ^ (u & 15)) * 16));
+                        sv[4 * b + g] = lds_read16(cs0 + (uint32_t)(((16 + cc) ^ (u & 15)) * 16));
+                    }
+                lgkm_wait8<0>(cv);
+                lgkm_wait8<0>(sv);
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x4_t c4 = __builtin_bit_cast(f32x4_t, cv[4 * b + g]);
+                        const f32x4_t s4 = __builtin_bit_cast(f32x4_t, sv[4 * b + g]);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) { in.c[b][4 * g + q] = c4[q]; in.s[b][4 * g + q] = s4[q]; }
+                    }
+            }
+            const RowOut o = epilogue_math<true, 2>(e, head, t, v, in);
+            row_store_staged(o, v, stage);
+        }
+    } else {
+        if (head >= a.heads) return;
+        uint8_t* stage = &lds[0] + wave * 8192;
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            float v[4][16];
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) v[b][i] = acc[b][tb][i];
+            const int32_t t = t_base + wt * 128 + tb * 32 + r;
+            EpiIn unused;
+            const RowOut o = epilogue_math<false, 1>(a.e, head, t, v, unused);
+            row_store_staged(o, v, stage);
+        }
     }
 }
 
