@@ -139,6 +139,19 @@ def test_project_produce_dyadic_matches_oracle(name):
     check(wl, d)
 
 
+@pytest.mark.parametrize("hidden", [64, 128, 192])
+def test_project_produce_tiled_short_hidden(hidden):
+    """The tiled kernel with one, two and three K stages: the RoPE coefficients of its epilogue are
+    copied in place of the stage copies past the last stage, which for these starts in the prologue
+    (one stage) or in the first stage (two)."""
+    wl = W.ragged(1300, seed=34, pad_frac=0.1)
+    h, w = W.with_projection(wl, hidden=hidden, seed=6, dyadic=True)
+    wl.x = oracle.project(h, w, num_threads=THREADS)
+    say(f"[gpu] msa_project_produce dyadic T={wl.T} hidden={hidden}")
+    d = fused(wl, h, w)
+    check(wl, d)
+
+
 def _rows(a, heads):
     return a.reshape(-1, 128) if heads else a.reshape(0, 128)
 
