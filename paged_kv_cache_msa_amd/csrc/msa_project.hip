@@ -724,7 +724,8 @@ void project_tile_kernel(const TileArgs a)
 {
     // Two stages, each [w | h] x 256 rows x 64 columns: 128-byte rows, chunk c of row r at position
     // c ^ ((r >> 1) & 7) (fragment reads of 32 rows at one chunk are free of bank conflicts;
-    // measured).  After the last step the first 32 KiB stage the output rows.
+    // measured).  After the last step the output rows are staged in the first 32 KiB (plain mode)
+    // or in the 32 KiB after the stages (produce mode, whose stages then hold RoPE coefficients).
     constexpr int kOp = kTile * 128;
     constexpr int kStage = 2 * kOp;
     // Produce mode: 32 KiB more, the output staging while the stages hold the RoPE coefficients.
