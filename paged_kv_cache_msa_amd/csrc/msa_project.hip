@@ -819,10 +819,10 @@ void project_tile_kernel(const TileArgs a)
     __builtin_amdgcn_s_barrier();
     if (nk > 1) {
 #pragma unroll
-        for (int i = 0; i < 12; ++i) copy(1, kBK, i);
+        for (int i = 0; i < 8; ++i) copy(1, kBK, i);
     } else {
 #pragma unroll
-        for (int i = 0; i < 12; ++i) rope_copy(0, i);
+        for (int i = 0; i < 8; ++i) rope_copy(0, i);
     }
     u32x4_t F0[8], F1[8];
 #pragma unroll
@@ -830,14 +830,16 @@ void project_tile_kernel(const TileArgs a)
     // Stage kt is in buffer kt & 1.  Each step issues its 16 products one per slot, and the other
     // instructions sit in fixed slots between them (sched_barrier keeps the order):
     //   steps 0-2, slots 0-7: the next step's fragments;
-    //   step 0, slots 0-3: the last four copy instructions of stage kt + 1;
+    //   step 0, even slots: the last eight copy instructions of stage kt + 1;
     //   step 3, slot 3: wait for this wave's copies of stage kt + 1, then the barrier (every
     //     wave's copies landed, every wave's reads of stage kt done);
-    //   step 3, slots 4-11: stage kt + 1's first fragments; slots 4-15: the first twelve copy
+    //   step 3, slots 4-11: stage kt + 1's first fragments and the first eight copy
     //     instructions of stage kt + 2, into the buffer the barrier released.
     // Past the last stage nothing is copied, or the RoPE coefficients (above).  A stage's copies
-    // so go out about four steps before the wait for them (issued at the top of the stage before,
-    // two and a half steps ahead, the kernel was 6% slower; all sixteen after the barrier, 3%).
+    // so go out three to four steps before the wait for them (issued at the top of the stage
+    // before, two and a half steps ahead, the kernel was 6% slower; all sixteen after the
+    // barrier, 3%; twelve after the barrier and four in step 0's first slots, 1.5%: the copies
+    // bunched in one step hold up the vector-memory issue).
     // The loop body for stage kt: M = 0 while stage kt + 2 exists, 1 for kt = nk - 2, 2 for the last
     // stage (the copies past the last stage are the RoPE coefficients' or none, without a branch
     // among the products).
@@ -854,21 +856,22 @@ void project_tile_kernel(const TileArgs a)
                 acc[i >> 2][i & 3] = mfma4(C[i >> 2], C[4 + (i & 3)], acc[i >> 2][i & 3]);
                 if (ks < 3) {
                     if (i < 8) N[i] = frag(buf, ks + 1, i);
-                    if (ks == 0 && i < 4) {
-                        if (m < 2) copy(nb, (kt + 1) * kBK, 12 + i);
-                        else rope_copy(0, 12 + i);
+                    if (ks == 0 && (i & 1) == 0) {
+                        if (m < 2) copy(nb, (kt + 1) * kBK, 8 + i / 2);
+                        else rope_copy(0, 8 + i / 2);
                     }
                 } else {
                     if (i == 3) {
                         __builtin_amdgcn_s_waitcnt(0x3f70);      // vmcnt(0)
                         __builtin_amdgcn_s_barrier();
                     }
-                    if (i >= 4 && i < 12) N[i - 4] = frag(nb, 0, i - 4);
-                    if (i >= 4) {
+                    if (i >= 4 && i < 12) {
+                        N[i - 4] = frag(nb, 0, i - 4);
                         if (m == 0) copy(buf, (kt + 2) * kBK, i - 4);
-                        else rope_copy(m - 1, i - 4);
+                        if (m == 1) rope_copy(0, i - 4);
                     }
-                    if (m == 2 && i >= 12) rope_copy(1, i);     // all sixteen: no stage follows
+                    if (m == 2 && i >= 4) rope_copy(1, i - 4);  // all sixteen: no stage follows
+                    if (m == 2 && i >= 12) rope_copy(1, i);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
