@@ -53,6 +53,22 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d)
     return w & ~clear;
 }
 
+// Four binary32 -> E4M3 with the conversion instruction alone: round-to-nearest-even, equal to
+// e4m3x4 wherever no byte comes out as a NaN code (a NaN input, or a magnitude of 464 or more:
+// the instruction writes a NaN code there instead of saturating).
+__device__ __forceinline__ uint32_t e4m3x4_rne(float a, float b, float c, float d)
+{
+    const uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+}
+
+// Nonzero iff some byte of w is an E4M3 NaN code (its low seven bits all set): adding 1 to the
+// low seven bits of each byte carries into bit 7 exactly there, never into the next byte.
+__device__ __forceinline__ uint32_t e4m3_nan_bytes(uint32_t w)
+{
+    return ((w & 0x7f7f7f7fu) + 0x01010101u) & 0x80808080u;
+}
+
 // Dequantisation scale -> quantisation multiplier, binary32 division rounded once.
 __device__ __forceinline__ float inv_scale(float scale) { return 1.0f / scale; }
 __device__ __forceinline__ float inv_scale_of(const float* scale) { return inv_scale(*scale); }

@@ -142,11 +142,13 @@ struct Epi {
 };
 
 // The epilogue's per-lane inputs for one (head, token): the head's norm weights at this lane's 64
-// features, the token's RoPE coefficients at this lane's 32 frequencies, and its cache slot.
+// features (bf16 pairs as loaded: w[b][g] holds features 32 b + 8 g + 4 hh .. + 3), where the
+// token's RoPE coefficients sit in LDS (cs: its 512-byte row, 16 chunks of cos then 16 of sin,
+// logical chunk c at position c ^ sw), and its cache slot.
 struct EpiIn {
-    float w[4][16];
-    float c[2][16];
-    float s[2][16];
+    uint2 w[4][4];
+    uint32_t cs;
+    int sw;
     int64_t slot;
     float scale;               // fp8 cache rows: the dequantisation scale (1 otherwise)
 };
@@ -167,11 +169,9 @@ struct RowOut {
 
 // One head's row for one token per lane pair: a[b][i] is feature 32 b + 8 (i / 4) + 4 hh + i % 4
 // (hh = lane / 32) of `head`, token t.  Rounds the row to bf16 (the packed row's values), then, in
-// produce mode, runs the producer arithmetic on it; returns the row's destination.  The norm
-// weights, RoPE coefficients and slot come from `in` (kInline 0: fetched ahead by the caller), are
-// loaded here where they are used (kInline 1: fewer live registers), or the norm weights are loaded
-// here and the rest comes from `in` (kInline 2).
-template <bool kProduce, int kInline>
+// produce mode, runs the producer arithmetic on it with the norm weights, RoPE coefficients, slot
+// and scale in `in` (fetched ahead by the caller); returns the row's destination.
+template <bool kProduce>
 __device__ __forceinline__ RowOut epilogue_math(const Epi& e, int head, int32_t t, float (&a)[4][16], const EpiIn& in)
 {
     const int hh = (threadIdx.x & 63) >> 5;
@@ -198,48 +198,54 @@ __device__ __forceinline__ RowOut epilogue_math(const Epi& e, int head, int32_t 
     // relies on it), whatever the token.
     o.fp8 = cache_row && !cd.is_bf16;
     if (st != kV) {
-        // RMSNorm: binary64 sum of squares over the lane's 64 features plus the partner lane's.
-        double ss = 0.0;
+        // RMSNorm: binary64 sum of squares over the lane's 64 features (two chains of 32, for the
+        // latency) plus the partner lane's.  The squares of bf16 values are exact in binary64, and
+        // so is every partial sum while the largest square is within about 2^30 of the smallest
+        // nonzero one; past that the order of the additions moves only the last bits of the
+        // binary64 sum, far below the binary32 scale taken from it.
+        double ss0 = 0.0, ss1 = 0.0;
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) ss = __builtin_fma((double)a[b][i], (double)a[b][i], ss);
+            for (int i = 0; i < 16; ++i) {
+                ss0 = __builtin_fma((double)a[b][i], (double)a[b][i], ss0);
+                ss1 = __builtin_fma((double)a[b + 2][i], (double)a[b + 2][i], ss1);
+            }
+        double ss = ss0 + ss1;
         ss += __shfl_xor(ss, 32);
         const float r = rms_from_ss(ss, e.eps);
-        const uint16_t* wp = e.w[st == kQ ? 0 : st == kK ? 1 : st == kIQ ? 2 : 3] + 4 * hh;
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                float w4[4];
-                if (kInline != 0) {
-                    const uint2 wv = *reinterpret_cast<const uint2*>(wp + 32 * b + 8 * g);
-                    w4[0] = bf16_lo(wv.x); w4[1] = bf16_hi(wv.x); w4[2] = bf16_lo(wv.y); w4[3] = bf16_hi(wv.y);
-                } else {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) w4[q] = in.w[b][4 * g + q];
-                }
-#pragma unroll
-                for (int q = 0; q < 4; ++q) a[b][4 * g + q] = (a[b][4 * g + q] * r) * w4[q];
-            }
-        // RoPE, neox rotate-half: frequency f < 64 pairs feature f (block b) with f + 64 (block b + 2).
-        const int32_t tl = tok ? t : e.T - 1;
-        const float* cp = e.cos + (int64_t)tl * kHalf + 4 * hh;
-        const float* sp = e.sin + (int64_t)tl * kHalf + 4 * hh;
+        // This lane's 32 frequencies 32 b + 8 g + 4 hh .. + 3 (b < 2) of cos and sin, read while the
+        // norm runs.
+        u32x4_t cv[8], sv[8];
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                float c[4], sn[4];
-                if (kInline == 1) {
-                    const float4 c4 = *reinterpret_cast<const float4*>(cp + 32 * b + 8 * g);
-                    const float4 s4 = *reinterpret_cast<const float4*>(sp + 32 * b + 8 * g);
-                    c[0] = c4.x; c[1] = c4.y; c[2] = c4.z; c[3] = c4.w;
-                    sn[0] = s4.x; sn[1] = s4.y; sn[2] = s4.z; sn[3] = s4.w;
-                } else {
+                const int cc = 8 * b + 2 * g + hh;
+                cv[4 * b + g] = lds_read16(in.cs + (uint32_t)((cc ^ in.sw) * 16));
+                sv[4 * b + g] = lds_read16(in.cs + (uint32_t)(((16 + cc) ^ in.sw) * 16));
+            }
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) { c[q] = in.c[b][4 * g + q]; sn[q] = in.s[b][4 * g + q]; }
-                }
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                uint2 wv = in.w[b][g];
+                // (Opaque per token block: otherwise the unpacked weights are shared by the four
+                // blocks and stay live across them, 64 registers where 32 suffice.)
+                asm volatile("" : "+v"(wv.x), "+v"(wv.y));
+                const float w4[4] = {bf16_lo(wv.x), bf16_hi(wv.x), bf16_lo(wv.y), bf16_hi(wv.y)};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) a[b][4 * g + q] = (a[b][4 * g + q] * r) * w4[q];
+            }
+        // RoPE, neox rotate-half: frequency f < 64 pairs feature f (block b) with f + 64 (block b + 2).
+        lgkm_wait8<0>(cv);
+        lgkm_wait8<0>(sv);
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4_t c = __builtin_bit_cast(f32x4_t, cv[4 * b + g]);
+                const f32x4_t sn = __builtin_bit_cast(f32x4_t, sv[4 * b + g]);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int i = 4 * g + q;
@@ -255,7 +261,7 @@ __device__ __forceinline__ RowOut epilogue_math(const Epi& e, int head, int32_t 
                                                     : e.iq_out + ((int64_t)t * e.hiq + (head - h_iq)) * kHeadDim);
         return o;
     }
-    const int64_t slot = kInline == 1 ? e.slots[t] : in.slot;
+    const int64_t slot = in.slot;
     if (slot < 0) return o;
     const int64_t page = slot / e.page_size;
     if (page >= e.num_pages) return o;
@@ -263,7 +269,7 @@ __device__ __forceinline__ RowOut epilogue_math(const Epi& e, int head, int32_t 
     const int hl = st == kK ? head - h_k : st == kV ? head - h_v : head - h_ik;
     const int64_t elem = page * cd.sp + off * cd.st + (int64_t)hl * cd.sh;
     o.dst = cd.data + (o.fp8 ? elem : 2 * elem);
-    if (o.fp8) o.m = kInline == 1 ? inv_scale_of(cd.scale) : inv_scale(in.scale);
+    if (o.fp8) o.m = inv_scale(in.scale);
     return o;
 }
 
@@ -281,12 +287,29 @@ __device__ __forceinline__ void row_store_staged(const RowOut& o, const float (&
     const uint32_t dlo = (uint32_t)reinterpret_cast<uintptr_t>(o.dst);
     const uint32_t dhi = (uint32_t)(reinterpret_cast<uintptr_t>(o.dst) >> 32);
     if (o.fp8) {
+        // The plain conversion first; only where some lane produced a NaN code (a NaN, or a value
+        // of magnitude 464 or more, which it does not saturate) is the block converted again with
+        // the saturating, sign-keeping conversion.  Elsewhere the two agree.
+        uint32_t q[4][4], nan_bytes = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                q[b][g] = e4m3x4_rne(a[b][4 * g] * o.m, a[b][4 * g + 1] * o.m, a[b][4 * g + 2] * o.m, a[b][4 * g + 3] * o.m);
+                nan_bytes |= e4m3_nan_bytes(q[b][g]);
+            }
+        if (__builtin_amdgcn_ballot_w64(nan_bytes != 0) != 0) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    q[b][g] = e4m3x4(a[b][4 * g] * o.m, a[b][4 * g + 1] * o.m, a[b][4 * g + 2] * o.m, a[b][4 * g + 3] * o.m);
+        }
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
             for (int g = 0; g < 4; ++g)
-                *reinterpret_cast<uint32_t*>(stage + r * 128 + (((2 * b + (g >> 1)) ^ (r & 7)) * 16) + (g & 1) * 8 + 4 * hh) =
-                    e4m3x4(a[b][4 * g] * o.m, a[b][4 * g + 1] * o.m, a[b][4 * g + 2] * o.m, a[b][4 * g + 3] * o.m);
+                *reinterpret_cast<uint32_t*>(stage + r * 128 + (((2 * b + (g >> 1)) ^ (r & 7)) * 16) + (g & 1) * 8 + 4 * hh) = q[b][g];
         __builtin_amdgcn_wave_barrier();
         // All reads and row addresses first, then the stores: no wait between the stores.
         u32x4_t v[4];
@@ -879,6 +902,27 @@ void project_tile_kernel(const TileArgs a)
     };
     for (int kt = 0; kt < nk - 2; ++kt) stage(kt, std::integral_constant<int, 0>{});
     if (nk > 1) stage(nk - 2, std::integral_constant<int, 1>{});
+    // Produce mode: the epilogue's norm weights (this lane's 64 features of the head, as bf16 pairs)
+    // and the cache slots of its four 32-token blocks are loaded before the last stage, whose
+    // products cover their latency.
+    const int head = tile_f * 2 + wf;
+    const int st = kProduce ? stream_of(a.e, min(head, a.heads - 1)) : kQ;
+    const bool cache_row = st == kK || st == kV || st == kIK;
+    EpiIn in;
+    int64_t slot4[4];
+    if constexpr (kProduce) {
+        const Epi& e = a.e;
+        in.scale = 1.0f;
+        if (cache_row) {
+            const CacheDev& cd = e.cache[st == kK ? 0 : st == kV ? 1 : 2];
+            if (!cd.is_bf16) in.scale = *cd.scale;
+        }
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            const int32_t t = t_base + wt * 128 + tb * 32 + r;
+            slot4[tb] = cache_row && t < e.T ? e.slots[t] : -1;
+        }
+    }
     stage(nk - 1, std::integral_constant<int, 2>{});
     __builtin_amdgcn_s_waitcnt(0x3f70);                          // vmcnt(0): every copy landed
     lgkm_wait8<0>(F0);
@@ -891,15 +935,14 @@ void project_tile_kernel(const TileArgs a)
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) asm volatile("" : "+a"(acc[b][tb]));
 
-    const int head = tile_f * 2 + wf;
     if constexpr (kProduce) {
         const Epi& e = a.e;
-        const int st = stream_of(e, min(head, a.heads - 1));
-        EpiIn in;
-        in.scale = 1.0f;
-        if (st == kK || st == kV || st == kIK) {
-            const CacheDev& cd = e.cache[st == kK ? 0 : st == kV ? 1 : 2];
-            if (!cd.is_bf16) in.scale = *cd.scale;
+        if (st != kV) {
+            const uint16_t* wp = e.w[st == kQ ? 0 : st == kK ? 1 : st == kIQ ? 2 : 3] + 4 * hh;
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) in.w[b][g] = *reinterpret_cast<const uint2*>(wp + 32 * b + 8 * g);
         }
         __builtin_amdgcn_s_waitcnt(0x3f70);                      // vmcnt(0): this wave's coefficient copies
         __syncthreads();                                         // everyone's
@@ -910,37 +953,19 @@ void project_tile_kernel(const TileArgs a)
         for (int tb = 0; tb < 4; ++tb) {
             float v[4][16];
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
+            for (int b = 0; b < 4; ++b) {
+                // (Ordered after the block before: read early, the blocks' values would all be
+                // live at once.)
+                asm volatile("" : "+a"(acc[b][tb]));
 #pragma unroll
                 for (int i = 0; i < 16; ++i) v[b][i] = acc[b][tb][i];
+            }
             const int u = wt * 128 + tb * 32 + r;
             const int32_t t = t_base + u;
-            const uint32_t cs0 = lds0e + (uint32_t)(((nk + wt) & 1) * kStage + (u & 127) * 512);
-            in.slot = (st == kK || st == kV || st == kIK) && t < e.T ? e.slots[t] : -1;
-            if (st != kV) {
-                const int hh = lane >> 5;
-                u32x4_t cv[8], sv[8];
-#pragma unroll
-                for (int b = 0; b < 2; ++b)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int cc = 8 * b + 2 * g + hh;
-                        cv[4 * b + g] = lds_read16(cs0 + (uint32_t)((cc ^ (u & 15)) * 16));
-                        sv[4 * b + g] = lds_read16(cs0 + (uint32_t)(((16 + cc) ^ (u & 15)) * 16));
-                    }
-                lgkm_wait8<0>(cv);
-                lgkm_wait8<0>(sv);
-#pragma unroll
-                for (int b = 0; b < 2; ++b)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const f32x4_t c4 = __builtin_bit_cast(f32x4_t, cv[4 * b + g]);
-                        const f32x4_t s4 = __builtin_bit_cast(f32x4_t, sv[4 * b + g]);
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) { in.c[b][4 * g + q] = c4[q]; in.s[b][4 * g + q] = s4[q]; }
-                    }
-            }
-            const RowOut o = epilogue_math<true, 2>(e, head, t, v, in);
+            in.cs = lds0e + (uint32_t)(((nk + wt) & 1) * kStage + (u & 127) * 512);
+            in.sw = u & 15;
+            in.slot = slot4[tb];
+            const RowOut o = epilogue_math<true>(e, head, t, v, in);
             row_store_staged(o, v, stage);
         }
     } else {
@@ -954,8 +979,7 @@ void project_tile_kernel(const TileArgs a)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) v[b][i] = acc[b][tb][i];
             const int32_t t = t_base + wt * 128 + tb * 32 + r;
-            EpiIn unused;
-            const RowOut o = epilogue_math<false, 1>(a.e, head, t, v, unused);
+            const RowOut o = epilogue_math<false>(a.e, head, t, v, in);
             row_store_staged(o, v, stage);
         }
     }
