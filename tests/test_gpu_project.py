@@ -152,6 +152,28 @@ def test_project_produce_tiled_short_hidden(hidden):
     check(wl, d)
 
 
+def test_project_produce_tiled_special_values():
+    """The tiled kernel's fp8 conversion on values it does not saturate by itself: 40 tokens' hidden
+    states scaled by 64 (value rows past the fp8 range, so saturated to +-448), one token with a NaN
+    and one with an infinity in its hidden state (NaN and infinite rows through RMSNorm, RoPE and
+    the fp8 and bf16 encodings).  Dyadic inputs, so the finite rows have one correct answer."""
+    wl = W.ragged(1300, seed=35, pad_frac=0.1)
+    h, w = W.with_projection(wl, seed=7, dyadic=True)
+    rng = np.random.default_rng(35)
+    rows = rng.choice(wl.T, 42, replace=False)
+    hf = H.bf16_bits_to_f32(h)
+    hf[rows[:40]] *= np.float32(64.0)
+    h = W.to_bf16_bits(hf)
+    h[rows[40], 5] = 0x7FC0                                   # NaN
+    h[rows[41], 7] = 0x7F80                                   # +infinity
+    wl.x = oracle.project(h, w, num_threads=THREADS)
+    xv = H.bf16_bits_to_f32(wl.x[:, (wl.hq + wl.hkv) * 128:(wl.hq + 2 * wl.hkv) * 128])
+    assert np.nanmax(np.abs(xv[np.isfinite(xv)])) > 2 * 448, "no value row reaches past the fp8 range"
+    say(f"[gpu] msa_project_produce special values T={wl.T}: scaled tokens, NaN token {rows[40]}, inf token {rows[41]}")
+    d = fused(wl, h, w)
+    check(wl, d)
+
+
 def _rows(a, heads):
     return a.reshape(-1, 128) if heads else a.reshape(0, 128)
 
