@@ -732,13 +732,29 @@ struct TileArgs {
 };
 
 // Block index -> linear tile index such that each XCD (blocks are dealt to the 8 XCDs round-robin)
-// receives a contiguous range of tiles; tiles are numbered feature-tile fastest.
+// receives a contiguous range of tiles.
 __device__ __forceinline__ uint32_t xcd_tile(uint32_t bid, uint32_t total)
 {
     const uint32_t x = bid & 7u;
     uint32_t prefix = 0;
     for (uint32_t i = 0; i < x; ++i) prefix += (total - i + 7u) >> 3;
     return prefix + (bid >> 3);
+}
+
+// Linear tile index -> (token tile, feature tile): blocks of four token tiles by every feature
+// tile, token tile fastest within a block.  The 32 work-groups an XCD runs at once then cover
+// 4 token tiles x 8 feature tiles of the 2,944-column projection, 12 distinct operand tiles per
+// stage for its L2, where numbering feature tiles fastest covers about 2.7 x 12, 14.7 of them
+// (measured 2% faster; blocks of two or eight token tiles were in between).  A bijection for any
+// tile counts (the last block may hold fewer token tiles).
+__device__ __forceinline__ void tile_of(uint32_t L, int n_tt, int n_tf, int& tile_t, int& tile_f)
+{
+    constexpr int kBlockT = 4;
+    const int per = kBlockT * n_tf;
+    const int blk = (int)L / per, rr = (int)L - blk * per;
+    const int t0 = kBlockT * blk, nt = min(kBlockT, n_tt - t0);
+    tile_t = t0 + rr % nt;
+    tile_f = rr / nt;
 }
 
 template <bool kProduce>
@@ -753,9 +769,8 @@ void project_tile_kernel(const TileArgs a)
     constexpr int kStage = 2 * kOp;
     // Produce mode: 32 KiB more, the output staging while the stages hold the RoPE coefficients.
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage + (kProduce ? 32768 : 0)];
-    const uint32_t L = xcd_tile(blockIdx.x, (uint32_t)(a.n_tt * a.n_tf));
-    const int tile_t = (int)(L / (uint32_t)a.n_tf);
-    const int tile_f = (int)(L - (uint32_t)tile_t * (uint32_t)a.n_tf);
+    int tile_t, tile_f;
+    tile_of(xcd_tile(blockIdx.x, (uint32_t)(a.n_tt * a.n_tf)), a.n_tt, a.n_tf, tile_t, tile_f);
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hh = lane >> 5, r = lane & 31;
     const int wf = wave & 1, wt = wave >> 1;            // head of the tile, 128-token half
