@@ -350,6 +350,30 @@ __device__ __forceinline__ void row_store_staged(const RowOut& o, const float (&
     __builtin_amdgcn_wave_barrier();
 }
 
+// Stores the bf16 rows of a 32-token block (lane l holds part of token l % 32's row, as above)
+// straight from the registers: the two lanes of a token swap halves of their pieces
+// (v_permlane32_swap) so that each lane holds 16 contiguous bytes, features 32 b + 8 g .. + 7 for
+// g = 2 p + hh, and stores them at its own token's row (o.dst; nullptr: no store).  A store
+// instruction writes 32 bytes of 32 rows; the eight of a block complete every row.
+__device__ __forceinline__ void row_store_bf16_direct(const RowOut& o, const float (&a)[4][16])
+{
+    const int hh = (threadIdx.x & 63) >> 5;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            uint32_t ax = bf16x2(a[b][8 * p], a[b][8 * p + 1]), ay = bf16x2(a[b][8 * p + 2], a[b][8 * p + 3]);
+            uint32_t bx = bf16x2(a[b][8 * p + 4], a[b][8 * p + 5]), by = bf16x2(a[b][8 * p + 6], a[b][8 * p + 7]);
+            // lanes 0-31 keep a and take the partner's a as b; lanes 32-63 take the partner's b as a
+            const auto sx = __builtin_amdgcn_permlane32_swap(ax, bx, false, false);
+            const auto sy = __builtin_amdgcn_permlane32_swap(ay, by, false, false);
+            if (o.dst != nullptr) {
+                u32x4_t v = {sx[0], sy[0], sx[1], sy[1]};
+                *reinterpret_cast<u32x4_t*>(o.dst + (32 * b + 8 * (2 * p + hh)) * 2) = v;
+            }
+        }
+}
+
 // ------------------------------------------------------------------ split-K kernel (<= 1,024 tokens)
 
 // Workspace of the split-K kernel: a 256-byte header (word 1: error bits), then the partial sums.
@@ -981,7 +1005,10 @@ void project_tile_kernel(const TileArgs a)
             in.sw = u & 15;
             in.slot = slot4[tb];
             const RowOut o = epilogue_math<true>(e, head, t, v, in);
-            row_store_staged(o, v, stage);
+            // bf16 rows (Q, index-Q, bf16 caches) from the registers: no LDS round trip and no
+            // exchange of row addresses (1% faster than staging them).
+            if (o.fp8) row_store_staged(o, v, stage);
+            else row_store_bf16_direct(o, v);
         }
     } else {
         if (head >= a.heads) return;
@@ -995,6 +1022,8 @@ void project_tile_kernel(const TileArgs a)
                 for (int i = 0; i < 16; ++i) v[b][i] = acc[b][tb][i];
             const int32_t t = t_base + wt * 128 + tb * 32 + r;
             const RowOut o = epilogue_math<false>(a.e, head, t, v, in);
+            // (Staged: stored straight from the registers, 32 bytes of 32 rows per instruction,
+            // the plain kernel's output bursts were 2% slower.)
             row_store_staged(o, v, stage);
         }
     }
