@@ -110,13 +110,6 @@ __device__ __forceinline__ void lgkm_wait8(u32x4_t (&a)[8])
                  : "n"(N));
 }
 
-// Waits until at most N LDS reads are in flight, tied to four fragments (see lgkm_wait).
-template <int N>
-__device__ __forceinline__ void lgkm_wait4(u32x4_t (&a)[4])
-{
-    asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]) : "n"(N));
-}
-
 __device__ __forceinline__ f32x16_t mfma4(const u32x4_t& a, const u32x4_t& b, const f32x16_t& c)
 {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
@@ -194,8 +187,8 @@ __device__ __forceinline__ RowOut epilogue_math(const Epi& e, int head, int32_t 
     const int st = stream_of(e, head);
     const bool cache_row = st == kK || st == kV || st == kIK;
     const CacheDev& cd = e.cache[st == kK ? 0 : st == kV ? 1 : 2];
-    // The row format depends on the head only, so it is uniform over the wave (row_store_staged
-    // relies on it), whatever the token.
+    // The row format depends on the head only, so it is uniform over the wave (the row stores
+    // rely on it), whatever the token.
     o.fp8 = cache_row && !cd.is_bf16;
     if (st != kV) {
         // RMSNorm: binary64 sum of squares over the lane's 64 features (two chains of 32, for the
@@ -273,12 +266,10 @@ __device__ __forceinline__ RowOut epilogue_math(const Epi& e, int head, int32_t 
     return o;
 }
 
-// Stores the rows of a 32-token block (lane l holds part of token l % 32's row, as above) through
-// this wave's 8 KiB of LDS: every lane first writes its pieces into the row-major block, then each
-// lane stores 16 contiguous bytes of one row, so that a store instruction writes whole rows.  In
-// the staging block the 16-byte chunk c of row r sits at position c ^ (r & 15) (256-byte rows) or
-// c ^ (r & 7) (128-byte rows).  o.fp8 must be uniform over the wave (one head): every lane takes
-// part in storing every row of the block.
+// Stores the bf16 rows of a 32-token block (lane l holds part of token l % 32's row, as above)
+// through this wave's 8 KiB of LDS: every lane first writes its pieces into the row-major block,
+// then each lane stores 16 contiguous bytes of one row, so that a store instruction writes whole
+// rows.  In the staging block the 16-byte chunk c of row r sits at position c ^ (r & 15).
 __device__ __forceinline__ void row_store_staged(const RowOut& o, const float (&a)[4][16], uint8_t* stage)
 {
     const int lane = threadIdx.x & 63;
@@ -286,67 +277,27 @@ __device__ __forceinline__ void row_store_staged(const RowOut& o, const float (&
     const int hh = lane >> 5, r = lane & 31;
     const uint32_t dlo = (uint32_t)reinterpret_cast<uintptr_t>(o.dst);
     const uint32_t dhi = (uint32_t)(reinterpret_cast<uintptr_t>(o.dst) >> 32);
-    if (o.fp8) {
-        // The plain conversion first; only where some lane produced a NaN code (a NaN, or a value
-        // of magnitude 464 or more, which it does not saturate) is the block converted again with
-        // the saturating, sign-keeping conversion.  Elsewhere the two agree.
-        uint32_t q[4][4], nan_bytes = 0;
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                q[b][g] = e4m3x4_rne(a[b][4 * g] * o.m, a[b][4 * g + 1] * o.m, a[b][4 * g + 2] * o.m, a[b][4 * g + 3] * o.m);
-                nan_bytes |= e4m3_nan_bytes(q[b][g]);
-            }
-        if (__builtin_amdgcn_ballot_w64(nan_bytes != 0) != 0) {
+        for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<uint2*>(stage + r * 256 + (((4 * b + g) ^ (r & 15)) * 16) + 8 * hh) =
+                make_uint2(bf16x2(a[b][4 * g], a[b][4 * g + 1]), bf16x2(a[b][4 * g + 2], a[b][4 * g + 3]));
+    __builtin_amdgcn_wave_barrier();
+    // All reads and row addresses first, then the stores: no wait between the stores.
+    u32x4_t v[8];
+    uintptr_t d[8];
+    const int c = lane & 15;
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    q[b][g] = e4m3x4(a[b][4 * g] * o.m, a[b][4 * g + 1] * o.m, a[b][4 * g + 2] * o.m, a[b][4 * g + 3] * o.m);
-        }
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-                *reinterpret_cast<uint32_t*>(stage + r * 128 + (((2 * b + (g >> 1)) ^ (r & 7)) * 16) + (g & 1) * 8 + 4 * hh) = q[b][g];
-        __builtin_amdgcn_wave_barrier();
-        // All reads and row addresses first, then the stores: no wait between the stores.
-        u32x4_t v[4];
-        uintptr_t d[4];
-        const int c = lane & 7;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int rr = 8 * i + (lane >> 3);
-            v[i] = lds_read16(st0 + (uint32_t)(rr * 128 + ((c ^ (rr & 7)) * 16)));
-            d[i] = ((uintptr_t)(uint32_t)__shfl((int)dhi, rr) << 32) | (uint32_t)__shfl((int)dlo, rr);
-        }
-        lgkm_wait4<0>(v);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (d[i] != 0) *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint8_t*>(d[i]) + c * 16) = v[i];
-    } else {
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-                *reinterpret_cast<uint2*>(stage + r * 256 + (((4 * b + g) ^ (r & 15)) * 16) + 8 * hh) =
-                    make_uint2(bf16x2(a[b][4 * g], a[b][4 * g + 1]), bf16x2(a[b][4 * g + 2], a[b][4 * g + 3]));
-        __builtin_amdgcn_wave_barrier();
-        u32x4_t v[8];
-        uintptr_t d[8];
-        const int c = lane & 15;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int rr = 4 * i + (lane >> 4);
-            v[i] = lds_read16(st0 + (uint32_t)(rr * 256 + ((c ^ (rr & 15)) * 16)));
-            d[i] = ((uintptr_t)(uint32_t)__shfl((int)dhi, rr) << 32) | (uint32_t)__shfl((int)dlo, rr);
-        }
-        lgkm_wait8<0>(v);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            if (d[i] != 0) *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint8_t*>(d[i]) + c * 16) = v[i];
+    for (int i = 0; i < 8; ++i) {
+        const int rr = 4 * i + (lane >> 4);
+        v[i] = lds_read16(st0 + (uint32_t)(rr * 256 + ((c ^ (rr & 15)) * 16)));
+        d[i] = ((uintptr_t)(uint32_t)__shfl((int)dhi, rr) << 32) | (uint32_t)__shfl((int)dlo, rr);
     }
+    lgkm_wait8<0>(v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        if (d[i] != 0) *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint8_t*>(d[i]) + c * 16) = v[i];
     __builtin_amdgcn_wave_barrier();
 }
 
@@ -372,6 +323,43 @@ __device__ __forceinline__ void row_store_bf16_direct(const RowOut& o, const flo
                 *reinterpret_cast<u32x4_t*>(o.dst + (32 * b + 8 * (2 * p + hh)) * 2) = v;
             }
         }
+}
+
+// Stores the fp8 rows of a 32-token block straight from the registers: encodes the lane's 64
+// values (e4m3 of value * o.m), then the two lanes of a token exchange words (v_permlane32_swap)
+// so that for each 32-feature block b lane hh holds the 16 contiguous bytes 32 b + 16 hh .. + 15,
+// stored at its own token's row (o.dst; nullptr: no store).  A store instruction writes 32 bytes
+// of 32 rows; the four of a block complete every row.
+__device__ __forceinline__ void row_store_fp8_direct(const RowOut& o, const float (&a)[4][16])
+{
+    uint32_t q[4][4], nan_bytes = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            q[b][g] = e4m3x4_rne(a[b][4 * g] * o.m, a[b][4 * g + 1] * o.m, a[b][4 * g + 2] * o.m, a[b][4 * g + 3] * o.m);
+            nan_bytes |= e4m3_nan_bytes(q[b][g]);
+        }
+    if (__builtin_amdgcn_ballot_w64(nan_bytes != 0) != 0) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                q[b][g] = e4m3x4(a[b][4 * g] * o.m, a[b][4 * g + 1] * o.m, a[b][4 * g + 2] * o.m, a[b][4 * g + 3] * o.m);
+    }
+    const int hh = (threadIdx.x & 63) >> 5;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        // q[b][g] holds features 32 b + 8 g + 4 hh .. + 3.  Lanes 0-31 end with (own g0, partner's g0,
+        // own g1, partner's g1) = features 32 b .. + 15; lanes 32-63 with (partner's g2, own g2,
+        // partner's g3, own g3) = features 32 b + 16 .. + 31.
+        const auto s0 = __builtin_amdgcn_permlane32_swap(q[b][0], q[b][2], false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(q[b][1], q[b][3], false, false);
+        if (o.dst != nullptr) {
+            u32x4_t v = {s0[0], s0[1], s1[0], s1[1]};
+            *reinterpret_cast<u32x4_t*>(o.dst + 32 * b + 16 * hh) = v;
+        }
+    }
 }
 
 // ------------------------------------------------------------------ split-K kernel (<= 1,024 tokens)
@@ -787,12 +775,11 @@ void project_tile_kernel(const TileArgs a)
 {
     // Two stages, each [w | h] x 256 rows x 64 columns: 128-byte rows, chunk c of row r at position
     // c ^ ((r >> 1) & 7) (fragment reads of 32 rows at one chunk are free of bank conflicts;
-    // measured).  After the last step the output rows are staged in the first 32 KiB (plain mode)
-    // or in the 32 KiB after the stages (produce mode, whose stages then hold RoPE coefficients).
+    // measured).  After the last step the output rows are staged in the first 32 KiB (plain mode);
+    // in produce mode the stages then hold RoPE coefficients and the rows go out from the registers.
     constexpr int kOp = kTile * 128;
     constexpr int kStage = 2 * kOp;
-    // Produce mode: 32 KiB more, the output staging while the stages hold the RoPE coefficients.
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage + (kProduce ? 32768 : 0)];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage];
     int tile_t, tile_f;
     tile_of(xcd_tile(blockIdx.x, (uint32_t)(a.n_tt * a.n_tf)), a.n_tt, a.n_tf, tile_t, tile_f);
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -986,7 +973,6 @@ void project_tile_kernel(const TileArgs a)
         __builtin_amdgcn_s_waitcnt(0x3f70);                      // vmcnt(0): this wave's coefficient copies
         __syncthreads();                                         // everyone's
         if (head >= a.heads) return;
-        uint8_t* stage = &lds[2 * kStage] + wave * 8192;
         const uint32_t lds0e = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)&lds[0];
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
@@ -1005,9 +991,9 @@ void project_tile_kernel(const TileArgs a)
             in.sw = u & 15;
             in.slot = slot4[tb];
             const RowOut o = epilogue_math<true>(e, head, t, v, in);
-            // bf16 rows (Q, index-Q, bf16 caches) from the registers: no LDS round trip and no
-            // exchange of row addresses (1% faster than staging them).
-            if (o.fp8) row_store_staged(o, v, stage);
+            // Rows from the registers: no LDS round trip and no exchange of row addresses (bf16
+            // rows: 1% faster than staging them).
+            if (o.fp8) row_store_fp8_direct(o, v);
             else row_store_bf16_direct(o, v);
         }
     } else {
